@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs shared by the oracle tests and the GPU path.
+
+This module draws random numbers and lays out grid allocations; it holds
+none of the quantization or product arithmetic.  Both sides of every parity
+check receive exactly the arrays it returns.
+
+* Weights: W ~ N(0, 0.02^2) in fp32 (``torch.randn`` with a seeded
+  generator, times 0.02).  The trained Qwen3 ThinkBit checkpoints that the
+  summary page serves are not available; these stand in for them with the
+  same shapes.
+* Activations: x ~ N(0, 1), rounded to bf16 by torch.
+* Mixed allocation (summary page onedev.kr/papers/1416, section "How it
+  differs": 75.3 % ternary, 6.0 % 2-bit, 18.7 % 3-bit of a layer's weights;
+  query/key kept at >= 2 bits, here forced to 3 bits): per layer, every
+  128-row block of the forced linears is 3-bit; the remaining blocks are
+  shuffled with a seeded permutation and assigned 3-bit until the layer's
+  3-bit share reaches 18.7 %, then 2-bit until 6.0 %, the rest ternary.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .configs import (BASE_SEED, GRID_I2, GRID_I3, GRID_MIXED, GRID_T, SHARE_I2, SHARE_I3, W_SIGMA,
+                      Workload)
+
+BLOCK_ROWS = 128
+
+
+def seed_of(*parts: int) -> int:
+    """A 63-bit seed derived from integer parts (numpy SeedSequence)."""
+    ss = np.random.SeedSequence([BASE_SEED] + [int(p) for p in parts])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] >> np.uint64(1))
+
+
+def weight(N: int, K: int, seed: int, device="cpu") -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * W_SIGMA
+
+
+def activations(M: int, K: int, seed: int, device="cpu") -> torch.Tensor:
+    """bf16 tensor [M][K]."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(M, K, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a bf16 tensor (host copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def n_blocks(N: int) -> int:
+    return (N + BLOCK_ROWS - 1) // BLOCK_ROWS
+
+
+def layer_allocation(linears, seed: int, forced_i3=("q", "k")) -> dict:
+    """Grid of every 128-row block of every linear of one layer -> {name: int8 array}."""
+    out = {l.name: np.full(n_blocks(l.N), GRID_T, dtype=np.int8) for l in linears}
+    total = sum(l.N * l.K for l in linears)
+    i3 = 0
+    free = []
+    for li, l in enumerate(linears):
+        for b in range(n_blocks(l.N)):
+            w = (min(BLOCK_ROWS, l.N - b * BLOCK_ROWS)) * l.K
+            if l.name in forced_i3:
+                out[l.name][b] = GRID_I3
+                i3 += w
+            else:
+                free.append((li, b, w))
+    order = np.random.default_rng(seed).permutation(len(free))
+    i2 = 0
+    for idx in order:
+        li, b, w = free[idx]
+        name = linears[li].name
+        if i3 < SHARE_I3 * total:
+            out[name][b] = GRID_I3
+            i3 += w
+        elif i2 < SHARE_I2 * total:
+            out[name][b] = GRID_I2
+            i2 += w
+    return out
+
+
+def allocation(wl: Workload, layer: int) -> dict:
+    if wl.grid != GRID_MIXED:
+        return {l.name: np.full(n_blocks(l.N), wl.grid, dtype=np.int8) for l in wl.linears}
+    return layer_allocation(list(wl.linears), seed_of(7, layer, len(wl.linears), wl.layers), wl.forced_i3)
+
+
+def realized_shares(wl: Workload) -> dict:
+    """Fraction of the workload's weights on each grid."""
+    tot = {GRID_T: 0, GRID_I2: 0, GRID_I3: 0}
+    for layer in range(wl.layers):
+        alloc = allocation(wl, layer)
+        for l in wl.linears:
+            for b, g in enumerate(alloc[l.name]):
+                tot[int(g)] += min(BLOCK_ROWS, l.N - b * BLOCK_ROWS) * l.K
+    s = sum(tot.values())
+    return {k: v / s for k, v in tot.items()}
+
+
+def weight_seed(wl_index: int, layer: int, mat: int) -> int:
+    return seed_of(1, wl_index, layer, mat)
+
+
+def x_seed(wl_index: int, layer: int, slot: str, M: int) -> int:
+    return seed_of(2, wl_index, layer, {"attn": 0, "o": 1, "mlp": 2, "down": 3}[slot], M)

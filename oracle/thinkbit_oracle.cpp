@@ -1,0 +1,429 @@
+// ThinkBit CPU oracle — TEST INFRASTRUCTURE ONLY.
+//
+// This file is the plain, slow reference that the HIP library is checked
+// against.  Only the test suite, the smoke entry point and the CPU-baseline
+// leg of the benchmark may load it.  It shares no source with the GPU path
+// (no headers, tables or helpers in common); the two meet only through the
+// seeded synthetic inputs.
+//
+// What it computes (each function cites the passage it follows):
+//   * ThinkBit summary page (onedev.kr/papers/1416), section "How it works":
+//     every weight is an integer codeword c times a bf16 scale s shared by
+//     128 weights; the codeword grid is ternary {-1,0,1}, 2-bit {-2..1} or
+//     3-bit {-4..3}; dequantization is one multiply; no codebooks, rotations
+//     or zero points.
+//   * The synthetic workload's quantizer: s = max|w| / |c_min| over a group
+//     of 128 consecutive input-dim weights, rounded to bf16, and
+//     c = clamp(round(w / s), c_min, c_max).  Re-rounding with a stored
+//     scale is the operation the k-quant calibration page
+//     (sotaaz.com/post/quantized-model-less-sure, section "Open question")
+//     shows to reproduce stored codes exactly.
+//   * The packed layout (five trits per byte in base 3, sixteen 2-bit codes
+//     per 32-bit word, thirty-two 3-bit codes per 96-bit triple, 64-row
+//     slabs, 128-row grid blocks) is this project's own definition; the
+//     pages fix no bit order.  It is written out once more, independently,
+//     in the HIP packer.
+//
+// Precision: codes are decided from an fp64 quotient; w = c*s is formed in
+// fp32 (exact: at most 11 significant bits); products and sums are fp64,
+// summed in ascending k.
+//
+// Readings where the pages are silent (listed with reasons in the design
+// notes): tie-break of round() is half-to-even; an all-zero group has s = 0
+// and all codes 0; NaN/Inf weights are rejected; trits past K are padding
+// with c = 0; padding rows of a slab have c = 0 and s = 0.
+
+#include <cstdint>
+#include <cstring>
+#include <cmath>
+#include <thread>
+#include <vector>
+#include <algorithm>
+#include <functional>
+
+namespace {
+
+constexpr int kGroup = 128;   // weights per scale (input dimension)
+constexpr int kSlab = 64;     // rows interleaved per slab
+constexpr int kBlock = 128;   // rows sharing one grid in a mixed matrix
+constexpr int kChunk = 16;    // bytes per row per slab step
+
+enum { GRID_T = 0, GRID_I2 = 1, GRID_I3 = 2 };
+
+int cmin_of(int grid) { return grid == GRID_T ? -1 : grid == GRID_I2 ? -2 : -4; }
+int cmax_of(int grid) { return grid == GRID_T ? 1 : grid == GRID_I2 ? 1 : 3; }
+bool grid_ok(int grid) { return grid == GRID_T || grid == GRID_I2 || grid == GRID_I3; }
+
+// IEEE-754 binary32 -> bfloat16, round to nearest, ties to even.
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;  // NaN
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+int64_t row_bytes_of(int grid, int64_t K) {
+  if (!grid_ok(grid) || K <= 0 || K % kGroup) return 0;
+  if (grid == GRID_T) return 16 * ((K + 79) / 80);  // 80 trits per 16 bytes, padded
+  if (grid == GRID_I2) return K / 4;                // 2 bits per code
+  return 3 * K / 8;                                 // 3 bits per code
+}
+
+// Code of row n at input index k, or 0 past K (padding).
+inline int code_at(const int8_t* codes, int64_t K, int64_t n, int64_t k) {
+  return k < K ? codes[n * K + k] : 0;
+}
+
+// Bytes of one row in the grid's own order (before slab interleave).
+void pack_row(int grid, int64_t K, const int8_t* codes, int64_t n, uint8_t* out) {
+  const int64_t rb = row_bytes_of(grid, K);
+  const int cmin = cmin_of(grid);
+  std::memset(out, 0, rb);
+  if (grid == GRID_T) {
+    // byte j = sum_{i=0..4} u_{5j+i} * 3^i, u = c + 1 (least significant trit = lowest k)
+    for (int64_t j = 0; j < rb; ++j) {
+      int v = 0, p = 1;
+      for (int i = 0; i < 5; ++i) {
+        v += (code_at(codes, K, n, 5 * j + i) - cmin) * p;
+        p *= 3;
+      }
+      out[j] = (uint8_t)v;
+    }
+  } else if (grid == GRID_I2) {
+    // little-endian 32-bit word j holds k = 16j+i at bits [2i, 2i+1], u = c + 2
+    for (int64_t j = 0; j < rb / 4; ++j) {
+      uint32_t w = 0;
+      for (int i = 0; i < 16; ++i) w |= (uint32_t)(code_at(codes, K, n, 16 * j + i) - cmin) << (2 * i);
+      std::memcpy(out + 4 * j, &w, 4);
+    }
+  } else {
+    // 96-bit triple t = three little-endian words w0,w1,w2 for k = 32t..32t+31, u = c + 4.
+    // Word d holds k = 32t+10d+2m at bits [3m,3m+2] and k = 32t+10d+2m+1 at
+    // bits [16+3m,16+3m+2], m = 0..4.  Code 32t+30 keeps its bit b in bit 15 of
+    // word b; code 32t+31 keeps its bit b in bit 31 of word b.
+    for (int64_t t = 0; t < K / 32; ++t) {
+      uint32_t w[3] = {0, 0, 0};
+      for (int d = 0; d < 3; ++d)
+        for (int m = 0; m < 5; ++m) {
+          uint32_t ue = (uint32_t)(code_at(codes, K, n, 32 * t + 10 * d + 2 * m) - cmin);
+          uint32_t uo = (uint32_t)(code_at(codes, K, n, 32 * t + 10 * d + 2 * m + 1) - cmin);
+          w[d] |= ue << (3 * m);
+          w[d] |= uo << (16 + 3 * m);
+        }
+      uint32_t u30 = (uint32_t)(code_at(codes, K, n, 32 * t + 30) - cmin);
+      uint32_t u31 = (uint32_t)(code_at(codes, K, n, 32 * t + 31) - cmin);
+      for (int b = 0; b < 3; ++b) {
+        w[b] |= ((u30 >> b) & 1u) << 15;
+        w[b] |= ((u31 >> b) & 1u) << 31;
+      }
+      std::memcpy(out + 12 * t, w, 12);
+    }
+  }
+}
+
+// Inverse of pack_row.  Returns false on a ternary byte above 242.
+bool unpack_row(int grid, int64_t K, const uint8_t* in, int8_t* row) {
+  const int64_t rb = row_bytes_of(grid, K);
+  const int cmin = cmin_of(grid);
+  if (grid == GRID_T) {
+    for (int64_t j = 0; j < rb; ++j) {
+      int v = in[j];
+      if (v > 242) return false;
+      for (int i = 0; i < 5; ++i) {
+        int64_t k = 5 * j + i;
+        if (k < K) row[k] = (int8_t)(v % 3 + cmin);
+        v /= 3;
+      }
+    }
+  } else if (grid == GRID_I2) {
+    for (int64_t j = 0; j < rb / 4; ++j) {
+      uint32_t w;
+      std::memcpy(&w, in + 4 * j, 4);
+      for (int i = 0; i < 16; ++i) row[16 * j + i] = (int8_t)((int)((w >> (2 * i)) & 3u) + cmin);
+    }
+  } else {
+    for (int64_t t = 0; t < K / 32; ++t) {
+      uint32_t w[3];
+      std::memcpy(w, in + 12 * t, 12);
+      for (int d = 0; d < 3; ++d)
+        for (int m = 0; m < 5; ++m) {
+          row[32 * t + 10 * d + 2 * m] = (int8_t)((int)((w[d] >> (3 * m)) & 7u) + cmin);
+          row[32 * t + 10 * d + 2 * m + 1] = (int8_t)((int)((w[d] >> (16 + 3 * m)) & 7u) + cmin);
+        }
+      uint32_t u30 = 0, u31 = 0;
+      for (int b = 0; b < 3; ++b) {
+        u30 |= ((w[b] >> 15) & 1u) << b;
+        u31 |= ((w[b] >> 31) & 1u) << b;
+      }
+      row[32 * t + 30] = (int8_t)((int)u30 + cmin);
+      row[32 * t + 31] = (int8_t)((int)u31 + cmin);
+    }
+  }
+  return true;
+}
+
+int64_t nblocks_of(int64_t N) { return (N + kBlock - 1) / kBlock; }
+int64_t nslabs_of(int64_t N) { return (N + kSlab - 1) / kSlab; }
+
+// Slabs held by grid block b (the last block may hold one).
+int64_t block_slabs(int64_t N, int64_t b) {
+  int64_t first = b * (kBlock / kSlab);
+  return std::min<int64_t>(kBlock / kSlab, nslabs_of(N) - first);
+}
+
+void parallel_rows(int64_t N, int nthreads, const std::function<void(int64_t, int64_t)>& fn) {
+  if (nthreads <= 1 || N < 2) {
+    fn(0, N);
+    return;
+  }
+  nthreads = (int)std::min<int64_t>(nthreads, N);
+  std::vector<std::thread> th;
+  for (int t = 0; t < nthreads; ++t) {
+    int64_t lo = N * t / nthreads, hi = N * (t + 1) / nthreads;
+    th.emplace_back([&fn, lo, hi] { fn(lo, hi); });
+  }
+  for (auto& x : th) x.join();
+}
+}  // namespace
+
+extern "C" {
+
+int ora_cmin(int grid) { return grid_ok(grid) ? cmin_of(grid) : 0; }
+int ora_cmax(int grid) { return grid_ok(grid) ? cmax_of(grid) : 0; }
+
+void ora_f32_to_bf16(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne(in[i]);
+}
+
+void ora_bf16_to_f32(const uint16_t* in, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_f32(in[i]);
+}
+
+int64_t ora_row_bytes(int grid, int64_t K) { return row_bytes_of(grid, K); }
+
+// Round-to-nearest quantization (summary page, "How it works"; scale rule of
+// the synthetic workload).  row_grid[n] is the grid of row n.  W is fp32
+// [N][K]; codes int8 [N][K]; scales bf16 bits [N][K/128].
+// Returns 0, or -1 for bad arguments / a non-finite weight.
+int ora_quantize(int64_t N, int64_t K, const int8_t* row_grid, const float* W, int8_t* codes,
+                 uint16_t* scales) {
+  if (N < 0 || K <= 0 || K % kGroup) return -1;
+  const int64_t G = K / kGroup;
+  for (int64_t n = 0; n < N; ++n) {
+    const int grid = row_grid[n];
+    if (!grid_ok(grid)) return -1;
+    const int cmin = cmin_of(grid), cmax = cmax_of(grid);
+    for (int64_t g = 0; g < G; ++g) {
+      const float* w = W + n * K + g * kGroup;
+      float a = 0.0f;
+      for (int i = 0; i < kGroup; ++i) {
+        if (!std::isfinite(w[i])) return -1;
+        a = std::max(a, std::fabs(w[i]));
+      }
+      const uint16_t sb = bf16_rne(a / (float)(-cmin));
+      scales[n * G + g] = sb;
+      const double s = (double)bf16_to_f32(sb);
+      for (int i = 0; i < kGroup; ++i) {
+        int c = 0;
+        if (s != 0.0) {
+          double q = std::nearbyint((double)w[i] / s);  // ties to even (default rounding mode)
+          c = (int)std::min<double>(std::max<double>(q, cmin), cmax);
+        }
+        codes[n * K + g * kGroup + i] = (int8_t)c;
+      }
+    }
+  }
+  return 0;
+}
+
+// Re-round W onto the grid with given scales (no new scale is computed).
+int ora_requantize(int64_t N, int64_t K, const int8_t* row_grid, const float* W, const uint16_t* scales,
+                   int8_t* codes) {
+  if (N < 0 || K <= 0 || K % kGroup) return -1;
+  const int64_t G = K / kGroup;
+  for (int64_t n = 0; n < N; ++n) {
+    const int grid = row_grid[n];
+    if (!grid_ok(grid)) return -1;
+    for (int64_t k = 0; k < K; ++k) {
+      const double s = (double)bf16_to_f32(scales[n * G + k / kGroup]);
+      int c = 0;
+      if (s != 0.0) {
+        double q = std::nearbyint((double)W[n * K + k] / s);
+        c = (int)std::min<double>(std::max<double>(q, cmin_of(grid)), cmax_of(grid));
+      }
+      codes[n * K + k] = (int8_t)c;
+    }
+  }
+  return 0;
+}
+
+// Byte offset of every grid block (nblk+1 entries) of a packed matrix.
+int ora_block_offsets(int64_t N, int64_t K, const int8_t* blk_grid, int64_t* off) {
+  if (N <= 0 || K <= 0 || K % kGroup) return -1;
+  const int64_t nb = nblocks_of(N);
+  off[0] = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    if (!grid_ok(blk_grid[b])) return -1;
+    off[b + 1] = off[b] + block_slabs(N, b) * kSlab * row_bytes_of(blk_grid[b], K);
+  }
+  return 0;
+}
+
+// Pack codes [N][K] into the slab-interleaved buffer: within a slab of 64
+// rows the bytes run chunk-major, 16 bytes of row r at offset
+// chunk*1024 + r*16.  Rows past N are padding (c = 0).
+int ora_pack(int64_t N, int64_t K, const int8_t* blk_grid, const int8_t* codes, uint8_t* packed) {
+  if (N <= 0 || K <= 0 || K % kGroup) return -1;
+  std::vector<int64_t> off(nblocks_of(N) + 1);
+  if (ora_block_offsets(N, K, blk_grid, off.data())) return -1;
+  std::vector<int8_t> zero(K, 0);
+  for (int64_t b = 0; b < nblocks_of(N); ++b) {
+    const int grid = blk_grid[b];
+    const int64_t rb = row_bytes_of(grid, K);
+    std::vector<uint8_t> row(rb);
+    for (int64_t sl = 0; sl < block_slabs(N, b); ++sl)
+      for (int r = 0; r < kSlab; ++r) {
+        const int64_t n = b * kBlock + sl * kSlab + r;
+        if (n < N)
+          pack_row(grid, K, codes, n, row.data());
+        else
+          pack_row(grid, K, zero.data(), 0, row.data());
+        uint8_t* dst = packed + off[b] + sl * kSlab * rb;
+        for (int64_t c = 0; c < rb / kChunk; ++c) std::memcpy(dst + c * kSlab * kChunk + r * kChunk, row.data() + c * kChunk, kChunk);
+      }
+  }
+  return 0;
+}
+
+// Inverse of ora_pack for the N real rows.  Returns -2 on an invalid ternary byte.
+int ora_unpack(int64_t N, int64_t K, const int8_t* blk_grid, const uint8_t* packed, int8_t* codes) {
+  if (N <= 0 || K <= 0 || K % kGroup) return -1;
+  std::vector<int64_t> off(nblocks_of(N) + 1);
+  if (ora_block_offsets(N, K, blk_grid, off.data())) return -1;
+  for (int64_t b = 0; b < nblocks_of(N); ++b) {
+    const int grid = blk_grid[b];
+    const int64_t rb = row_bytes_of(grid, K);
+    std::vector<uint8_t> row(rb);
+    for (int64_t sl = 0; sl < block_slabs(N, b); ++sl)
+      for (int r = 0; r < kSlab; ++r) {
+        const int64_t n = b * kBlock + sl * kSlab + r;
+        if (n >= N) continue;
+        const uint8_t* src = packed + off[b] + sl * kSlab * rb;
+        for (int64_t c = 0; c < rb / kChunk; ++c) std::memcpy(row.data() + c * kChunk, src + c * kSlab * kChunk + r * kChunk, kChunk);
+        if (!unpack_row(grid, K, row.data(), codes + n * K)) return -2;
+      }
+  }
+  return 0;
+}
+
+// Scales [N][G] -> slab layout: for slab s, group octet q = g/8, row r in the
+// slab, element (((s*G8 + q)*64 + r)*8 + g%8), G8 = ceil(G/8); unused
+// entries are 0.
+int64_t ora_packed_scales_len(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % kGroup) return 0;
+  return nslabs_of(N) * ((K / kGroup + 7) / 8) * kSlab * 8;
+}
+
+int ora_pack_scales(int64_t N, int64_t K, const uint16_t* scales, uint16_t* ps) {
+  const int64_t len = ora_packed_scales_len(N, K);
+  if (!len) return -1;
+  const int64_t G = K / kGroup, G8 = (G + 7) / 8;
+  std::fill(ps, ps + len, (uint16_t)0);
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < G; ++g)
+      ps[(((n / kSlab) * G8 + g / 8) * kSlab + n % kSlab) * 8 + g % 8] = scales[n * G + g];
+  return 0;
+}
+
+int ora_unpack_scales(int64_t N, int64_t K, const uint16_t* ps, uint16_t* scales) {
+  if (!ora_packed_scales_len(N, K)) return -1;
+  const int64_t G = K / kGroup, G8 = (G + 7) / 8;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < G; ++g)
+      scales[n * G + g] = ps[(((n / kSlab) * G8 + g / 8) * kSlab + n % kSlab) * 8 + g % 8];
+  return 0;
+}
+
+// Dequantization, one multiply (summary page, "How it works"): w32 = c*s in
+// fp32 (exact), w16 = bf16_rne(w32).  Either output may be null.
+void ora_dequant(int64_t N, int64_t K, const int8_t* codes, const uint16_t* scales, float* w32, uint16_t* w16) {
+  const int64_t G = K / kGroup;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const float w = (float)codes[n * K + k] * bf16_to_f32(scales[n * G + k / kGroup]);
+      if (w32) w32[n * K + k] = w;
+      if (w16) w16[n * K + k] = bf16_rne(w);
+    }
+}
+
+// y[m][n] = sum_k w32[n][k] * x[m][k], fp64 products and an fp64 sum in
+// ascending k; x is bf16 bits [M][K].  Rows are split over threads, which
+// changes no bit of the result.
+void ora_gemv(int64_t M, int64_t N, int64_t K, const int8_t* codes, const uint16_t* scales, const uint16_t* x,
+              double* y, int nthreads) {
+  const int64_t G = K / kGroup;
+  std::vector<double> xd(M * K);
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = (double)bf16_to_f32(x[i]);
+  parallel_rows(N, nthreads, [&](int64_t lo, int64_t hi) {
+    std::vector<double> w(K);
+    for (int64_t n = lo; n < hi; ++n) {
+      for (int64_t k = 0; k < K; ++k)
+        w[k] = (double)((float)codes[n * K + k] * bf16_to_f32(scales[n * G + k / kGroup]));
+      for (int64_t m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += w[k] * xd[m * K + k];
+        y[m * N + n] = acc;
+      }
+    }
+  });
+}
+
+// The same product read from packed buffers (decode each row with this
+// file's own unpacker, then as ora_gemv).  Returns -2 on a corrupt byte.
+int ora_gemv_packed(int64_t M, int64_t N, int64_t K, const int8_t* blk_grid, const uint8_t* packed,
+                    const uint16_t* pscales, const uint16_t* x, double* y, int nthreads) {
+  if (N <= 0 || K <= 0 || K % kGroup || M <= 0) return -1;
+  std::vector<int64_t> off(nblocks_of(N) + 1);
+  if (ora_block_offsets(N, K, blk_grid, off.data())) return -1;
+  const int64_t G = K / kGroup, G8 = (G + 7) / 8;
+  std::vector<double> xd(M * K);
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = (double)bf16_to_f32(x[i]);
+  int bad = 0;
+  parallel_rows(N, nthreads, [&](int64_t lo, int64_t hi) {
+    std::vector<int8_t> c(K);
+    std::vector<double> w(K);
+    for (int64_t n = lo; n < hi; ++n) {
+      const int64_t b = n / kBlock, sl = (n % kBlock) / kSlab, r = n % kSlab;
+      const int grid = blk_grid[b];
+      const int64_t rb = row_bytes_of(grid, K);
+      std::vector<uint8_t> row(rb);
+      const uint8_t* src = packed + off[b] + sl * kSlab * rb;
+      for (int64_t ch = 0; ch < rb / kChunk; ++ch) std::memcpy(row.data() + ch * kChunk, src + ch * kSlab * kChunk + r * kChunk, kChunk);
+      if (!unpack_row(grid, K, row.data(), c.data())) {
+        bad = 1;
+        continue;
+      }
+      for (int64_t k = 0; k < K; ++k) {
+        const uint16_t sb = pscales[(((n / kSlab) * G8 + (k / kGroup) / 8) * kSlab + r) * 8 + (k / kGroup) % 8];
+        w[k] = (double)((float)c[k] * bf16_to_f32(sb));
+      }
+      for (int64_t m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += w[k] * xd[m * K + k];
+        y[m * N + n] = acc;
+      }
+    }
+  });
+  return bad ? -2 : 0;
+}
+
+}  // extern "C"
