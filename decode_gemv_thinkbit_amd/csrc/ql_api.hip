@@ -1,0 +1,206 @@
+// C ABI of the qlinear library: argument checks, then dispatch to the launchers.
+// Every check happens before anything is enqueued.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ql_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ql_status fail(ql_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ql_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QL_OK;
+  return fail(QL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool grid_valid(int g) { return g == QL_GRID_T || g == QL_GRID_I2 || g == QL_GRID_I3; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+ql_status check_shape(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return fail(QL_EINVAL, "N and K must be positive (N=%lld, K=%lld)", (long long)N, (long long)K);
+  if (K % QL_GROUP) return fail(QL_EINVAL, "K=%lld is not a multiple of %d", (long long)K, QL_GROUP);
+  if (N > kMaxDim || K > kMaxDim || N * K > ((int64_t)1 << 40))
+    return fail(QL_EINVAL, "shape too large (N=%lld, K=%lld)", (long long)N, (long long)K);
+  return QL_OK;
+}
+
+ql_status check_grid(int grid, const int8_t* blk_grid, const int64_t* blk_off, bool need_off) {
+  if (grid == QL_GRID_MIXED) {
+    if (!blk_grid) return fail(QL_EINVAL, "mixed grid needs blk_grid");
+    if (need_off && !blk_off) return fail(QL_EINVAL, "mixed grid needs blk_off");
+    return QL_OK;
+  }
+  if (!grid_valid(grid)) return fail(QL_EINVAL, "unknown grid id %d", grid);
+  return QL_OK;
+}
+
+ql_status check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (!p) return fail(QL_EINVAL, "null pointer argument");
+    if (!aligned16(p)) return fail(QL_EINVAL, "pointer %p is not 16-byte aligned", p);
+  }
+  return QL_OK;
+}
+
+#define QL_TRY(x)                    \
+  do {                               \
+    ql_status _s = (x);              \
+    if (_s != QL_OK) return _s;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int qlinear_version(void) { return QL_LAYOUT_VERSION; }
+
+const char* qlinear_last_error(void) { return g_err; }
+
+int64_t qlinear_row_bytes(int grid, int64_t K) {
+  if (!grid_valid(grid) || K <= 0 || K % QL_GROUP || K > kMaxDim) return 0;
+  return ql::row_bytes(grid, K);
+}
+
+ql_status qlinear_block_offsets(int64_t N, int64_t K, const int8_t* blk_grid, int64_t* off) {
+  QL_TRY(check_shape(N, K));
+  if (!blk_grid || !off) return fail(QL_EINVAL, "null pointer argument");
+  const int64_t S = (N + QL_SLAB - 1) / QL_SLAB, nb = (N + QL_BLOCK - 1) / QL_BLOCK;
+  off[0] = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    if (!grid_valid(blk_grid[b])) return fail(QL_EINVAL, "blk_grid[%lld] = %d is not a grid", (long long)b, blk_grid[b]);
+    const int64_t slabs = (S - 2 * b) < 2 ? (S - 2 * b) : 2;
+    off[b + 1] = off[b] + slabs * QL_SLAB * ql::row_bytes(blk_grid[b], K);
+  }
+  return QL_OK;
+}
+
+int64_t qlinear_packed_bytes(int64_t N, int64_t K, int grid) {
+  if (check_shape(N, K) != QL_OK || !grid_valid(grid)) return 0;
+  return ((N + QL_SLAB - 1) / QL_SLAB) * QL_SLAB * ql::row_bytes(grid, K);
+}
+
+int64_t qlinear_packed_scales_len(int64_t N, int64_t K) {
+  if (check_shape(N, K) != QL_OK) return 0;
+  return ((N + QL_SLAB - 1) / QL_SLAB) * ((K / QL_GROUP + 7) / 8) * QL_SLAB * 8;
+}
+
+ql_status qlinear_quantize(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const float* W, int8_t* codes,
+                           uint16_t* scales, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, nullptr, false));
+  QL_TRY(check_ptrs({W, codes, scales}));
+  return hip_status(ql::launch_quantize(N, K, grid, blk_grid, W, codes, scales, stream), "quantize launch");
+}
+
+ql_status qlinear_pack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                       const int8_t* codes, void* packed, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, blk_off, true));
+  QL_TRY(check_ptrs({codes, packed}));
+  return hip_status(ql::launch_pack(N, K, grid, blk_grid, blk_off, codes, static_cast<uint8_t*>(packed), stream),
+                    "pack launch");
+}
+
+ql_status qlinear_pack_scales(int64_t N, int64_t K, const uint16_t* scales, uint16_t* pscales, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_ptrs({scales, pscales}));
+  return hip_status(ql::launch_scales(N, K, const_cast<uint16_t*>(scales), pscales, 0, stream), "pack_scales launch");
+}
+
+ql_status qlinear_unpack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                         const void* packed, int8_t* codes, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, blk_off, true));
+  QL_TRY(check_ptrs({packed, codes}));
+  return hip_status(ql::launch_unpack(N, K, grid, blk_grid, blk_off, static_cast<const uint8_t*>(packed), nullptr, 0,
+                                      codes, stream),
+                    "unpack launch");
+}
+
+ql_status qlinear_unpack_scales(int64_t N, int64_t K, const uint16_t* pscales, uint16_t* scales, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_ptrs({pscales, scales}));
+  return hip_status(ql::launch_scales(N, K, scales, const_cast<uint16_t*>(pscales), 1, stream),
+                    "unpack_scales launch");
+}
+
+ql_status qlinear_dequant(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                          const void* packed, const uint16_t* pscales, int out_bf16, void* out, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, blk_off, true));
+  QL_TRY(check_ptrs({packed, pscales, out}));
+  return hip_status(ql::launch_unpack(N, K, grid, blk_grid, blk_off, static_cast<const uint8_t*>(packed), pscales,
+                                      out_bf16 ? 2 : 1, out, stream),
+                    "dequant launch");
+}
+
+static ql_status mat_args(int64_t M, int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                          const void* packed, const uint16_t* pscales, const uint16_t* x, float* y, ql::MatArgs* a) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, blk_off, true));
+  QL_TRY(check_ptrs({packed, pscales, x, y}));
+  if (N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "N and K must be below 2^31");
+  *a = ql::MatArgs{static_cast<const uint8_t*>(packed), pscales, blk_grid, blk_off, x, y, (int32_t)N, (int32_t)K, grid};
+  (void)M;
+  return QL_OK;
+}
+
+ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                       const void* packed, const uint16_t* pscales, const uint16_t* x, float* y, hipStream_t stream) {
+  if (M < 1 || M > 8) return fail(QL_EINVAL, "gemv needs 1 <= M <= 8 (M=%lld)", (long long)M);
+  ql::MatArgs a;
+  QL_TRY(mat_args(M, N, K, grid, blk_grid, blk_off, packed, pscales, x, y, &a));
+  return hip_status(ql::launch_gemv(a, (int)M, stream), "gemv launch");
+}
+
+int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
+  if (!descs || count <= 0) return fail(QL_EINVAL, "empty descriptor list"), -1;
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    ql_gemv_desc& d = descs[i];
+    if (check_shape(d.N, d.K) != QL_OK) return -1;
+    if (check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
+    if (check_ptrs({d.packed, d.pscales, d.x, d.y}) != QL_OK) return -1;
+    if (total >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "too many slabs"), -1;
+    d.slab_begin = (int32_t)total;
+    total += (d.N + QL_SLAB - 1) / QL_SLAB;
+  }
+  return total;
+}
+
+ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int32_t M,
+                               hipStream_t stream) {
+  if (M < 1 || M > 8) return fail(QL_EINVAL, "grouped gemv needs 1 <= M <= 8 (M=%d)", M);
+  if (count <= 0 || total_slabs <= 0 || total_slabs >= ((int64_t)1 << 31))
+    return fail(QL_EINVAL, "bad count (%d) or slab total (%lld)", count, (long long)total_slabs);
+  QL_TRY(check_ptrs({descs}));
+  return hip_status(ql::launch_gemv_grouped(descs, count, total_slabs, M, stream), "grouped gemv launch");
+}
+
+size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return ql::gemm_workspace_bytes(M, N, K); }
+
+ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                       const void* packed, const uint16_t* pscales, const uint16_t* x, float* y, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (M < 1 || M >= ((int64_t)1 << 24)) return fail(QL_EINVAL, "gemm needs 1 <= M < 2^24 (M=%lld)", (long long)M);
+  ql::MatArgs a;
+  QL_TRY(mat_args(M, N, K, grid, blk_grid, blk_off, packed, pscales, x, y, &a));
+  if (workspace_bytes < ql::gemm_workspace_bytes(M, N, K))
+    return fail(QL_EINVAL, "workspace too small (%zu < %zu)", workspace_bytes, ql::gemm_workspace_bytes(M, N, K));
+  return hip_status(ql::launch_gemm(a, (int)M, workspace, workspace_bytes, stream), "gemm launch");
+}
+
+}  // extern "C"

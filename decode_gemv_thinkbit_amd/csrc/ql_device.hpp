@@ -1,0 +1,53 @@
+// Device-side helpers shared by the qlinear kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlinear.h"
+
+namespace ql {
+
+constexpr int kGroup = QL_GROUP;  // 128 weights per scale
+constexpr int kSlab = QL_SLAB;    // 64 rows per slab
+constexpr int kBlock = QL_BLOCK;  // 128 rows per grid block
+constexpr int kChunkBytes = 16;   // bytes per row per slab step
+constexpr int kSlabChunkBytes = kChunkBytes * kSlab;  // 1024
+constexpr int kTritsPerChunk = 80;  // 16 bytes x 5 trits
+constexpr int kPeriodK = 640;       // lcm(80, 128): 8 ternary chunks = 5 groups
+
+__host__ __device__ inline int grid_cmin(int g) { return g == QL_GRID_T ? -1 : (g == QL_GRID_I2 ? -2 : -4); }
+__host__ __device__ inline int grid_cmax(int g) { return g == QL_GRID_I3 ? 3 : 1; }
+
+__host__ __device__ inline int64_t row_bytes(int grid, int64_t K) {
+  if (grid == QL_GRID_T) return 16 * ((K + 79) / 80);
+  if (grid == QL_GRID_I2) return K / 4;
+  return 3 * K / 8;
+}
+
+// Byte offset of slab `s` in a packed matrix (uniform grid, or per-block tables).
+__device__ inline int64_t slab_offset(int64_t s, int64_t K, int grid, const int8_t* blk_grid,
+                                      const int64_t* blk_off, int* grid_out) {
+  if (grid == QL_GRID_MIXED) {
+    const int g = blk_grid[s >> 1];
+    *grid_out = g;
+    return blk_off[s >> 1] + (s & 1) * (int64_t)kSlab * row_bytes(g, K);
+  }
+  *grid_out = grid;
+  return s * (int64_t)kSlab * row_bytes(grid, K);
+}
+
+// Element index of scale (n, g) in the packed scale array.
+__host__ __device__ inline int64_t pscale_index(int64_t n, int64_t g, int64_t G8) {
+  return (((n / kSlab) * G8 + (g >> 3)) * kSlab + (n % kSlab)) * 8 + (g & 7);
+}
+
+__device__ inline float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ inline uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// bf16 bits of a small integer code (-4..3), exact.
+__device__ inline uint32_t code_bf16(int c) { return (uint32_t)f32_to_bf16_bits((float)c); }
+
+}  // namespace ql

@@ -1,0 +1,37 @@
+// Internal launcher declarations of the qlinear library (not part of the C ABI).
+#pragma once
+
+#include "ql_device.hpp"
+
+namespace ql {
+
+hipError_t launch_quantize(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const float* W, int8_t* codes,
+                           uint16_t* scales, hipStream_t stream);
+hipError_t launch_pack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                       const int8_t* codes, uint8_t* packed, hipStream_t stream);
+// mode 0: int8 codes, 1: fp32 c*s, 2: bf16 bits of c*s
+hipError_t launch_unpack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                         const uint8_t* packed, const uint16_t* pscales, int mode, void* out, hipStream_t stream);
+// dir 0: pack, 1: unpack
+hipError_t launch_scales(int64_t N, int64_t K, uint16_t* scales, uint16_t* ps, int dir, hipStream_t stream);
+
+// One matrix of a GEMV / GEMM.
+struct MatArgs {
+  const uint8_t* packed;
+  const uint16_t* pscales;
+  const int8_t* blk_grid;
+  const int64_t* blk_off;
+  const uint16_t* x;
+  float* y;
+  int32_t N, K, grid;
+};
+
+hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
+hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M,
+                               hipStream_t stream);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace ql

@@ -1,0 +1,272 @@
+"""Thin Python binding of libqlinear.so (argument marshalling only).
+
+Every step of the path runs in the HIP kernels behind the C ABI declared in
+``include/qlinear.h``; this module only checks tensor dtypes/devices, passes
+raw device pointers and the current torch stream, and maps status codes to
+exceptions.  There is no fallback: if the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+GRID_T, GRID_I2, GRID_I3, GRID_MIXED = 0, 1, 2, 3
+GROUP, SLAB, BLOCK = 128, 64, 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libqlinear.so")
+
+_lib = None
+
+
+class QLinearError(RuntimeError):
+    pass
+
+
+class ql_gemv_desc(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("pscales", ctypes.c_void_p), ("blk_grid", ctypes.c_void_p),
+                ("blk_off", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("slab_begin", ctypes.c_int32)]
+
+
+def lib():
+    """Load libqlinear.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QLinearError(f"HIP library not built: {LIB_PATH} (run decode_gemv_thinkbit_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.qlinear_version.restype = i32
+        L.qlinear_last_error.restype = ctypes.c_char_p
+        L.qlinear_row_bytes.argtypes = [i32, i64]
+        L.qlinear_row_bytes.restype = i64
+        L.qlinear_block_offsets.argtypes = [i64, i64, vp, vp]
+        L.qlinear_packed_bytes.argtypes = [i64, i64, i32]
+        L.qlinear_packed_bytes.restype = i64
+        L.qlinear_packed_scales_len.argtypes = [i64, i64]
+        L.qlinear_packed_scales_len.restype = i64
+        L.qlinear_quantize.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
+        L.qlinear_pack.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
+        L.qlinear_pack_scales.argtypes = [i64, i64, vp, vp, vp]
+        L.qlinear_unpack.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
+        L.qlinear_unpack_scales.argtypes = [i64, i64, vp, vp, vp]
+        L.qlinear_dequant.argtypes = [i64, i64, i32, vp, vp, vp, vp, i32, vp, vp]
+        L.qlinear_gemv.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.qlinear_grouped_prepare.argtypes = [vp, ctypes.c_int32]
+        L.qlinear_grouped_prepare.restype = i64
+        L.qlinear_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp]
+        L.qlinear_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.qlinear_gemm_workspace_bytes.restype = sz
+        L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in ("qlinear_block_offsets", "qlinear_quantize", "qlinear_pack", "qlinear_pack_scales",
+                     "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
+                     "qlinear_gemv_grouped", "qlinear_gemm"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise QLinearError(f"{what}: status {status}: {lib().qlinear_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# ---------------------------------------------------------------- sizes
+def row_bytes(grid: int, K: int) -> int:
+    return int(lib().qlinear_row_bytes(grid, K))
+
+
+def n_blocks(N: int) -> int:
+    return (N + BLOCK - 1) // BLOCK
+
+
+def block_offsets(N: int, K: int, blk_grid) -> np.ndarray:
+    t = np.ascontiguousarray(blk_grid, dtype=np.int8)
+    if t.shape != (n_blocks(N),):
+        raise ValueError("blk_grid needs one entry per 128-row block")
+    off = np.empty(len(t) + 1, dtype=np.int64)
+    _check(lib().qlinear_block_offsets(N, K, t.ctypes.data_as(ctypes.c_void_p), off.ctypes.data_as(ctypes.c_void_p)),
+           "block_offsets")
+    return off
+
+
+def packed_scales_len(N: int, K: int) -> int:
+    return int(lib().qlinear_packed_scales_len(N, K))
+
+
+@dataclass
+class PackedWeight:
+    """A ThinkBit weight in the library's packed layout (device tensors)."""
+    packed: torch.Tensor      # uint8, packed codes
+    pscales: torch.Tensor     # bfloat16, packed scale array
+    N: int
+    K: int
+    grid: int                 # GRID_T/I2/I3 or GRID_MIXED
+    blk_grid: Optional[torch.Tensor] = None  # int8 [ceil(N/128)] on device (mixed only)
+    blk_off: Optional[torch.Tensor] = None   # int64 [ceil(N/128)+1] on device (mixed only)
+
+    @property
+    def nbytes(self) -> int:
+        """Stored bytes of codes and scales (padding included)."""
+        return self.packed.numel() + 2 * self.pscales.numel()
+
+
+def _grid_tables(N: int, K: int, grid, device):
+    """(grid id, blk_grid dev tensor or None, blk_off dev tensor or None, packed size)."""
+    if isinstance(grid, (int, np.integer)):
+        g = int(grid)
+        size = int(lib().qlinear_packed_bytes(N, K, g))
+        if size <= 0:
+            raise ValueError(f"invalid grid {g} or shape {N}x{K}")
+        return g, None, None, size
+    table = np.ascontiguousarray(np.asarray(grid), dtype=np.int8)
+    off = block_offsets(N, K, table)
+    bg = torch.from_numpy(table).to(device)
+    bo = torch.from_numpy(off).to(device)
+    return GRID_MIXED, bg, bo, int(off[-1])
+
+
+# ---------------------------------------------------------------- quantize / pack
+def quantize(W: torch.Tensor, grid) -> tuple[torch.Tensor, torch.Tensor]:
+    """Round-to-nearest codes (int8 [N,K]) and bf16 scales [N, K/128] on the device."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    g, bg, _, _ = _grid_tables(N, K, grid, W.device)
+    codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    scales = torch.empty((N, K // GROUP), dtype=torch.bfloat16, device=W.device)
+    _check(lib().qlinear_quantize(N, K, g, _ptr(bg), _ptr(W), _ptr(codes), _ptr(scales), _stream()), "quantize")
+    return codes, scales
+
+
+def pack(codes: torch.Tensor, scales: torch.Tensor, grid) -> PackedWeight:
+    _dev(codes, torch.int8, "codes")
+    _dev(scales, torch.bfloat16, "scales")
+    N, K = codes.shape
+    if tuple(scales.shape) != (N, K // GROUP):
+        raise ValueError("scales must be [N, K/128]")
+    g, bg, bo, size = _grid_tables(N, K, grid, codes.device)
+    packed = torch.empty(size, dtype=torch.uint8, device=codes.device)
+    _check(lib().qlinear_pack(N, K, g, _ptr(bg), _ptr(bo), _ptr(codes), _ptr(packed), _stream()), "pack")
+    ps = torch.empty(packed_scales_len(N, K), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().qlinear_pack_scales(N, K, _ptr(scales), _ptr(ps), _stream()), "pack_scales")
+    return PackedWeight(packed, ps, N, K, g, bg, bo)
+
+
+def quantize_pack(W: torch.Tensor, grid) -> PackedWeight:
+    codes, scales = quantize(W, grid)
+    return pack(codes, scales, grid)
+
+
+def unpack(pw: PackedWeight) -> torch.Tensor:
+    codes = torch.empty((pw.N, pw.K), dtype=torch.int8, device=pw.packed.device)
+    _check(lib().qlinear_unpack(pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
+                                _ptr(codes), _stream()), "unpack")
+    return codes
+
+
+def unpack_scales(pw: PackedWeight) -> torch.Tensor:
+    s = torch.empty((pw.N, pw.K // GROUP), dtype=torch.bfloat16, device=pw.packed.device)
+    _check(lib().qlinear_unpack_scales(pw.N, pw.K, _ptr(pw.pscales), _ptr(s), _stream()), "unpack_scales")
+    return s
+
+
+def dequant(pw: PackedWeight, out_bf16: bool = False) -> torch.Tensor:
+    out = torch.empty((pw.N, pw.K), dtype=torch.bfloat16 if out_bf16 else torch.float32, device=pw.packed.device)
+    _check(lib().qlinear_dequant(pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
+                                 _ptr(pw.pscales), 1 if out_bf16 else 0, _ptr(out), _stream()), "dequant")
+    return out
+
+
+# ---------------------------------------------------------------- products
+def _xy(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor]):
+    _dev(x, torch.bfloat16, "x")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    M, K = x.shape
+    if K != pw.K:
+        raise ValueError(f"x has K={K}, weight has K={pw.K}")
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=x.device)
+    else:
+        _dev(out, torch.float32, "out")
+        if tuple(out.shape) != (M, pw.N):
+            raise ValueError("out must be [M, N]")
+    return x, M, out
+
+
+def gemv(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M, N] fp32 = x [M, K] bf16 times the packed weight transposed, M <= 8."""
+    x, M, out = _xy(x, pw, out)
+    _check(lib().qlinear_gemv(M, pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
+                              _ptr(pw.pscales), _ptr(x), _ptr(out), _stream()), "gemv")
+    return out
+
+
+def gemm(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M, N] fp32 = x [M, K] bf16 times the packed weight transposed (MFMA path)."""
+    x, M, out = _xy(x, pw, out)
+    need = int(lib().qlinear_gemm_workspace_bytes(M, pw.N, pw.K))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().qlinear_gemm(M, pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
+                              _ptr(pw.pscales), _ptr(x), _ptr(out), _ptr(workspace), need, _stream()), "gemm")
+    return out
+
+
+class GroupedGemv:
+    """One persistent launch over many independent (x, W, y) products with the same M."""
+
+    def __init__(self, items):
+        """items: list of (PackedWeight, x [M,K] bf16, y [M,N] fp32)."""
+        if not items:
+            raise ValueError("no items")
+        self.items = items
+        self.M = items[0][1].shape[0] if items[0][1].dim() == 2 else 1
+        arr = (ql_gemv_desc * len(items))()
+        for i, (pw, x, y) in enumerate(items):
+            _dev(x, torch.bfloat16, "x")
+            _dev(y, torch.float32, "y")
+            m = x.shape[0] if x.dim() == 2 else 1
+            if m != self.M or x.shape[-1] != pw.K or y.numel() != m * pw.N:
+                raise ValueError(f"item {i}: shapes do not match")
+            arr[i] = ql_gemv_desc(pw.packed.data_ptr(), pw.pscales.data_ptr(),
+                                  pw.blk_grid.data_ptr() if pw.blk_grid is not None else None,
+                                  pw.blk_off.data_ptr() if pw.blk_off is not None else None,
+                                  x.data_ptr(), y.data_ptr(), pw.N, pw.K, pw.grid, 0)
+        total = lib().qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(items))
+        if total < 0:
+            _check(1, "grouped_prepare")
+        self.total = int(total)
+        raw = bytes(memoryview(arr))
+        self.count = len(items)
+        self.descs = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(items[0][1].device)
+
+    def run(self):
+        _check(lib().qlinear_gemv_grouped(_ptr(self.descs), self.count, self.total, self.M, _stream()),
+               "gemv_grouped")

@@ -1,0 +1,178 @@
+/*
+ * qlinear.h -- C ABI of the ThinkBit low-bit GEMV/GEMM library for MI355X (gfx950).
+ *
+ * Weight format (ThinkBit summary page, onedev.kr/papers/1416, section "How it
+ * works"): every weight is an integer codeword c times a bf16 scale s shared by
+ * 128 consecutive input-dimension weights; the codeword grid is ternary
+ * {-1,0,1}, 2-bit {-2,-1,0,1} or 3-bit {-4,...,3}; dequantization is one
+ * multiply, with no codebook, rotation or zero point.  The same page (section
+ * "Premises & limits") notes that published checkpoints keep the codewords in
+ * 4-bit containers because kernels that read 2- and 3-bit codes directly do
+ * not exist; this library reads them at 1.6, 2 and 3 bits.
+ *
+ * Notation: W is [N][K] (N output rows, K input columns, K % 128 == 0),
+ * x is [M][K] bf16, y = x * W^T is [M][N] fp32.
+ *
+ * Packed layout, version 1 (this project's definition; the pages fix no bit
+ * order).  u = c - c_min is stored (ternary c+1, 2-bit c+2, 3-bit c+4).
+ *   row bytes: ternary 16*ceil(K/80); 2-bit K/4; 3-bit 3K/8.
+ *   ternary: byte j of a row = sum_{i<5} u[5j+i] * 3^i (lowest k least
+ *            significant); trits past K are padding with c = 0; bytes <= 242.
+ *   2-bit:   little-endian 32-bit word j holds k = 16j+i at bits [2i, 2i+1].
+ *   3-bit:   96-bit triple t (words w0,w1,w2 read as w0 | w1<<32 | w2<<64)
+ *            holds k = 32t+i at bits [3i, 3i+2].
+ *   slabs:   rows are grouped in slabs of 64; within a slab the bytes run
+ *            chunk-major: bytes 16c..16c+15 of row r of the slab sit at
+ *            c*1024 + r*16.  Rows past N are padding (all c = 0).
+ *   grids:   one grid per block of 128 rows.  A packed matrix is its blocks
+ *            concatenated in row order, each in its own grid's layout; block b
+ *            holds min(2, slabs left) slabs and starts at byte blk_off[b].
+ *            A uniform matrix is the special case with one grid everywhere.
+ *   scales:  bf16 bits; the packed scale array stores scale (n, g) at element
+ *            ((n/64 * G8 + g/8) * 64 + n%64) * 8 + g%8, G = K/128,
+ *            G8 = ceil(G/8); unused entries are 0.  Scales sit apart from the
+ *            codes, so recalibrated scales can be written without repacking.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (dev) are device memory owned by the caller; (host) are
+ *     host memory.  The library allocates nothing and never synchronizes;
+ *     device calls are enqueued on `stream` (0 = the null stream).
+ *   - Arguments are checked before anything is enqueued; a bad argument
+ *     returns QL_EINVAL (or QL_EUNSUPPORTED) and enqueues nothing.  A failed
+ *     launch returns QL_EHIP.  qlinear_last_error() describes the last failure
+ *     of the calling thread.
+ *   - Device pointers must be 16-byte aligned; y and every output must not
+ *     alias an input.
+ *   - Codes outside the grid, ternary bytes above 242 and non-finite inputs
+ *     are outside the contract (undefined results, never out-of-bounds
+ *     accesses).
+ *   - GEMV results are bitwise deterministic for a given launch shape.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QL_GROUP 128 /* weights per scale, along K */
+#define QL_SLAB 64   /* rows per interleaved slab */
+#define QL_BLOCK 128 /* rows per grid block */
+#define QL_LAYOUT_VERSION 1
+
+typedef enum { QL_GRID_T = 0, QL_GRID_I2 = 1, QL_GRID_I3 = 2, QL_GRID_MIXED = 3 } ql_grid;
+typedef enum { QL_OK = 0, QL_EINVAL = 1, QL_EUNSUPPORTED = 2, QL_EHIP = 3 } ql_status;
+
+/* Library and layout version (QL_LAYOUT_VERSION). */
+int qlinear_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *qlinear_last_error(void);
+
+/* ---------------------------------------------------------------- sizes (host only, no GPU) */
+
+/* Bytes of one packed row of grid T/I2/I3 (multiple of 16); 0 if the grid or K is invalid. */
+int64_t qlinear_row_bytes(int grid, int64_t K);
+
+/* Byte offset of every grid block of a packed N x K matrix.  blk_grid (host, ceil(N/128)
+ * entries) holds the grid of each block; off (host, ceil(N/128)+1 entries) receives the
+ * offsets, off[nblk] being the total packed size. */
+ql_status qlinear_block_offsets(int64_t N, int64_t K, const int8_t *blk_grid, int64_t *off);
+
+/* Packed size of an N x K matrix of one uniform grid (bytes); 0 if invalid. */
+int64_t qlinear_packed_bytes(int64_t N, int64_t K, int grid);
+
+/* Elements (bf16) of the packed scale array of an N x K matrix; 0 if invalid. */
+int64_t qlinear_packed_scales_len(int64_t N, int64_t K);
+
+/* ---------------------------------------------------------------- quantize / pack (device) */
+
+/* Round-to-nearest quantization of fp32 weights, the rule of the synthetic workloads:
+ * per row n and group g, s = bf16_rne(max|W[n,g*128..g*128+127]| / |c_min|), and
+ * c = clamp(rint(W / s), c_min, c_max) with the quotient in fp64 and ties to even
+ * (c = 0 where s = 0).  Re-rounding with a stored scale reproduces stored codes (k-quant
+ * calibration page, sotaaz.com/post/quantized-model-less-sure, section "Open question").
+ *   grid: QL_GRID_T/I2/I3, or QL_GRID_MIXED with blk_grid (dev, ceil(N/128) int8) giving
+ *         the grid of each 128-row block (ignored otherwise, may be NULL).
+ *   W (dev) fp32 [N][K]; codes (dev) int8 [N][K]; scales (dev) bf16 bits [N][K/128]. */
+ql_status qlinear_quantize(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const float *W,
+                           int8_t *codes, uint16_t *scales, hipStream_t stream);
+
+/* Pack codes int8 [N][K] (dev) into the layout above.  grid/blk_grid as for quantize;
+ * blk_off (dev, ceil(N/128)+1 int64, from qlinear_block_offsets) is required for
+ * QL_GRID_MIXED and ignored otherwise.  packed (dev) has the packed size. */
+ql_status qlinear_pack(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const int64_t *blk_off,
+                       const int8_t *codes, void *packed, hipStream_t stream);
+
+/* Scales bf16 [N][K/128] (dev) -> packed scale array (dev, qlinear_packed_scales_len elements). */
+ql_status qlinear_pack_scales(int64_t N, int64_t K, const uint16_t *scales, uint16_t *pscales,
+                              hipStream_t stream);
+
+/* Inverse of qlinear_pack for the N real rows: codes int8 [N][K] (dev). */
+ql_status qlinear_unpack(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const int64_t *blk_off,
+                         const void *packed, int8_t *codes, hipStream_t stream);
+
+/* Inverse of qlinear_pack_scales: scales bf16 [N][K/128] (dev). */
+ql_status qlinear_unpack_scales(int64_t N, int64_t K, const uint16_t *pscales, uint16_t *scales,
+                                hipStream_t stream);
+
+/* Dequantize (summary page, "How it works": one multiply): out[n][k] = c * s as fp32
+ * (exact) when out_bf16 == 0, or bf16_rne(c * s) bits when out_bf16 != 0.  out (dev) [N][K]. */
+ql_status qlinear_dequant(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const int64_t *blk_off,
+                          const void *packed, const uint16_t *pscales, int out_bf16, void *out,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------- products (device) */
+
+/* Decode-time GEMV, 1 <= M <= 8 (the per-token weight stream that the summary page,
+ * section "What it is", names as the bandwidth-bound step of decoding):
+ * y[m][n] = sum_k c[n][k] * s[n][k/128] * x[m][k].  Codes are read at 1.6/2/3 bits with
+ * 128-bit loads and decoded in registers; products c*x are exact in fp32 and are summed
+ * in fp32, each scale applied once per group.
+ *   x (dev) bf16 bits [M][K]; y (dev) fp32 [M][N]. */
+ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t *blk_grid,
+                       const int64_t *blk_off, const void *packed, const uint16_t *pscales,
+                       const uint16_t *x, float *y, hipStream_t stream);
+
+/* One entry of a grouped GEMV launch: an independent y = x * W^T on its own matrix. */
+typedef struct {
+  const void *packed;       /* (dev) packed codes */
+  const uint16_t *pscales;  /* (dev) packed scales */
+  const int8_t *blk_grid;   /* (dev) per-block grids, QL_GRID_MIXED only (else NULL) */
+  const int64_t *blk_off;   /* (dev) block offsets, QL_GRID_MIXED only (else NULL) */
+  const uint16_t *x;        /* (dev) bf16 bits [M][K] */
+  float *y;                 /* (dev) fp32 [M][N] */
+  int32_t N, K, grid;       /* shape and grid (QL_GRID_*) */
+  int32_t slab_begin;       /* filled by qlinear_grouped_prepare */
+} ql_gemv_desc;
+
+/* Fill slab_begin of every descriptor (host array) and return the total number of 64-row
+ * slabs (the task count), or -1 on a bad descriptor. */
+int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
+
+/* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
+ * descs (dev), count entries, all with the same M <= 8) in one persistent launch.  The
+ * products are independent: no y may alias another entry's x or y. */
+ql_status qlinear_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_slabs, int32_t M,
+                               hipStream_t stream);
+
+/* Batched GEMM for 1 <= M (tuned for 16..512): tiles of codes are decoded into LDS as bf16
+ * (codes are exact in bf16) and contracted on MFMA (bf16 x bf16 -> fp32); the group scale
+ * is applied to each 128-deep partial product in fp32.  Dequantizing to bf16 and computing
+ * in bf16 reproduces the native low-bit result (k-quant calibration page, section "Not just
+ * any noise").  workspace (dev) of qlinear_gemm_workspace_bytes(M, N, K) bytes (may be 0). */
+size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t *blk_grid,
+                       const int64_t *blk_off, const void *packed, const uint16_t *pscales,
+                       const uint16_t *x, float *y, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -106,24 +106,16 @@ void pack_row(int grid, int64_t K, const int8_t* codes, int64_t n, uint8_t* out)
       std::memcpy(out + 4 * j, &w, 4);
     }
   } else {
-    // 96-bit triple t = three little-endian words w0,w1,w2 for k = 32t..32t+31, u = c + 4.
-    // Word d holds k = 32t+10d+2m at bits [3m,3m+2] and k = 32t+10d+2m+1 at
-    // bits [16+3m,16+3m+2], m = 0..4.  Code 32t+30 keeps its bit b in bit 15 of
-    // word b; code 32t+31 keeps its bit b in bit 31 of word b.
+    // 96-bit triple t: three little-endian words w0,w1,w2 read as the integer
+    // w0 | w1<<32 | w2<<64 holds k = 32t+i at bits [3i, 3i+2], u = c + 4.
     for (int64_t t = 0; t < K / 32; ++t) {
       uint32_t w[3] = {0, 0, 0};
-      for (int d = 0; d < 3; ++d)
-        for (int m = 0; m < 5; ++m) {
-          uint32_t ue = (uint32_t)(code_at(codes, K, n, 32 * t + 10 * d + 2 * m) - cmin);
-          uint32_t uo = (uint32_t)(code_at(codes, K, n, 32 * t + 10 * d + 2 * m + 1) - cmin);
-          w[d] |= ue << (3 * m);
-          w[d] |= uo << (16 + 3 * m);
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t u = (uint32_t)(code_at(codes, K, n, 32 * t + i) - cmin);
+        for (int b = 0; b < 3; ++b) {
+          const int bit = 3 * i + b;
+          w[bit / 32] |= ((u >> b) & 1u) << (bit % 32);
         }
-      uint32_t u30 = (uint32_t)(code_at(codes, K, n, 32 * t + 30) - cmin);
-      uint32_t u31 = (uint32_t)(code_at(codes, K, n, 32 * t + 31) - cmin);
-      for (int b = 0; b < 3; ++b) {
-        w[b] |= ((u30 >> b) & 1u) << 15;
-        w[b] |= ((u31 >> b) & 1u) << 31;
       }
       std::memcpy(out + 12 * t, w, 12);
     }
@@ -154,18 +146,14 @@ bool unpack_row(int grid, int64_t K, const uint8_t* in, int8_t* row) {
     for (int64_t t = 0; t < K / 32; ++t) {
       uint32_t w[3];
       std::memcpy(w, in + 12 * t, 12);
-      for (int d = 0; d < 3; ++d)
-        for (int m = 0; m < 5; ++m) {
-          row[32 * t + 10 * d + 2 * m] = (int8_t)((int)((w[d] >> (3 * m)) & 7u) + cmin);
-          row[32 * t + 10 * d + 2 * m + 1] = (int8_t)((int)((w[d] >> (16 + 3 * m)) & 7u) + cmin);
+      for (int i = 0; i < 32; ++i) {
+        uint32_t u = 0;
+        for (int b = 0; b < 3; ++b) {
+          const int bit = 3 * i + b;
+          u |= ((w[bit / 32] >> (bit % 32)) & 1u) << b;
         }
-      uint32_t u30 = 0, u31 = 0;
-      for (int b = 0; b < 3; ++b) {
-        u30 |= ((w[b] >> 15) & 1u) << b;
-        u31 |= ((w[b] >> 31) & 1u) << b;
+        row[32 * t + i] = (int8_t)((int)u + cmin);
       }
-      row[32 * t + 30] = (int8_t)((int)u30 + cmin);
-      row[32 * t + 31] = (int8_t)((int)u31 + cmin);
     }
   }
   return true;

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments before touching the GPU (CPU only: no compute call reaches a launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_gemv_thinkbit_amd import qlinear as ql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qlinear.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlinear_\w+)\s*\(", src)))
+
+
+def test_all_declared_symbols_exported():
+    L = ql.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_sizes():
+    assert ql.row_bytes(ql.GRID_T, 4096) == 832
+    assert ql.row_bytes(ql.GRID_I2, 4096) == 1024
+    assert ql.row_bytes(ql.GRID_I3, 4096) == 1536
+    assert ql.row_bytes(ql.GRID_T, 100) == 0  # K not a multiple of 128
+    assert ql.row_bytes(7, 128) == 0
+    assert ql.lib().qlinear_packed_bytes(130, 256, ql.GRID_I2) == 3 * 64 * 64
+    assert ql.packed_scales_len(70, 1280) == 2 * 2 * 64 * 8
+    off = ql.block_offsets(300, 384, [0, 2, 1])
+    assert list(off) == [0, 128 * 80, 128 * 80 + 128 * 144, 128 * 80 + 128 * 144 + 64 * 96]  # T row 80 B at K=384
+    assert ql.lib().qlinear_version() == 1
+
+
+def test_sizes_match_oracle(ora):
+    for K in (128, 640, 1280, 4096, 5120, 12288, 17408):
+        for g in (0, 1, 2):
+            assert ql.row_bytes(g, K) == ora.row_bytes(g, K)
+    t = np.array([2, 0, 1, 1, 0], np.int8)
+    assert np.array_equal(ql.block_offsets(600, 2048, t), ora.block_offsets(600, 2048, t))
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def status_and_msg(rc):
+    return rc, ql.lib().qlinear_last_error().decode()
+
+
+def test_gemv_argument_errors():
+    L = ql.lib()
+    args = lambda M, N, K, grid, p=FAKE: (M, N, K, grid, None, None, p, FAKE, FAKE, FAKE, None)
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(0, 64, 128, 0)))
+    assert rc == 1 and "M" in msg
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(9, 64, 128, 0)))
+    assert rc == 1
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(1, 64, 100, 0)))
+    assert rc == 1 and "multiple of 128" in msg
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(1, 0, 128, 0)))
+    assert rc == 1
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(1, 64, 128, 5)))
+    assert rc == 1 and "grid" in msg
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(1, 64, 128, 3)))  # mixed without tables
+    assert rc == 1 and "blk_grid" in msg
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(1, 64, 128, 0, p=None)))
+    assert rc == 1 and "null" in msg
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(1, 64, 128, 0, p=MISALIGNED)))
+    assert rc == 1 and "aligned" in msg
+
+
+def test_other_argument_errors():
+    L = ql.lib()
+    assert L.qlinear_gemm(0, 64, 128, 0, None, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert L.qlinear_quantize(4, 100, 0, None, FAKE, FAKE, FAKE, None) == 1
+    assert L.qlinear_pack(4, 128, 3, None, None, FAKE, FAKE, None) == 1
+    assert L.qlinear_unpack(4, 128, 9, None, None, FAKE, FAKE, None) == 1
+    assert L.qlinear_dequant(4, 128, 0, None, None, None, FAKE, 0, FAKE, None) == 1
+    assert L.qlinear_gemv_grouped(FAKE, 0, 10, 1, None) == 1
+    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 9, None) == 1
+    bad = np.array([0, 7], np.int8)
+    with pytest.raises(ql.QLinearError):
+        ql.block_offsets(200, 128, bad)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    pw = ql.PackedWeight(torch.zeros(16, dtype=torch.uint8), torch.zeros(8, dtype=torch.bfloat16), 1, 128, 0)
+    with pytest.raises(ValueError):
+        ql.gemv(torch.zeros(1, 128, dtype=torch.bfloat16), pw)

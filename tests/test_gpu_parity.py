@@ -1,0 +1,175 @@
+"""GPU parity: every kernel behind the C ABI against the CPU oracle (needs gfx950).
+
+Bit-exact for codes, scales, packed bytes, unpacked codes and dequantized
+weights; the products within max_n |dy| / ||y_row||_2 <= 2e-3 (GEMV, fp32
+accumulation) and 1e-2 (GEMM, bf16 MFMA), plus tighter tripwires that the
+measured error sits far below.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from decode_gemv_thinkbit_amd import qlinear as ql
+from decode_gemv_thinkbit_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+T, I2, I3 = 0, 1, 2
+GEMV_TOL, GEMM_TOL = 2e-3, 1e-2
+TRIP_GEMV, TRIP_GEMM = 1e-5, 1e-4  # normwise tripwires for the paths' actual arithmetic
+
+
+def note(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def grid_arg(N, grid, seed=0):
+    """An int grid, or a seeded per-block table covering all three grids."""
+    if grid != "mixed":
+        return grid
+    rng = np.random.default_rng(seed)
+    nb = (N + 127) // 128
+    t = rng.integers(0, 3, nb).astype(np.int8)
+    t[: min(3, nb)] = [2, 0, 1][: min(3, nb)]
+    return t
+
+
+def oracle_grid(grid):
+    return grid
+
+
+SHAPES = [(1, 128), (3, 256), (64, 640), (129, 1280), (200, 2048), (1000, 4096), (130, 5120), (70, 384)]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ql.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
+def test_quantize_pack_dequant_bit_exact(ora, dev, N, K, grid):
+    note(f"quantize/pack N={N} K={K} grid={grid}")
+    g = grid_arg(N, grid, seed=N + K)
+    W = synth.weight(N, K, seed=100 + N + K)
+    c_ref, s_ref = ora.quantize(W.numpy(), g)
+    codes, scales = ql.quantize(W.to(dev), g)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(bits(scales), s_ref)
+    pw = ql.pack(codes, scales, g)
+    assert np.array_equal(pw.packed.cpu().numpy(), ora.pack(c_ref, g))
+    assert np.array_equal(bits(pw.pscales), ora.pack_scales(s_ref, K))
+    assert np.array_equal(ql.unpack(pw).cpu().numpy(), c_ref)
+    assert np.array_equal(bits(ql.unpack_scales(pw)), s_ref)
+    w32, w16 = ora.dequant(c_ref, s_ref)
+    assert np.array_equal(ql.dequant(pw).cpu().numpy().view(np.uint32), w32.view(np.uint32))
+    assert np.array_equal(bits(ql.dequant(pw, out_bf16=True)), w16)
+
+
+def test_quantize_ties_and_zero_groups(ora, dev):
+    s = 0.015625
+    W = np.zeros((3, 256), np.float32)
+    W[0, :9] = (np.arange(-9, 9, 2) / 2.0 * s).astype(np.float32)  # exact half-integer quotients
+    W[0, 100] = 4 * s
+    W[1, 128:] = 0.0  # an all-zero group
+    W[1, :5] = [1e-40, -2e-41, 3e-39, 0, 5e-38]
+    W[2] = synth.weight(1, 256, seed=5).numpy()[0]
+    for g in (T, I2, I3):
+        c_ref, s_ref = ora.quantize(W, g)
+        codes, scales = ql.quantize(torch.from_numpy(W).to(dev), g)
+        assert np.array_equal(codes.cpu().numpy(), c_ref)
+        assert np.array_equal(bits(scales), s_ref)
+
+
+def _gemv_case(ora, dev, N, K, grid, M, seed):
+    g = grid_arg(N, grid, seed=seed)
+    W = synth.weight(N, K, seed=seed)
+    c_ref, s_ref = ora.quantize(W.numpy(), g)
+    pw = ql.quantize_pack(W.to(dev), g)
+    x = synth.activations(M, K, seed=seed + 1)
+    y64 = ora.gemv(c_ref, s_ref, synth.bf16_bits(x))
+    return pw, x.to(dev), y64, c_ref, s_ref
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_gemv_parity(ora, dev, N, K, grid, M):
+    note(f"gemv N={N} K={K} grid={grid} M={M}")
+    pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=N * 31 + K + M)
+    y = ql.gemv(x, pw)
+    torch.cuda.synchronize()
+    err, normwise = ora.rel_err(y.cpu().numpy(), y64)
+    assert err <= GEMV_TOL, (err, normwise)
+    assert normwise <= TRIP_GEMV, normwise
+    y2 = ql.gemv(x, pw)
+    assert torch.equal(y, y2)  # bitwise deterministic
+
+
+@pytest.mark.parametrize("grid", [T, I2, I3])
+def test_gemv_one_hot_decodes_every_position(ora, dev, grid):
+    """x = e_k gives y[n] = c[n,k] * s[n,k/128] exactly: the kernel's decode is bit-exact at every
+    position residue (mod 80 for ternary chunks, mod 16 / 32 for 2-/3-bit words)."""
+    N, K = 130, 1280
+    note(f"one-hot grid={grid}")
+    W = synth.weight(N, K, seed=77 + grid)
+    c_ref, s_ref = ora.quantize(W.numpy(), grid)
+    w32, _ = ora.dequant(c_ref, s_ref)
+    pw = ql.quantize_pack(W.to(dev), grid)
+    ks = list(range(0, 160)) + list(range(600, 700)) + list(range(K - 100, K))
+    X = torch.zeros((len(ks), K), dtype=torch.bfloat16)
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    X = X.to(dev)
+    for i0 in range(0, len(ks), 8):
+        y = ql.gemv(X[i0:i0 + 8].contiguous(), pw).cpu().numpy()
+        for j, k in enumerate(ks[i0:i0 + 8]):
+            assert np.array_equal(y[j], w32[:, k]), k
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (129, 1280), (1000, 4096), (70, 384), (256, 5120)])
+@pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
+@pytest.mark.parametrize("M", [1, 16, 17, 64, 100])
+def test_gemm_parity(ora, dev, N, K, grid, M):
+    note(f"gemm N={N} K={K} grid={grid} M={M}")
+    pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=N * 7 + K + M)
+    y = ql.gemm(x, pw)
+    torch.cuda.synchronize()
+    err, normwise = ora.rel_err(y.cpu().numpy(), y64)
+    assert err <= GEMM_TOL, (err, normwise)
+    assert normwise <= TRIP_GEMM, normwise
+
+
+def test_grouped_gemv_parity(ora, dev):
+    note("grouped gemv")
+    cases = [(256, 4096, "mixed"), (1024, 4096, I3), (128, 12288, T), (3, 640, I2), (1000, 2048, T)]
+    for M in (1, 4):
+        items, refs = [], []
+        for i, (N, K, grid) in enumerate(cases):
+            pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=500 + i + M)
+            y = torch.full((M, N), float("nan"), device=dev)
+            items.append((pw, x, y))
+            refs.append(y64)
+        grp = ql.GroupedGemv(items)
+        grp.run()
+        torch.cuda.synchronize()
+        for (pw, x, y), y64 in zip(items, refs):
+            err, normwise = ora.rel_err(y.cpu().numpy(), y64)
+            assert err <= GEMV_TOL and normwise <= TRIP_GEMV, (pw.N, pw.K, err, normwise)
+
+
+def test_workload_linear2048_i2(ora, dev):
+    """One 2048x2048 linear, uniform 2-bit grid, batch 1, at full size."""
+    note("workload linear2048_i2")
+    pw, x, y64, _, _ = _gemv_case(ora, dev, 2048, 2048, I2, 1, seed=synth.weight_seed(0, 0, 0))
+    err, normwise = ora.rel_err(ql.gemv(x, pw).cpu().numpy(), y64)
+    assert err <= GEMV_TOL and normwise <= TRIP_GEMV

@@ -233,16 +233,10 @@ def test_i2_each_value_each_position(ora, pos):
         assert np.all(np.delete(words, 1) == 0)
 
 
-# bit positions of code i (0..31) in the 96-bit triple, three bits each (low bit first), written
-# out by hand from the layout definition
+# bit positions of code i (0..31) in the 96-bit triple, low bit first: the layout puts code i at
+# bits 3i..3i+2 of w0 | w1<<32 | w2<<64 (codes 10 and 21 straddle words)
 def _i3_bits(i):
-    if i < 30:
-        d, r = divmod(i, 10)
-        m, odd = divmod(r, 2)
-        base = 32 * d + 16 * odd + 3 * m
-        return [base, base + 1, base + 2]
-    hi = 15 if i == 30 else 31
-    return [hi, 32 + hi, 64 + hi]
+    return [3 * i, 3 * i + 1, 3 * i + 2]
 
 
 @pytest.mark.parametrize("pos", range(32))
