@@ -93,91 +93,6 @@ __device__ __forceinline__ uint32_t xpair(cu32p xb, int kleft) {
   }
 }
 
-// ---------------------------------------------------------------- ternary
-// code pair a = (c_K0, c_K0+1) against x; split when a group boundary falls
-// between the two codes.
-template <int M, int K0, bool GUARD>
-__device__ __forceinline__ void t_pair(uint32_t a, const cu32p (&xb)[M], int kleft, float (&acc)[M][5]) {
-  constexpr int g0 = K0 / 128, g1 = (K0 + 1) / 128;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint32_t xp = xpair<K0, GUARD>(xb[m], kleft);
-    if constexpr (g0 == g1) {
-      acc[m][g0] = dot2(a, xp, acc[m][g0]);
-    } else {
-      acc[m][g0] = dot2(a, xp & 0x0000FFFFu, acc[m][g0]);
-      acc[m][g1] = dot2(a, xp & 0xFFFF0000u, acc[m][g1]);
-    }
-  }
-}
-
-// a = (c_K0, 0): the fifth trit of a byte.  Only x_K0 is read (into the low
-// half); the high half is zeroed so nothing past the period is touched.
-template <int M, int K0, bool GUARD>
-__device__ __forceinline__ void t_single(uint32_t a, const cu32p (&xb)[M], int kleft, float (&acc)[M][5]) {
-  constexpr int g0 = K0 / 128;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint32_t xp = (K0 & 1) ? (xdw<GUARD>(xb[m], K0 >> 1, kleft) >> 16)
-                                 : (xdw<GUARD>(xb[m], K0 >> 1, kleft) & 0xFFFFu);
-    acc[m][g0] = dot2(a, xp, acc[m][g0]);
-  }
-}
-
-template <int M, int CH, int J, bool GUARD>
-__device__ __forceinline__ void t_byte(uint32_t wj, const uint8_t* lut, uint32_t lane_off, const cu32p (&xb)[M],
-                                       int kleft, float (&acc)[M][5]) {
-  // address = (byte J&3 of wj) << 8 | lane_off, in one v_perm
-  const uint32_t addr = __builtin_amdgcn_perm(wj, lane_off, 0x0C0C0000u | ((4u + (J & 3)) << 8));
-  const uint4 e = *reinterpret_cast<const uint4*>(lut + kTLut + addr);
-  constexpr int k0 = CH * 80 + 5 * J;
-  t_pair<M, k0, GUARD>(e.x, xb, kleft, acc);
-  t_pair<M, k0 + 2, GUARD>(e.y, xb, kleft, acc);
-  t_single<M, k0 + 4, GUARD>(e.z, xb, kleft, acc);
-}
-
-template <int M, int CH, bool GUARD, int... J>
-__device__ __forceinline__ void t_chunk(const uint4 d, const uint8_t* lut, uint32_t lane_off, const cu32p (&xb)[M],
-                                        int kleft, float (&acc)[M][5], std::integer_sequence<int, J...>) {
-  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-  (t_byte<M, CH, J, GUARD>(w[J >> 2], lut, lane_off, xb, kleft, acc), ...);
-}
-
-template <int M, int CH, bool GUARD>
-__device__ __forceinline__ void t_chunk_if(const uint4 d, int nch, const uint8_t* lut, uint32_t lane_off,
-                                           const cu32p (&xb)[M], int kleft, float (&acc)[M][5]) {
-  if (GUARD && CH >= nch) return;
-  t_chunk<M, CH, GUARD>(d, lut, lane_off, xb, kleft, acc, std::make_integer_sequence<int, 16>{});
-}
-
-template <int M, bool GUARD, int... CH>
-__device__ __forceinline__ void t_period(const uint4 (&d)[8], int nch, const uint8_t* lut, uint32_t lane_off,
-                                         const cu32p (&xb)[M], int kleft, float (&acc)[M][5],
-                                         std::integer_sequence<int, CH...>) {
-  (t_chunk_if<M, CH, GUARD>(d[CH], nch, lut, lane_off, xb, kleft, acc), ...);
-}
-
-// ---------------------------------------------------------------- 2-bit
-template <int M, int K0, int J>
-__device__ __forceinline__ void i2_byte(uint32_t wj, const uint8_t* lut, uint32_t lane_off, const cu32p (&xb)[M],
-                                        float (&acc)[M]) {
-  const uint32_t b = (wj >> (8 * (J & 3))) & 0xFFu;
-  const uint2 e = *reinterpret_cast<const uint2*>(lut + kI2Lut + ((b << 5) | lane_off));
-  constexpr int k = K0 + 4 * J;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    acc[m] = dot2(e.x, xpair<k, false>(xb[m], 0), acc[m]);
-    acc[m] = dot2(e.y, xpair<k + 2, false>(xb[m], 0), acc[m]);
-  }
-}
-
-template <int M, int K0, int... J>
-__device__ __forceinline__ void i2_chunk(const uint4 d, const uint8_t* lut, uint32_t lane_off, const cu32p (&xb)[M],
-                                         float (&acc)[M], std::integer_sequence<int, J...>) {
-  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-  (i2_byte<M, K0, J>(w[J >> 2], lut, lane_off, xb, acc), ...);
-}
-
 // ---------------------------------------------------------------- 3-bit
 // 4 * (6-bit field P of the 96-bit triple w0|w1<<32|w2<<64)
 template <int P>
@@ -198,37 +113,88 @@ __device__ __forceinline__ uint32_t i3_field_x4(uint32_t w0, uint32_t w1, uint32
   }
 }
 
-template <int M, int K0, int P>
-__device__ __forceinline__ void i3_pair(uint32_t w0, uint32_t w1, uint32_t w2, const uint8_t* lut,
-                                        const cu32p (&xb)[M], float (&acc)[M]) {
-  const uint32_t a = *reinterpret_cast<const uint32_t*>(lut + kI3Lut + i3_field_x4<P>(w0, w1, w2));
-  constexpr int k = K0 + 2 * P;
-#pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = dot2(a, xpair<k, false>(xb[m], 0), acc[m]);
-}
-
-template <int M, int K0, int... P>
-__device__ __forceinline__ void i3_triple(uint32_t w0, uint32_t w1, uint32_t w2, const uint8_t* lut,
-                                          const cu32p (&xb)[M], float (&acc)[M], std::integer_sequence<int, P...>) {
-  (i3_pair<M, K0, P>(w0, w1, w2, lut, xb, acc), ...);
-}
-
 // ---------------------------------------------------------------- per-slab drivers
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+//
+// Software pipeline.  A slab row is consumed in units (M = 1: 8 bytes per lane).
+// Issuing a unit starts its LDS table reads and its scalar x loads; the unit
+// before it is then multiplied (dot2) and a single lgkmcnt(0) wait closes the
+// step.  Scalar loads may return out of order, so a wait on a partial count is
+// impossible while they are in flight; ordering "issue next, compute current,
+// wait" overlaps both latencies with the current unit's arithmetic instead.
+// Code chunks stream through an 8-deep ring of 128-bit registers, each slot
+// reloaded as soon as its last byte has been turned into table addresses.
 
-// streamed once: non-temporal 128-bit load
-__device__ __forceinline__ uint4 ld_chunk(const uint8_t* __restrict__ p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+template <class F, int... I>
+__device__ __forceinline__ void sfor_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
 }
+template <int N, class F>
+__device__ __forceinline__ void sfor(F&& f) {
+  sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// s_waitcnt lgkmcnt(0), leaving vmcnt/expcnt alone.
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// A uniform zero that the compiler cannot see through, computed from v.  The
+// next unit's addresses add it, so its loads cannot be hoisted above the
+// arithmetic that produced v (which would keep several units' operands live
+// at once and spill).
+__device__ __forceinline__ uint32_t opaque_zero(float v) {
+  uint32_t z = __builtin_amdgcn_readfirstlane(__float_as_uint(v));
+  asm("s_mov_b32 %0, 0" : "+s"(z));
+  return z;
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef const __attribute__((address_space(1))) u32x4_t* gu32x4p;  // global memory
+typedef const __attribute__((address_space(3))) u32x4_t* lu32x4p;  // LDS
+typedef const __attribute__((address_space(3))) u32x2_t* lu32x2p;
+typedef const __attribute__((address_space(3))) uint32_t* lu32p;
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Code chunks of one slab, read through a buffer resource: a chunk past the
+// wave's range reads as zero without a memory access, so the prefetch ring
+// needs no branches.  Non-temporal: each weight byte is used once per pass.
+struct ChunkSrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lane_off;  // lane * 16
+  __device__ __forceinline__ ChunkSrc(const uint8_t* slab, int nchunks, int lane)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(slab), (short)0, nchunks * kSlabChunkBytes,
+                                               0x00020000)),
+        lane_off((uint32_t)lane * kChunkBytes) {}
+  __device__ __forceinline__ uint4 load(int chunk) const {
+    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + (uint32_t)chunk * kSlabChunkBytes, 0, 2);
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+  }
+};
+
+// Table reads from LDS.  The ternary read keeps all 16 bytes (volatile stops
+// the compiler from narrowing it to ds_read_b96, which the probe measured at
+// less than half the throughput of ds_read_b128 on replicated tables).
+__device__ __forceinline__ u32x4_t lds_b128(const uint8_t* p) {
+  return *(const volatile __attribute__((address_space(3))) u32x4_t*)(p);
+}
+__device__ __forceinline__ u32x2_t lds_b64(const uint8_t* p) { return *(lu32x2p)(p); }
+__device__ __forceinline__ uint32_t lds_b32(const uint8_t* p) { return *(lu32p)(p); }
+
+typedef const __attribute__((address_space(1))) uint16_t* gu16p;
 
 __device__ __forceinline__ float ld_scale(const uint16_t* __restrict__ ss, int g, int lane) {
-  return bf16_bits_to_f32(ss[((g >> 3) * kSlab + lane) * 8 + (g & 7)]);
+  return bf16_bits_to_f32(((gu16p)ss)[((g >> 3) * kSlab + lane) * 8 + (g & 7)]);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& d, int w) {
+  return w == 0 ? d.x : (w == 1 ? d.y : (w == 2 ? d.z : d.w));
 }
 
 template <int M>
 struct SlabCtx {
-  const uint8_t* codes;      // slab base + lane * 16
+  const uint8_t* codes;      // slab base
   const uint16_t* scales;    // slab's scale block
   const uint16_t* x;         // x row 0
   int K, G, Mact, lane;
@@ -244,144 +210,414 @@ __device__ __forceinline__ void set_xb(cu32p (&xb)[M], const SlabCtx<M>& c, int 
   }
 }
 
+// pair (x_k, x_k+1) from a dword window whose first element is input KK = 0
+template <int KK, int XD>
+__device__ __forceinline__ uint32_t wpair(const uint32_t (&x)[XD]) {
+  if constexpr ((KK & 1) == 0) {
+    return x[KK >> 1];
+  } else {
+    return (uint32_t)((((uint64_t)x[(KK + 1) >> 1]) << 32 | x[(KK - 1) >> 1]) >> 16);
+  }
+}
+
+// ---------------------------------------------------------------- ternary units
+template <int UB>
+constexpr int t_xd() { return UB >= 2 ? 5 * UB / 2 : 3; }
+template <int UB, int U>
+constexpr int t_w0() { return (5 * UB * U) / 2; }
+
+template <int M, int UB>
+struct TBuf {
+  u32x4_t e[UB];          // table entries: (c0,c1), (c2,c3), (c4,0) per byte
+  uint32_t xp[M][3 * UB]; // matching x pairs: (x_k0,x_k0+1), (x_k0+2,x_k0+3), (x_k0+4,0)
+};
+
+template <int M, int UB, int U, bool GUARD>
+__device__ __forceinline__ void t_issue(TBuf<M, UB>& b, const uint4 (&d)[4], uint32_t lane_off0, const uint8_t* lut,
+                                        const cu32p (&xb)[M], int kleft, uint32_t dep) {
+  const uint32_t lane_off = lane_off0 + dep;
+  sfor<UB>([&](auto bi) __attribute__((always_inline)) {
+    constexpr int j = U * UB + decltype(bi)::value;  // byte within the period
+    const uint32_t w = word_of(d[(j >> 4) & 3], (j & 15) >> 2);
+    const uint32_t addr = __builtin_amdgcn_perm(w, lane_off, 0x0C0C0000u | ((4u + (j & 3)) << 8));
+    b.e[decltype(bi)::value] = lds_b128(lut + kTLut + addr);
+  });
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const cu32p xm = xb[m] + dep;
+    sfor<UB>([&](auto bi) __attribute__((always_inline)) {
+      constexpr int q = decltype(bi)::value;
+      constexpr int k0 = 5 * (U * UB + q);  // first trit of the byte within the period
+      // pairs are formed from scalar loads directly (no local array), so the
+      // odd-position shifts stay s_lshr_b64 on loaded SGPR pairs
+      b.xp[m][3 * q + 0] = xpair<k0, GUARD>(xm, kleft);
+      b.xp[m][3 * q + 1] = xpair<k0 + 2, GUARD>(xm, kleft);
+      b.xp[m][3 * q + 2] = ((k0 + 4) & 1) ? (xdw<GUARD>(xm, (k0 + 4) >> 1, kleft) >> 16)
+                                         : (xdw<GUARD>(xm, (k0 + 4) >> 1, kleft) & 0xFFFFu);
+    });
+  }
+}
+
+template <int M, int K0>
+__device__ __forceinline__ void t_dot(uint32_t a, uint32_t xp, float (&acc)[5]) {
+  constexpr int g0 = K0 / 128, g1 = (K0 + 1) / 128;
+  if constexpr (g0 == g1) {
+    acc[g0] = dot2(a, xp, acc[g0]);
+  } else {  // a group boundary falls between the two codes
+    acc[g0] = dot2(a, xp & 0x0000FFFFu, acc[g0]);
+    acc[g1] = dot2(a, xp & 0xFFFF0000u, acc[g1]);
+  }
+}
+
+template <int M, int UB, int U>
+__device__ __forceinline__ void t_compute(const TBuf<M, UB>& b, float (&acc)[M][5]) {
+  constexpr int kf = 5 * UB * U;
+  sfor<UB>([&](auto bi) __attribute__((always_inline)) {
+    constexpr int q = decltype(bi)::value;
+    constexpr int k0 = kf + 5 * q;
+    const u32x4_t e = b.e[q];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      t_dot<M, k0>(e.x, b.xp[m][3 * q + 0], acc[m]);
+      t_dot<M, k0 + 2>(e.y, b.xp[m][3 * q + 1], acc[m]);
+      acc[m][(k0 + 4) / 128] = dot2(e.z, b.xp[m][3 * q + 2], acc[m][(k0 + 4) / 128]);
+    }
+  });
+}
+
+template <int M>
+constexpr int t_ub() { return M == 1 ? 8 : (M == 2 ? 4 : (M <= 4 ? 2 : 1)); }
+
 template <int M>
 __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
+  constexpr int UB = t_ub<M>();
+  constexpr int NU = 128 / UB;  // units per period (even)
+  if (p0 >= p1) return;
   const int nchunks = (c.K + 79) / 80;
+  const int Pfull = c.K / kPeriodK;
+  const int pe = p1 < Pfull ? p1 : Pfull;
   const uint32_t lane_off = (uint32_t)(c.lane & 15) << 4;
-  uint4 cur[8], nxt[8];
-  auto load = [&](uint4(&d)[8], int p) {
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      const int cc = 8 * p + ch;
-      d[ch] = cc < nchunks ? ld_chunk(c.codes + (int64_t)cc * kSlabChunkBytes) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  if (p0 < p1) load(cur, p0);
-  for (int p = p0; p < p1; ++p) {
-    if (p + 1 < p1) load(nxt, p + 1);
+  // chunks of this wave's periods; later ones read as zero
+  const ChunkSrc src(c.codes, min(nchunks, 8 * p1), c.lane);
+  // ring of 4: chunk ch of a period lives in slot ch & 3; once a chunk's last
+  // byte is addressed its slot takes the chunk four positions later
+  uint4 d[4];
+  sfor<4>([&](auto ch) __attribute__((always_inline)) { d[decltype(ch)::value] = src.load(8 * p0 + decltype(ch)::value); });
+  TBuf<M, UB> A, B;
+  cu32p xb[M];
+  float acc[M][5];
+  uint32_t dep = 0;
+  if (p0 < pe) {
+    set_xb(xb, c, kPeriodK * p0);
+    t_issue<M, UB, 0, false>(A, d, lane_off, c.lut, xb, 0, 0u);
+    lgkm_wait0();
+  }
+  for (int p = p0; p < pe; ++p) {
     float sc[5];
 #pragma unroll
-    for (int gl = 0; gl < 5; ++gl) sc[gl] = (5 * p + gl < c.G) ? ld_scale(c.scales, 5 * p + gl, c.lane) : 0.0f;
-    float acc[M][5];
+    for (int gl = 0; gl < 5; ++gl) sc[gl] = ld_scale(c.scales, 5 * p + gl, c.lane);
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
       for (int gl = 0; gl < 5; ++gl) acc[m][gl] = 0.0f;
-    cu32p xb[M];
-    set_xb(xb, c, kPeriodK * p);
-    const int kleft = c.K - kPeriodK * p;
-    if (kleft >= kPeriodK) {
-      t_period<M, false>(cur, 8, c.lut, lane_off, xb, kleft, acc, std::make_integer_sequence<int, 8>{});
-    } else {
-      const int nch = (kleft + 79) / 80;
-      t_period<M, true>(cur, nch, c.lut, lane_off, xb, kleft, acc, std::make_integer_sequence<int, 8>{});
-    }
+    cu32p xn[M];
+    set_xb(xn, c, kPeriodK * (p + 1));
+    const bool more = p + 1 < pe;
+    sfor<NU>([&](auto u) __attribute__((always_inline)) {
+      constexpr int U = decltype(u)::value;
+      if constexpr (U + 1 < NU) {
+        if constexpr ((U & 1) == 0)
+          t_issue<M, UB, U + 1, false>(B, d, lane_off, c.lut, xb, 0, dep);
+        else
+          t_issue<M, UB, U + 1, false>(A, d, lane_off, c.lut, xb, 0, dep);
+        constexpr int last_byte = (U + 1) * UB + UB - 1;
+        if constexpr ((last_byte & 15) == 15) {
+          constexpr int ch = last_byte >> 4;
+          d[ch & 3] = src.load(ch < 4 ? 8 * p + ch + 4 : 8 * (p + 1) + ch - 4);
+        }
+      } else {
+        if (more) t_issue<M, UB, 0, false>(A, d, lane_off, c.lut, xn, 0, dep);
+      }
+      sched_fence();
+      if constexpr ((U & 1) == 0)
+        t_compute<M, UB, U>(A, acc);
+      else
+        t_compute<M, UB, U>(B, acc);
+      dep = opaque_zero(acc[0][(5 * UB * U) / 128]);
+      sched_fence();
+      lgkm_wait0();
+    });
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
       for (int gl = 0; gl < 5; ++gl) y[m] = fmaf(sc[gl], acc[m][gl], y[m]);
 #pragma unroll
-    for (int ch = 0; ch < 8; ++ch) cur[ch] = nxt[ch];
+    for (int m = 0; m < M; ++m) xb[m] = xn[m];
+  }
+  // last, partial period: trits past K are padding and x past K reads as 0
+  if (p1 > Pfull) {
+    const int p = Pfull;
+    const int kleft = c.K - kPeriodK * p;
+    const int nu = ((kleft + 79) / 80) * (16 / UB);
+    set_xb(xb, c, kPeriodK * p);
+    float sc[5];
+#pragma unroll
+    for (int gl = 0; gl < 5; ++gl) sc[gl] = (5 * p + gl < c.G) ? ld_scale(c.scales, 5 * p + gl, c.lane) : 0.0f;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int gl = 0; gl < 5; ++gl) acc[m][gl] = 0.0f;
+    sfor<NU>([&](auto u) __attribute__((always_inline)) {
+      constexpr int U = decltype(u)::value;
+      if (U < nu) {
+        t_issue<M, UB, U, true>(A, d, lane_off, c.lut, xb, kleft, dep);
+        constexpr int last_byte = U * UB + UB - 1;
+        if constexpr ((last_byte & 15) == 15 && (last_byte >> 4) < 4) {
+          constexpr int ch = last_byte >> 4;
+          d[ch] = src.load(8 * p + ch + 4);
+        }
+        lgkm_wait0();
+        t_compute<M, UB, U>(A, acc);
+        dep = opaque_zero(acc[0][(5 * UB * U) / 128]);
+      }
+    });
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int gl = 0; gl < 5; ++gl) y[m] = fmaf(sc[gl], acc[m][gl], y[m]);
   }
 }
 
-template <int M, int GL>
-__device__ __forceinline__ void i2_group(const uint4 d0, const uint4 d1, const SlabCtx<M>& c, uint32_t lane_off,
-                                         const cu32p (&xb)[M], float (&acc)[M]) {
-  i2_chunk<M, 128 * GL>(d0, c.lut, lane_off, xb, acc, std::make_integer_sequence<int, 16>{});
-  i2_chunk<M, 128 * GL + 64>(d1, c.lut, lane_off, xb, acc, std::make_integer_sequence<int, 16>{});
+// ---------------------------------------------------------------- 2-bit units
+// unit = UB2 bytes of one group (4 codes per byte); a group is 32 bytes = 2 chunks.
+template <int M>
+constexpr int i2_ub() { return 8 / M; }
+
+template <int M>
+struct I2Buf {
+  u32x2_t e[i2_ub<M>()];
+  uint32_t x[M][2 * i2_ub<M>()];
+};
+
+// ring: 4 chunks = 2 groups; group slot S (0, 1) holds chunks 2S, 2S+1
+template <int M, int S, int U>
+__device__ __forceinline__ void i2_issue(I2Buf<M>& b, const uint4 (&d)[4], uint32_t lane_off0, const uint8_t* lut,
+                                         const cu32p (&xb)[M], uint32_t dep) {
+  constexpr int UB = i2_ub<M>();
+  const uint32_t lane_off = lane_off0 + dep;
+  sfor<UB>([&](auto bi) __attribute__((always_inline)) {
+    constexpr int j = U * UB + decltype(bi)::value;  // byte within the group (0..31)
+    const uint32_t w = word_of(d[2 * S + (j >> 4)], (j & 15) >> 2);
+    const uint32_t bv = (w >> (8 * (j & 3))) & 0xFFu;
+    b.e[decltype(bi)::value] = lds_b64(lut + kI2Lut + ((bv << 5) | lane_off));
+  });
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    sfor<2 * UB>([&](auto i) __attribute__((always_inline)) {
+      b.x[m][decltype(i)::value] = (xb[m] + dep)[2 * U * UB + decltype(i)::value];
+    });
 }
 
 template <int M>
-__device__ void run_i2(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
+__device__ __forceinline__ void i2_compute(const I2Buf<M>& b, float (&acc)[M]) {
+  constexpr int UB = i2_ub<M>();
+  sfor<UB>([&](auto bi) __attribute__((always_inline)) {
+    constexpr int q = decltype(bi)::value;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      acc[m] = dot2(b.e[q].x, b.x[m][2 * q], acc[m]);
+      acc[m] = dot2(b.e[q].y, b.x[m][2 * q + 1], acc[m]);
+    }
+  });
+}
+
+template <int M>
+__device__ void run_i2(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
+  constexpr int NU = 32 / i2_ub<M>();  // units per group
+  if (g0 >= g1) return;
   const uint32_t lane_off = (uint32_t)(c.lane & 3) << 3;
-  uint4 cur[10], nxt[10];
-  auto load = [&](uint4(&d)[10], int p) {
+  const ChunkSrc src(c.codes, 2 * g1, c.lane);
+  uint4 d[4];
+  sfor<4>([&](auto q) __attribute__((always_inline)) { d[decltype(q)::value] = src.load(2 * g0 + decltype(q)::value); });
+  I2Buf<M> A, B;
+  cu32p xb[M];
+  set_xb(xb, c, kGroup * g0);
+  uint32_t dep = 0;
+  i2_issue<M, 0, 0>(A, d, lane_off, c.lut, xb, 0u);
+  lgkm_wait0();
+  for (int gb = g0; gb < g1; gb += 2) {
+    sfor<2>([&](auto s_) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_)::value;
+      const int g = gb + S;
+      if (g < g1) {
+        const float sc = ld_scale(c.scales, g, c.lane);
+        float acc[M];
 #pragma unroll
-    for (int ch = 0; ch < 10; ++ch) {
-      const int g = 5 * p + (ch >> 1);
-      d[ch] = g < c.G ? ld_chunk(c.codes + (int64_t)(10 * p + ch) * kSlabChunkBytes) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  if (p0 < p1) load(cur, p0);
-  for (int p = p0; p < p1; ++p) {
-    if (p + 1 < p1) load(nxt, p + 1);
-    cu32p xb[M];
-    set_xb(xb, c, kPeriodK * p);
-#define QL_I2_GROUP(GL)                                                  \
-    if (5 * p + GL < c.G) {                                              \
-      const float s = ld_scale(c.scales, 5 * p + GL, c.lane);            \
-      float acc[M];                                                      \
-      _Pragma("unroll") for (int m = 0; m < M; ++m) acc[m] = 0.0f;       \
-      i2_group<M, GL>(cur[2 * GL], cur[2 * GL + 1], c, lane_off, xb, acc); \
-      _Pragma("unroll") for (int m = 0; m < M; ++m) y[m] = fmaf(s, acc[m], y[m]); \
-    }
-    QL_I2_GROUP(0) QL_I2_GROUP(1) QL_I2_GROUP(2) QL_I2_GROUP(3) QL_I2_GROUP(4)
-#undef QL_I2_GROUP
+        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+        cu32p xn[M];
+        set_xb(xn, c, kGroup * (g + 1));
+        const bool more = g + 1 < g1;
+        sfor<NU>([&](auto u) __attribute__((always_inline)) {
+          constexpr int U = decltype(u)::value;
+          constexpr bool even = ((S * NU + U) & 1) == 0;  // buffer of this unit
+          if constexpr (U + 1 < NU) {
+            if constexpr (even)
+              i2_issue<M, S, U + 1>(B, d, lane_off, c.lut, xb, dep);
+            else
+              i2_issue<M, S, U + 1>(A, d, lane_off, c.lut, xb, dep);
+          } else {
+            if (more) {
+              if constexpr (even)
+                i2_issue<M, S ^ 1, 0>(B, d, lane_off, c.lut, xn, dep);
+              else
+                i2_issue<M, S ^ 1, 0>(A, d, lane_off, c.lut, xn, dep);
+            }
+            // every byte of this group is addressed: its slot takes group g + 2
+            d[2 * S] = src.load(2 * (g + 2));
+            d[2 * S + 1] = src.load(2 * (g + 2) + 1);
+          }
+          sched_fence();
+          if constexpr (even)
+            i2_compute<M>(A, acc);
+          else
+            i2_compute<M>(B, acc);
+          dep = opaque_zero(acc[0]);
+          sched_fence();
+          lgkm_wait0();
+        });
 #pragma unroll
-    for (int ch = 0; ch < 10; ++ch) cur[ch] = nxt[ch];
+        for (int m = 0; m < M; ++m) y[m] = fmaf(sc, acc[m], y[m]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) xb[m] = xn[m];
+      }
+    });
   }
 }
 
-template <int M, int GL>
-__device__ __forceinline__ void i3_group(const uint4 d0, const uint4 d1, const uint4 d2, const SlabCtx<M>& c,
-                                         const cu32p (&xb)[M], float (&acc)[M]) {
-  const uint32_t w[12] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w, d2.x, d2.y, d2.z, d2.w};
-  i3_triple<M, 128 * GL + 0>(w[0], w[1], w[2], c.lut, xb, acc, std::make_integer_sequence<int, 16>{});
-  i3_triple<M, 128 * GL + 32>(w[3], w[4], w[5], c.lut, xb, acc, std::make_integer_sequence<int, 16>{});
-  i3_triple<M, 128 * GL + 64>(w[6], w[7], w[8], c.lut, xb, acc, std::make_integer_sequence<int, 16>{});
-  i3_triple<M, 128 * GL + 96>(w[9], w[10], w[11], c.lut, xb, acc, std::make_integer_sequence<int, 16>{});
+// ---------------------------------------------------------------- 3-bit units
+// unit = NP 6-bit fields (pairs) of one 96-bit triple; a group is 4 triples = 3 chunks.
+template <int M>
+constexpr int i3_np() { return 16 / M; }
+
+template <int M>
+struct I3Buf {
+  uint32_t e[i3_np<M>()];
+  uint32_t x[M][i3_np<M>()];
+};
+
+// triple T (0..3) of group slot S: words 3T..3T+2 of the slot's 3 chunks (12 words)
+template <int M, int S, int U>
+__device__ __forceinline__ void i3_issue(I3Buf<M>& b, const uint4 (&d)[6], const uint8_t* lut, const cu32p (&xb)[M],
+                                         uint32_t dep) {
+  constexpr int NP = i3_np<M>();
+  constexpr int T = (U * NP) / 16;   // triple within the group
+  constexpr int P0 = (U * NP) % 16;  // first pair within the triple
+  constexpr int wb = 3 * T;          // first word of the triple within the group
+  const uint32_t w0 = word_of(d[3 * S + (wb >> 2)], wb & 3) + dep;
+  const uint32_t w1 = word_of(d[3 * S + ((wb + 1) >> 2)], (wb + 1) & 3) + dep;
+  const uint32_t w2 = word_of(d[3 * S + ((wb + 2) >> 2)], (wb + 2) & 3) + dep;
+  sfor<NP>([&](auto pi) __attribute__((always_inline)) {
+    constexpr int P = P0 + decltype(pi)::value;
+    b.e[decltype(pi)::value] = lds_b32(lut + kI3Lut + i3_field_x4<P>(w0, w1, w2));
+  });
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    sfor<NP>([&](auto i) __attribute__((always_inline)) {
+      b.x[m][decltype(i)::value] = (xb[m] + dep)[16 * T + P0 + decltype(i)::value];
+    });
 }
 
 template <int M>
-__device__ void run_i3(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
-  uint4 cur[15], nxt[15];
-  auto load = [&](uint4(&d)[15], int p) {
+__device__ __forceinline__ void i3_compute(const I3Buf<M>& b, float (&acc)[M]) {
+  sfor<i3_np<M>()>([&](auto pi) __attribute__((always_inline)) {
+    constexpr int q = decltype(pi)::value;
 #pragma unroll
-    for (int ch = 0; ch < 15; ++ch) {
-      const int g = 5 * p + ch / 3;
-      d[ch] = g < c.G ? ld_chunk(c.codes + (int64_t)(15 * p + ch) * kSlabChunkBytes) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  if (p0 < p1) load(cur, p0);
-  for (int p = p0; p < p1; ++p) {
-    if (p + 1 < p1) load(nxt, p + 1);
-    cu32p xb[M];
-    set_xb(xb, c, kPeriodK * p);
-#define QL_I3_GROUP(GL)                                                        \
-    if (5 * p + GL < c.G) {                                                    \
-      const float s = ld_scale(c.scales, 5 * p + GL, c.lane);                  \
-      float acc[M];                                                            \
-      _Pragma("unroll") for (int m = 0; m < M; ++m) acc[m] = 0.0f;             \
-      i3_group<M, GL>(cur[3 * GL], cur[3 * GL + 1], cur[3 * GL + 2], c, xb, acc); \
-      _Pragma("unroll") for (int m = 0; m < M; ++m) y[m] = fmaf(s, acc[m], y[m]); \
-    }
-    QL_I3_GROUP(0) QL_I3_GROUP(1) QL_I3_GROUP(2) QL_I3_GROUP(3) QL_I3_GROUP(4)
-#undef QL_I3_GROUP
+    for (int m = 0; m < M; ++m) acc[m] = dot2(b.e[q], b.x[m][q], acc[m]);
+  });
+}
+
+template <int M>
+__device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
+  constexpr int NU = 64 / i3_np<M>();  // units per group (4 triples x 16 pairs)
+  if (g0 >= g1) return;
+  const ChunkSrc src(c.codes, 3 * g1, c.lane);
+  uint4 d[6];
+  sfor<6>([&](auto q) __attribute__((always_inline)) { d[decltype(q)::value] = src.load(3 * g0 + decltype(q)::value); });
+  I3Buf<M> A, B;
+  cu32p xb[M];
+  set_xb(xb, c, kGroup * g0);
+  uint32_t dep = 0;
+  i3_issue<M, 0, 0>(A, d, c.lut, xb, 0u);
+  lgkm_wait0();
+  for (int gb = g0; gb < g1; gb += 2) {
+    sfor<2>([&](auto s_) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_)::value;
+      const int g = gb + S;
+      if (g < g1) {
+        const float sc = ld_scale(c.scales, g, c.lane);
+        float acc[M];
 #pragma unroll
-    for (int ch = 0; ch < 15; ++ch) cur[ch] = nxt[ch];
+        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+        cu32p xn[M];
+        set_xb(xn, c, kGroup * (g + 1));
+        const bool more = g + 1 < g1;
+        sfor<NU>([&](auto u) __attribute__((always_inline)) {
+          constexpr int U = decltype(u)::value;
+          constexpr bool even = ((S * NU + U) & 1) == 0;
+          if constexpr (U + 1 < NU) {
+            if constexpr (even)
+              i3_issue<M, S, U + 1>(B, d, c.lut, xb, dep);
+            else
+              i3_issue<M, S, U + 1>(A, d, c.lut, xb, dep);
+          } else {
+            if (more) {
+              if constexpr (even)
+                i3_issue<M, S ^ 1, 0>(B, d, c.lut, xn, dep);
+              else
+                i3_issue<M, S ^ 1, 0>(A, d, c.lut, xn, dep);
+            }
+#pragma unroll
+            for (int q = 0; q < 3; ++q) d[3 * S + q] = src.load(3 * (g + 2) + q);
+          }
+          sched_fence();
+          if constexpr (even)
+            i3_compute<M>(A, acc);
+          else
+            i3_compute<M>(B, acc);
+          dep = opaque_zero(acc[0]);
+          sched_fence();
+          lgkm_wait0();
+        });
+#pragma unroll
+        for (int m = 0; m < M; ++m) y[m] = fmaf(sc, acc[m], y[m]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) xb[m] = xn[m];
+      }
+    });
   }
 }
 
+// A slab's share of the input: periods [p0, p1) (groups 5*p0 .. 5*p1).
 template <int M>
 __device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
+  const int g0 = 5 * p0, g1 = (5 * p1 < c.G) ? 5 * p1 : c.G;
   if (gr == QL_GRID_T)
     run_t<M>(c, p0, p1, y);
   else if (gr == QL_GRID_I2)
-    run_i2<M>(c, p0, p1, y);
+    run_i2<M>(c, g0, g1, y);
   else
-    run_i3<M>(c, p0, p1, y);
+    run_i3<M>(c, g0, g1, y);
 }
 
 // ---------------------------------------------------------------- kernels
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;  // 512 threads; two workgroups (16 waves) per CU
 
 // Single matrix.  Each workgroup iteration takes kWaves/KS slabs; the KS waves
-// of a slab split its periods and are summed in LDS in fixed order.
+// of a slab split its periods and are summed in LDS in a fixed order.
 template <int M>
-__global__ void __launch_bounds__(kWaves * 64, 2) gemv_kernel(MatArgs a, int Mact, int KS, int64_t nslabs) {
+__global__ void __launch_bounds__(kWaves * 64, 4) gemv_kernel(MatArgs a, int Mact, int KS, int64_t nslabs) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  __shared__ float red[kWaves][M][64];
+  __shared__ float red[kWaves][64];
   build_luts(lut);
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -400,23 +636,23 @@ __global__ void __launch_bounds__(kWaves * 64, 2) gemv_kernel(MatArgs a, int Mac
     if (slab < nslabs) {
       int gr;
       const int64_t off = slab_offset(slab, a.K, a.grid, a.blk_grid, a.blk_off, &gr);
-      SlabCtx<M> c{a.packed + off + lane * kChunkBytes, a.pscales + slab * (int64_t)G8 * kSlab * 8, a.x, a.K, G,
+      SlabCtx<M> c{a.packed + off, a.pscales + slab * (int64_t)G8 * kSlab * 8, a.x, a.K, G,
                    Mact, lane, lut};
       run_slab<M>(gr, c, p0, p1, y);
     }
     const int64_t row = slab * kSlab + lane;
     if (KS > 1) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) red[wave][m][lane] = y[m];
-      __syncthreads();
-      if (kpart == 0 && slab < nslabs && row < a.N) {
-        for (int m = 0; m < Mact; ++m) {
-          float s = red[wave][m][lane];
-          for (int q = 1; q < KS; ++q) s += red[wave + q][m][lane];
+      for (int m = 0; m < M; ++m) {
+        red[wave][lane] = y[m];
+        __syncthreads();
+        if (kpart == 0 && slab < nslabs && row < a.N && m < Mact) {
+          float s = red[wave][lane];
+          for (int q = 1; q < KS; ++q) s += red[wave + q][lane];
           a.y[(int64_t)m * a.N + row] = s;
         }
+        __syncthreads();
       }
-      __syncthreads();
     } else if (slab < nslabs && row < a.N) {
       for (int m = 0; m < Mact; ++m) a.y[(int64_t)m * a.N + row] = y[m];
     }
@@ -425,7 +661,7 @@ __global__ void __launch_bounds__(kWaves * 64, 2) gemv_kernel(MatArgs a, int Mac
 
 // Many independent matrices in one persistent launch; one slab per wave task.
 template <int M>
-__global__ void __launch_bounds__(kWaves * 64, 2) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
+__global__ void __launch_bounds__(kWaves * 64, 4) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
                                                                       int count, int64_t total, int Mact) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
   build_luts(lut);
@@ -447,7 +683,7 @@ __global__ void __launch_bounds__(kWaves * 64, 2) gemv_grouped_kernel(const ql_g
     float y[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) y[m] = 0.0f;
-    SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off + lane * kChunkBytes,
+    SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off,
                  d.pscales + slab * (int64_t)G8 * kSlab * 8, d.x, K, G, Mact, lane, lut};
     run_slab<M>(gr, c, 0, (K + kPeriodK - 1) / kPeriodK, y);
     const int64_t row = slab * kSlab + lane;
