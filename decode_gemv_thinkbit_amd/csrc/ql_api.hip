@@ -163,7 +163,9 @@ ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t* 
   if (M < 1 || M > 8) return fail(QL_EINVAL, "gemv needs 1 <= M <= 8 (M=%lld)", (long long)M);
   ql::MatArgs a;
   QL_TRY(mat_args(M, N, K, grid, blk_grid, blk_off, packed, pscales, x, y, &a));
-  return hip_status(ql::launch_gemv(a, (int)M, stream), "gemv launch");
+  if (M == 1) return hip_status(ql::launch_gemv(a, 1, stream), "gemv launch");
+  // 2 <= M <= 8: a multi-token contraction, run on the MFMA path
+  return hip_status(ql::launch_gemm(a, (int)M, nullptr, 0, stream), "gemv (MFMA) launch");
 }
 
 int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
@@ -184,6 +186,7 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
 ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int32_t M,
                                hipStream_t stream) {
   if (M < 1 || M > 8) return fail(QL_EINVAL, "grouped gemv needs 1 <= M <= 8 (M=%d)", M);
+  if (M != 1) return fail(QL_EUNSUPPORTED, "grouped gemv runs batch 1 only (M=%d); use qlinear_gemm per matrix", M);
   if (count <= 0 || total_slabs <= 0 || total_slabs >= ((int64_t)1 << 31))
     return fail(QL_EINVAL, "bad count (%d) or slab total (%lld)", count, (long long)total_slabs);
   QL_TRY(check_ptrs({descs}));

@@ -81,15 +81,22 @@ __device__ __forceinline__ uint32_t xdw(cu32p xb, int i, int kleft) {
   }
 }
 
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+// {high half of lo, low half of hi} of two uniform words, as a two-lane 16-bit
+// vector so that it lowers to s_pack_ll_b32_b16 on the scalar unit.
+__device__ __forceinline__ uint32_t pack_hi_lo(uint32_t lo, uint32_t hi) {
+  const u16x2_t v = {(uint16_t)(lo >> 16), (uint16_t)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // (x_k, x_{k+1}) as a bf16 pair; odd k is re-aligned on the scalar unit.
 template <int K0, bool GUARD>
 __device__ __forceinline__ uint32_t xpair(cu32p xb, int kleft) {
   if constexpr ((K0 & 1) == 0) {
     return xdw<GUARD>(xb, K0 >> 1, kleft);
   } else {
-    const uint32_t lo = xdw<GUARD>(xb, (K0 - 1) >> 1, kleft);
-    const uint32_t hi = xdw<GUARD>(xb, (K0 + 1) >> 1, kleft);
-    return (uint32_t)((((uint64_t)hi << 32) | lo) >> 16);
+    return pack_hi_lo(xdw<GUARD>(xb, (K0 - 1) >> 1, kleft), xdw<GUARD>(xb, (K0 + 1) >> 1, kleft));
   }
 }
 
@@ -157,6 +164,16 @@ typedef const __attribute__((address_space(3))) uint32_t* lu32p;
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
+// A pointer the compiler must treat as wave-uniform (it is: every slab
+// pointer is derived from wave-uniform task indices), so resources built from
+// it live in SGPRs and need no per-lane waterfall.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
+
 // Code chunks of one slab, read through a buffer resource: a chunk past the
 // wave's range reads as zero without a memory access, so the prefetch ring
 // needs no branches.  Non-temporal: each weight byte is used once per pass.
@@ -164,8 +181,8 @@ struct ChunkSrc {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lane_off;  // lane * 16
   __device__ __forceinline__ ChunkSrc(const uint8_t* slab, int nchunks, int lane)
-      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(slab), (short)0, nchunks * kSlabChunkBytes,
-                                               0x00020000)),
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(uniform_ptr(slab), (short)0,
+                                               __builtin_amdgcn_readfirstlane(nchunks * kSlabChunkBytes), 0x00020000)),
         lane_off((uint32_t)lane * kChunkBytes) {}
   __device__ __forceinline__ uint4 load(int chunk) const {
     const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + (uint32_t)chunk * kSlabChunkBytes, 0, 2);
@@ -216,7 +233,7 @@ __device__ __forceinline__ uint32_t wpair(const uint32_t (&x)[XD]) {
   if constexpr ((KK & 1) == 0) {
     return x[KK >> 1];
   } else {
-    return (uint32_t)((((uint64_t)x[(KK + 1) >> 1]) << 32 | x[(KK - 1) >> 1]) >> 16);
+    return pack_hi_lo(x[(KK - 1) >> 1], x[(KK + 1) >> 1]);
   }
 }
 
@@ -232,9 +249,15 @@ struct TBuf {
   uint32_t xp[M][3 * UB]; // matching x pairs: (x_k0,x_k0+1), (x_k0+2,x_k0+3), (x_k0+4,0)
 };
 
-template <int M, int UB, int U, bool GUARD>
-__device__ __forceinline__ void t_issue(TBuf<M, UB>& b, const uint4 (&d)[4], uint32_t lane_off0, const uint8_t* lut,
-                                        const cu32p (&xb)[M], int kleft, uint32_t dep) {
+template <int M, int UB>
+struct TRaw {
+  uint32_t r[M][t_xd<UB>()];  // x dwords of a unit's window
+};
+
+// LDS table reads of unit U (the addresses come from the chunk ring).
+template <int M, int UB, int U>
+__device__ __forceinline__ void t_lds(TBuf<M, UB>& b, const uint4 (&d)[4], uint32_t lane_off0, const uint8_t* lut,
+                                      uint32_t dep) {
   const uint32_t lane_off = lane_off0 + dep;
   sfor<UB>([&](auto bi) __attribute__((always_inline)) {
     constexpr int j = U * UB + decltype(bi)::value;  // byte within the period
@@ -242,18 +265,35 @@ __device__ __forceinline__ void t_issue(TBuf<M, UB>& b, const uint4 (&d)[4], uin
     const uint32_t addr = __builtin_amdgcn_perm(w, lane_off, 0x0C0C0000u | ((4u + (j & 3)) << 8));
     b.e[decltype(bi)::value] = lds_b128(lut + kTLut + addr);
   });
+}
+
+// Scalar loads of unit U's x window.
+template <int M, int UB, int U, bool GUARD>
+__device__ __forceinline__ void t_xraw(TRaw<M, UB>& r, const cu32p (&xb)[M], int kleft, uint32_t dep) {
+  constexpr int W0 = t_w0<UB, U>();
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const cu32p xm = xb[m] + dep;
+    sfor<t_xd<UB>()>([&](auto i) __attribute__((always_inline)) {
+      r.r[m][decltype(i)::value] = xdw<GUARD>(xm, W0 + decltype(i)::value, kleft);
+    });
+  }
+}
+
+// x pairs of unit U from its window, on the scalar unit.  The window arrived
+// one step earlier, so these shifts never wait on the table reads in flight.
+template <int M, int UB, int U>
+__device__ __forceinline__ void t_pairs(TBuf<M, UB>& b, const TRaw<M, UB>& r) {
+  constexpr int base = 2 * t_w0<UB, U>();
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t (&v)[t_xd<UB>()] = r.r[m];
     sfor<UB>([&](auto bi) __attribute__((always_inline)) {
       constexpr int q = decltype(bi)::value;
-      constexpr int k0 = 5 * (U * UB + q);  // first trit of the byte within the period
-      // pairs are formed from scalar loads directly (no local array), so the
-      // odd-position shifts stay s_lshr_b64 on loaded SGPR pairs
-      b.xp[m][3 * q + 0] = xpair<k0, GUARD>(xm, kleft);
-      b.xp[m][3 * q + 1] = xpair<k0 + 2, GUARD>(xm, kleft);
-      b.xp[m][3 * q + 2] = ((k0 + 4) & 1) ? (xdw<GUARD>(xm, (k0 + 4) >> 1, kleft) >> 16)
-                                         : (xdw<GUARD>(xm, (k0 + 4) >> 1, kleft) & 0xFFFFu);
+      constexpr int kk = 5 * (U * UB + q) - base;  // first trit of the byte within the window
+      b.xp[m][3 * q + 0] = wpair<kk>(v);
+      b.xp[m][3 * q + 1] = wpair<kk + 2>(v);
+      b.xp[m][3 * q + 2] = ((kk + 4) & 1) ? (v[(kk + 4) >> 1] >> 16) : (v[(kk + 4) >> 1] & 0xFFFFu);
     });
   }
 }
@@ -303,13 +343,20 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
   // byte is addressed its slot takes the chunk four positions later
   uint4 d[4];
   sfor<4>([&](auto ch) __attribute__((always_inline)) { d[decltype(ch)::value] = src.load(8 * p0 + decltype(ch)::value); });
+  // Per step U: table reads of unit U+1, x window of unit U+2, dot2 of unit
+  // U, x pairs of unit U+1, one lgkmcnt(0) wait.  Unit u uses buffer u & 1.
   TBuf<M, UB> A, B;
+  TRaw<M, UB> R0, R1;
   cu32p xb[M];
   float acc[M][5];
   uint32_t dep = 0;
   if (p0 < pe) {
     set_xb(xb, c, kPeriodK * p0);
-    t_issue<M, UB, 0, false>(A, d, lane_off, c.lut, xb, 0, 0u);
+    t_xraw<M, UB, 0, false>(R0, xb, 0, 0u);
+    lgkm_wait0();
+    t_pairs<M, UB, 0>(A, R0);
+    t_lds<M, UB, 0>(A, d, lane_off, c.lut, 0u);
+    t_xraw<M, UB, 1, false>(R1, xb, 0, 0u);
     lgkm_wait0();
   }
   for (int p = p0; p < pe; ++p) {
@@ -325,24 +372,37 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
     const bool more = p + 1 < pe;
     sfor<NU>([&](auto u) __attribute__((always_inline)) {
       constexpr int U = decltype(u)::value;
+      constexpr bool odd = (U & 1) != 0;
+      auto& cur = odd ? B : A;     // unit U
+      auto& nxt = odd ? A : B;     // unit U+1
+      auto& rn1 = odd ? R0 : R1;   // raw window of unit U+1
+      auto& rn2 = odd ? R1 : R0;   // raw window of unit U+2
+      // 1. table reads of unit U+1
       if constexpr (U + 1 < NU) {
-        if constexpr ((U & 1) == 0)
-          t_issue<M, UB, U + 1, false>(B, d, lane_off, c.lut, xb, 0, dep);
-        else
-          t_issue<M, UB, U + 1, false>(A, d, lane_off, c.lut, xb, 0, dep);
+        t_lds<M, UB, U + 1>(nxt, d, lane_off, c.lut, dep);
         constexpr int last_byte = (U + 1) * UB + UB - 1;
         if constexpr ((last_byte & 15) == 15) {
           constexpr int ch = last_byte >> 4;
           d[ch & 3] = src.load(ch < 4 ? 8 * p + ch + 4 : 8 * (p + 1) + ch - 4);
         }
       } else {
-        if (more) t_issue<M, UB, 0, false>(A, d, lane_off, c.lut, xn, 0, dep);
+        if (more) t_lds<M, UB, 0>(nxt, d, lane_off, c.lut, dep);
+      }
+      // 2. x window of unit U+2
+      if constexpr (U + 2 < NU) {
+        t_xraw<M, UB, U + 2, false>(rn2, xb, 0, dep);
+      } else {
+        if (more) t_xraw<M, UB, U + 2 - NU, false>(rn2, xn, 0, dep);
       }
       sched_fence();
-      if constexpr ((U & 1) == 0)
-        t_compute<M, UB, U>(A, acc);
-      else
-        t_compute<M, UB, U>(B, acc);
+      // 3. arithmetic of unit U
+      t_compute<M, UB, U>(cur, acc);
+      // 4. x pairs of unit U+1
+      if constexpr (U + 1 < NU) {
+        t_pairs<M, UB, U + 1>(nxt, rn1);
+      } else {
+        if (more) t_pairs<M, UB, 0>(nxt, rn1);
+      }
       dep = opaque_zero(acc[0][(5 * UB * U) / 128]);
       sched_fence();
       lgkm_wait0();
@@ -370,13 +430,15 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
     sfor<NU>([&](auto u) __attribute__((always_inline)) {
       constexpr int U = decltype(u)::value;
       if (U < nu) {
-        t_issue<M, UB, U, true>(A, d, lane_off, c.lut, xb, kleft, dep);
+        t_lds<M, UB, U>(A, d, lane_off, c.lut, dep);
+        t_xraw<M, UB, U, true>(R0, xb, kleft, dep);
         constexpr int last_byte = U * UB + UB - 1;
         if constexpr ((last_byte & 15) == 15 && (last_byte >> 4) < 4) {
           constexpr int ch = last_byte >> 4;
           d[ch] = src.load(8 * p + ch + 4);
         }
         lgkm_wait0();
+        t_pairs<M, UB, U>(A, R0);
         t_compute<M, UB, U>(A, acc);
         dep = opaque_zero(acc[0][(5 * UB * U) / 128]);
       }
@@ -612,60 +674,12 @@ __device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, in
 // ---------------------------------------------------------------- kernels
 constexpr int kWaves = 8;  // 512 threads; two workgroups (16 waves) per CU
 
-// Single matrix.  Each workgroup iteration takes kWaves/KS slabs; the KS waves
-// of a slab split its periods and are summed in LDS in a fixed order.
+// One slab of one descriptor per wave task; persistent workgroups stride over
+// the tasks.  Descriptor fields are re-read per task, which keeps their live
+// ranges short (the kernels stay free of register spills).
 template <int M>
-__global__ void __launch_bounds__(kWaves * 64, 4) gemv_kernel(MatArgs a, int Mact, int KS, int64_t nslabs) {
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  __shared__ float red[kWaves][64];
-  build_luts(lut);
-  __syncthreads();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int spw = kWaves / KS;
-  const int64_t ntasks = (nslabs + spw - 1) / spw;
-  const int P = (a.K + kPeriodK - 1) / kPeriodK;
-  const int kpart = wave % KS;
-  const int p0 = P * kpart / KS, p1 = P * (kpart + 1) / KS;
-  const int G = a.K / kGroup, G8 = (G + 7) / 8;
-  for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
-    const int64_t slab = t * spw + wave / KS;
-    float y[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) y[m] = 0.0f;
-    if (slab < nslabs) {
-      int gr;
-      const int64_t off = slab_offset(slab, a.K, a.grid, a.blk_grid, a.blk_off, &gr);
-      SlabCtx<M> c{a.packed + off, a.pscales + slab * (int64_t)G8 * kSlab * 8, a.x, a.K, G,
-                   Mact, lane, lut};
-      run_slab<M>(gr, c, p0, p1, y);
-    }
-    const int64_t row = slab * kSlab + lane;
-    if (KS > 1) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        red[wave][lane] = y[m];
-        __syncthreads();
-        if (kpart == 0 && slab < nslabs && row < a.N && m < Mact) {
-          float s = red[wave][lane];
-          for (int q = 1; q < KS; ++q) s += red[wave + q][lane];
-          a.y[(int64_t)m * a.N + row] = s;
-        }
-        __syncthreads();
-      }
-    } else if (slab < nslabs && row < a.N) {
-      for (int m = 0; m < Mact; ++m) a.y[(int64_t)m * a.N + row] = y[m];
-    }
-  }
-}
-
-// Many independent matrices in one persistent launch; one slab per wave task.
-template <int M>
-__global__ void __launch_bounds__(kWaves * 64, 4) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
-                                                                      int count, int64_t total, int Mact) {
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  build_luts(lut);
-  __syncthreads();
+__device__ __forceinline__ void gemv_tasks(const ql_gemv_desc* __restrict__ descs, int count, int64_t total, int Mact,
+                                           const uint8_t* lut) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t < total; t += (int64_t)gridDim.x * kWaves) {
@@ -683,13 +697,34 @@ __global__ void __launch_bounds__(kWaves * 64, 4) gemv_grouped_kernel(const ql_g
     float y[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) y[m] = 0.0f;
-    SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off,
-                 d.pscales + slab * (int64_t)G8 * kSlab * 8, d.x, K, G, Mact, lane, lut};
+    SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off, d.pscales + slab * (int64_t)G8 * kSlab * 8, d.x, K, G,
+                 Mact, lane, lut};
     run_slab<M>(gr, c, 0, (K + kPeriodK - 1) / kPeriodK, y);
     const int64_t row = slab * kSlab + lane;
     if (row < d.N)
       for (int m = 0; m < Mact; ++m) d.y[(int64_t)m * d.N + row] = y[m];
   }
+}
+
+// A single matrix: its descriptor travels in the kernel arguments.  `count`
+// (always 1) is a runtime value so the descriptor reads stay inside the task
+// loop instead of being hoisted and kept live across it.
+template <int M>
+__global__ void __launch_bounds__(kWaves * 64, 4) gemv_kernel(ql_gemv_desc desc, int count, int64_t total, int Mact) {
+  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
+  build_luts(lut);
+  __syncthreads();
+  gemv_tasks<M>(&desc, count, total, Mact, lut);
+}
+
+// Many independent matrices in one persistent launch.
+template <int M>
+__global__ void __launch_bounds__(kWaves * 64, 4) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
+                                                                      int count, int64_t total, int Mact) {
+  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
+  build_luts(lut);
+  __syncthreads();
+  gemv_tasks<M>(descs, count, total, Mact, lut);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -707,43 +742,28 @@ int device_cu_count() {
   return cu_count_cached;
 }
 
-template <int M>
-static hipError_t launch_gemv_m(const MatArgs& a, int Mact, hipStream_t stream) {
-  const int64_t nslabs = ((int64_t)a.N + kSlab - 1) / kSlab;
-  const int P = (a.K + kPeriodK - 1) / kPeriodK;
-  const int slots = device_cu_count() * 2;  // two resident workgroups per CU
-  // split the periods of a slab over waves when there are too few slabs to fill the chip
-  int KS = 1;
-  while (KS < kWaves && (nslabs * KS) < (int64_t)slots * kWaves && P >= 2 * KS) KS *= 2;
-  const int64_t ntasks = (nslabs + (kWaves / KS) - 1) / (kWaves / KS);
-  const int grid = (int)(ntasks < slots ? ntasks : slots);
-  hipLaunchKernelGGL(gemv_kernel<M>, dim3(grid), dim3(kWaves * 64), 0, stream, a, Mact, KS, nslabs);
-  return hipGetLastError();
-}
-
+// Only the batch-1 instantiation exists: the pipelined template for
+// 2 <= M <= 8 spilled thousands of registers and faulted the GPU in its first
+// test, so it is not built; M >= 2 runs on the MFMA path instead.
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream) {
-  if (M == 1) return launch_gemv_m<1>(a, M, stream);
-  if (M == 2) return launch_gemv_m<2>(a, M, stream);
-  if (M <= 4) return launch_gemv_m<4>(a, M, stream);
-  return launch_gemv_m<8>(a, M, stream);
-}
-
-template <int M>
-static hipError_t launch_grouped_m(const ql_gemv_desc* descs, int32_t count, int64_t total, int Mact,
-                                   hipStream_t stream) {
-  const int slots = device_cu_count() * 2;
-  const int64_t wg_needed = (total + kWaves - 1) / kWaves;
+  if (M != 1) return hipErrorInvalidValue;
+  const int64_t nslabs = ((int64_t)a.N + kSlab - 1) / kSlab;
+  const ql_gemv_desc d{a.packed, a.pscales, a.blk_grid, a.blk_off, a.x, a.y, a.N, a.K, a.grid, 0};
+  const int slots = device_cu_count() * 2;  // two resident workgroups per CU
+  const int64_t wg_needed = (nslabs + kWaves - 1) / kWaves;
   const int grid = (int)(wg_needed < slots ? wg_needed : slots);
-  hipLaunchKernelGGL(gemv_grouped_kernel<M>, dim3(grid), dim3(kWaves * 64), 0, stream, descs, count, total, Mact);
+  hipLaunchKernelGGL(gemv_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, d, 1, nslabs, 1);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M,
                                hipStream_t stream) {
-  if (M == 1) return launch_grouped_m<1>(descs, count, total_slabs, M, stream);
-  if (M == 2) return launch_grouped_m<2>(descs, count, total_slabs, M, stream);
-  if (M <= 4) return launch_grouped_m<4>(descs, count, total_slabs, M, stream);
-  return launch_grouped_m<8>(descs, count, total_slabs, M, stream);
+  if (M != 1) return hipErrorInvalidValue;
+  const int slots = device_cu_count() * 2;
+  const int64_t wg_needed = (total_slabs + kWaves - 1) / kWaves;
+  const int grid = (int)(wg_needed < slots ? wg_needed : slots);
+  hipLaunchKernelGGL(gemv_grouped_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, descs, count, total_slabs, 1);
+  return hipGetLastError();
 }
 
 }  // namespace ql

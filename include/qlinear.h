@@ -130,9 +130,10 @@ ql_status qlinear_dequant(int64_t N, int64_t K, int grid, const int8_t *blk_grid
 
 /* Decode-time GEMV, 1 <= M <= 8 (the per-token weight stream that the summary page,
  * section "What it is", names as the bandwidth-bound step of decoding):
- * y[m][n] = sum_k c[n][k] * s[n][k/128] * x[m][k].  Codes are read at 1.6/2/3 bits with
- * 128-bit loads and decoded in registers; products c*x are exact in fp32 and are summed
- * in fp32, each scale applied once per group.
+ * y[m][n] = sum_k c[n][k] * s[n][k/128] * x[m][k].  At M = 1 codes are read at 1.6/2/3
+ * bits with 128-bit loads and decoded in registers; products c*x are exact in fp32 and
+ * are summed in fp32, each scale applied once per group.  2 <= M <= 8 is a multi-token
+ * contraction and runs on the MFMA path of qlinear_gemm (same numerics contract).
  *   x (dev) bf16 bits [M][K]; y (dev) fp32 [M][N]. */
 ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t *blk_grid,
                        const int64_t *blk_off, const void *packed, const uint16_t *pscales,
@@ -155,8 +156,8 @@ typedef struct {
 int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
 
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
- * descs (dev), count entries, all with the same M <= 8) in one persistent launch.  The
- * products are independent: no y may alias another entry's x or y. */
+ * descs (dev), count entries) at batch M = 1 in one persistent launch; other M return
+ * QL_EUNSUPPORTED.  The products are independent: no y may alias another entry's x or y. */
 ql_status qlinear_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_slabs, int32_t M,
                                hipStream_t stream);
 
