@@ -19,6 +19,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     # keep the compiler from emitting packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep single-lane atomics as written: the wave-aggregating rewrite waits on the
+    # grouped GEMV's ticket fetch at once instead of when the ticket is used
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -2,6 +2,7 @@
 // Every check happens before anything is enqueued.
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 
 #include "ql_internal.hpp"
@@ -170,12 +171,17 @@ ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t* 
 
 int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
   if (!descs || count <= 0) return fail(QL_EINVAL, "empty descriptor list"), -1;
-  int64_t total = 0;
   for (int32_t i = 0; i < count; ++i) {
-    ql_gemv_desc& d = descs[i];
+    const ql_gemv_desc& d = descs[i];
     if (check_shape(d.N, d.K) != QL_OK) return -1;
     if (check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
     if (check_ptrs({d.packed, d.pscales, d.x, d.y}) != QL_OK) return -1;
+  }
+  // longest rows first: the tail of the launch is then made of short tasks
+  std::stable_sort(descs, descs + count, [](const ql_gemv_desc& a, const ql_gemv_desc& b) { return a.K > b.K; });
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    ql_gemv_desc& d = descs[i];
     if (total >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "too many slabs"), -1;
     d.slab_begin = (int32_t)total;
     total += (d.N + QL_SLAB - 1) / QL_SLAB;
@@ -184,13 +190,13 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
 }
 
 ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int32_t M,
-                               hipStream_t stream) {
+                               uint32_t* sched, hipStream_t stream) {
   if (M < 1 || M > 8) return fail(QL_EINVAL, "grouped gemv needs 1 <= M <= 8 (M=%d)", M);
   if (M != 1) return fail(QL_EUNSUPPORTED, "grouped gemv runs batch 1 only (M=%d); use qlinear_gemm per matrix", M);
   if (count <= 0 || total_slabs <= 0 || total_slabs >= ((int64_t)1 << 31))
     return fail(QL_EINVAL, "bad count (%d) or slab total (%lld)", count, (long long)total_slabs);
-  QL_TRY(check_ptrs({descs}));
-  return hip_status(ql::launch_gemv_grouped(descs, count, total_slabs, M, stream), "grouped gemv launch");
+  QL_TRY(check_ptrs({descs, sched}));
+  return hip_status(ql::launch_gemv_grouped(descs, count, total_slabs, M, sched, stream), "grouped gemv launch");
 }
 
 size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return ql::gemm_workspace_bytes(M, N, K); }

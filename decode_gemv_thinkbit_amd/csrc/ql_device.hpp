@@ -16,6 +16,19 @@ constexpr int kSlabChunkBytes = kChunkBytes * kSlab;  // 1024
 constexpr int kTritsPerChunk = 80;  // 16 bytes x 5 trits
 constexpr int kPeriodK = 640;       // lcm(80, 128): 8 ternary chunks = 5 groups
 
+// Ternary digit order, layout version 2.  A stored byte j holds inputs
+// 5j..5j+4 as base-3 digits.  Even bytes keep input order (digit i = input
+// 5j+i).  Odd bytes rotate it: digits 0..3 are inputs 5j+1..5j+4 and digit 4
+// is input 5j, so that within a byte pair every even-aligned input pair but
+// one is a digit pair.  These two maps convert between the stored byte and
+// the input-order value (digit i = input 5j+i).
+__host__ __device__ inline uint32_t tern_to_input_order(uint32_t b, int64_t j) {
+  return (j & 1) ? (b % 81u) * 3u + b / 81u : b;
+}
+__host__ __device__ inline uint32_t tern_from_input_order(uint32_t v, int64_t j) {
+  return (j & 1) ? (v % 3u) * 81u + v / 3u : v;
+}
+
 __host__ __device__ inline int grid_cmin(int g) { return g == QL_GRID_T ? -1 : (g == QL_GRID_I2 ? -2 : -4); }
 __host__ __device__ inline int grid_cmax(int g) { return g == QL_GRID_I3 ? 3 : 1; }
 

@@ -29,7 +29,7 @@ __device__ __forceinline__ void decode32(const uint8_t* __restrict__ slab, int r
   if (gr == QL_GRID_T) {
     int64_t j = k0 / 5;
     int i = (int)(k0 % 5);
-    uint32_t b = rowbyte(j);
+    uint32_t b = tern_to_input_order(rowbyte(j), j);
     for (int t = 0; t < i; ++t) b /= 3;
     for (int q = 0; q < 32; ++q) {
       out[q] = code_bf16((int)(b % 3) - 1);
@@ -37,7 +37,7 @@ __device__ __forceinline__ void decode32(const uint8_t* __restrict__ slab, int r
       if (++i == 5) {
         i = 0;
         ++j;
-        b = (5 * j < K) ? rowbyte(j) : 121u;
+        b = (5 * j < K) ? tern_to_input_order(rowbyte(j), j) : 121u;
       }
     }
   } else if (gr == QL_GRID_I2) {

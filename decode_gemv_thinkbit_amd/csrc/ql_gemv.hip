@@ -52,7 +52,7 @@ __device__ void build_luts(uint8_t* smem) {
     q.x = code_bf16(c[0]) | (code_bf16(c[1]) << 16);
     q.y = code_bf16(c[2]) | (code_bf16(c[3]) << 16);
     q.z = code_bf16(c[4]);
-    q.w = 0;
+    q.w = code_bf16(c[4]) << 16;
     *reinterpret_cast<uint4*>(smem + kTLut + b * 256 + r * 16) = q;
   }
   for (int e = threadIdx.x; e < 256 * 4; e += blockDim.x) {
@@ -238,215 +238,149 @@ __device__ __forceinline__ uint32_t wpair(const uint32_t (&x)[XD]) {
 }
 
 // ---------------------------------------------------------------- ternary units
-template <int UB>
-constexpr int t_xd() { return UB >= 2 ? 5 * UB / 2 : 3; }
-template <int UB, int U>
-constexpr int t_w0() { return (5 * UB * U) / 2; }
+// The table entry of a stored byte holds its digits as bf16 codes in digit
+// order: (d0,d1), (d2,d3), (d4,0), (0,d4).  With the layout's digit order, a
+// byte pair covering inputs k..k+9 (k = 10q) multiplies
+//   even byte: .x (x_k, x_k+1)  .y (x_k+2, x_k+3)  .z (x_k+4, x_k+5)
+//   odd byte:  .x (x_k+6, x_k+7)  .y (x_k+8, x_k+9)  .w (x_k+4, x_k+5)
+// so every activation operand is an aligned dword straight from the scalar
+// loads, and no dword straddles a 128-input group edge (the edges are even).
+//
+// Activations come through scalar buffer loads whose range is the x row:
+// dwords past K read as zero, so the last, partial period runs through the
+// same pipelined loop (its codes past K meet zero activations).
 
-template <int M, int UB>
-struct TBuf {
-  u32x4_t e[UB];          // table entries: (c0,c1), (c2,c3), (c4,0) per byte
-  uint32_t xp[M][3 * UB]; // matching x pairs: (x_k0,x_k0+1), (x_k0+2,x_k0+3), (x_k0+4,0)
+__device__ i32x4_t ql_sbuf_load_x4(i32x4_t rsrc, int offset, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v4i32");
+
+// Buffer resource over n_bytes of uniform memory at p (raw, stride 0).
+__device__ __forceinline__ i32x4_t scalar_rsrc(const void* p, uint32_t n_bytes) {
+  const uint64_t v = (uint64_t)p;
+  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)v),
+                 (int)(__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) & 0xFFFFu),
+                 (int)__builtin_amdgcn_readfirstlane(n_bytes), 0x00020000};
+}
+
+constexpr int kTUnit = 8;                   // bytes per pipeline unit (4 byte pairs)
+constexpr int kTUnits = 128 / kTUnit;       // units per period
+constexpr int kTUnitXd = 5 * kTUnit / 2;    // x dwords per unit (20)
+
+struct TEnt {
+  u32x4_t e[kTUnit];
 };
-
-template <int M, int UB>
-struct TRaw {
-  uint32_t r[M][t_xd<UB>()];  // x dwords of a unit's window
+struct TWin {
+  uint32_t r[kTUnitXd];
 };
 
 // LDS table reads of unit U (the addresses come from the chunk ring).
-template <int M, int UB, int U>
-__device__ __forceinline__ void t_lds(TBuf<M, UB>& b, const uint4 (&d)[4], uint32_t lane_off0, const uint8_t* lut,
+template <int U, int R>
+__device__ __forceinline__ void t_lds(TEnt& b, const uint4 (&d)[R], uint32_t lane_off0, const uint8_t* lut,
                                       uint32_t dep) {
   const uint32_t lane_off = lane_off0 + dep;
-  sfor<UB>([&](auto bi) __attribute__((always_inline)) {
-    constexpr int j = U * UB + decltype(bi)::value;  // byte within the period
-    const uint32_t w = word_of(d[(j >> 4) & 3], (j & 15) >> 2);
+  sfor<kTUnit>([&](auto bi) __attribute__((always_inline)) {
+    constexpr int j = U * kTUnit + decltype(bi)::value;  // byte within the period
+    const uint32_t w = word_of(d[(j >> 4) % R], (j & 15) >> 2);
     const uint32_t addr = __builtin_amdgcn_perm(w, lane_off, 0x0C0C0000u | ((4u + (j & 3)) << 8));
     b.e[decltype(bi)::value] = lds_b128(lut + kTLut + addr);
   });
 }
 
-// Scalar loads of unit U's x window.
-template <int M, int UB, int U, bool GUARD>
-__device__ __forceinline__ void t_xraw(TRaw<M, UB>& r, const cu32p (&xb)[M], int kleft, uint32_t dep) {
-  constexpr int W0 = t_w0<UB, U>();
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const cu32p xm = xb[m] + dep;
-    sfor<t_xd<UB>()>([&](auto i) __attribute__((always_inline)) {
-      r.r[m][decltype(i)::value] = xdw<GUARD>(xm, W0 + decltype(i)::value, kleft);
-    });
-  }
-}
-
-// x pairs of unit U from its window, on the scalar unit.  The window arrived
-// one step earlier, so these shifts never wait on the table reads in flight.
-template <int M, int UB, int U>
-__device__ __forceinline__ void t_pairs(TBuf<M, UB>& b, const TRaw<M, UB>& r) {
-  constexpr int base = 2 * t_w0<UB, U>();
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint32_t (&v)[t_xd<UB>()] = r.r[m];
-    sfor<UB>([&](auto bi) __attribute__((always_inline)) {
-      constexpr int q = decltype(bi)::value;
-      constexpr int kk = 5 * (U * UB + q) - base;  // first trit of the byte within the window
-      b.xp[m][3 * q + 0] = wpair<kk>(v);
-      b.xp[m][3 * q + 1] = wpair<kk + 2>(v);
-      b.xp[m][3 * q + 2] = ((kk + 4) & 1) ? (v[(kk + 4) >> 1] >> 16) : (v[(kk + 4) >> 1] & 0xFFFFu);
-    });
-  }
-}
-
-template <int M, int K0>
-__device__ __forceinline__ void t_dot(uint32_t a, uint32_t xp, float (&acc)[5]) {
-  constexpr int g0 = K0 / 128, g1 = (K0 + 1) / 128;
-  if constexpr (g0 == g1) {
-    acc[g0] = dot2(a, xp, acc[g0]);
-  } else {  // a group boundary falls between the two codes
-    acc[g0] = dot2(a, xp & 0x0000FFFFu, acc[g0]);
-    acc[g1] = dot2(a, xp & 0xFFFF0000u, acc[g1]);
-  }
-}
-
-template <int M, int UB, int U>
-__device__ __forceinline__ void t_compute(const TBuf<M, UB>& b, float (&acc)[M][5]) {
-  constexpr int kf = 5 * UB * U;
-  sfor<UB>([&](auto bi) __attribute__((always_inline)) {
-    constexpr int q = decltype(bi)::value;
-    constexpr int k0 = kf + 5 * q;
-    const u32x4_t e = b.e[q];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      t_dot<M, k0>(e.x, b.xp[m][3 * q + 0], acc[m]);
-      t_dot<M, k0 + 2>(e.y, b.xp[m][3 * q + 1], acc[m]);
-      acc[m][(k0 + 4) / 128] = dot2(e.z, b.xp[m][3 * q + 2], acc[m][(k0 + 4) / 128]);
-    }
+// Scalar loads of unit U's x window (x_off: byte offset of the period in x).
+template <int U>
+__device__ __forceinline__ void t_x(TWin& w, i32x4_t xrs, int x_off, uint32_t dep) {
+  sfor<kTUnitXd / 4>([&](auto i) __attribute__((always_inline)) {
+    constexpr int q = decltype(i)::value;
+    const i32x4_t v = ql_sbuf_load_x4(xrs, x_off + (int)dep + 4 * (kTUnitXd * U + 4 * q), 0);
+    w.r[4 * q + 0] = (uint32_t)v.x;
+    w.r[4 * q + 1] = (uint32_t)v.y;
+    w.r[4 * q + 2] = (uint32_t)v.z;
+    w.r[4 * q + 3] = (uint32_t)v.w;
   });
 }
 
-template <int M>
-constexpr int t_ub() { return M == 1 ? 8 : (M == 2 ? 4 : (M <= 4 ? 2 : 1)); }
+template <int U>
+__device__ __forceinline__ void t_compute(const TEnt& b, const TWin& w, float (&acc)[5]) {
+  sfor<kTUnit / 2>([&](auto qi) __attribute__((always_inline)) {
+    constexpr int q = decltype(qi)::value;
+    constexpr int k = 5 * kTUnit * U + 10 * q;  // first input of the byte pair, within the period
+    const u32x4_t A = b.e[2 * q], B = b.e[2 * q + 1];
+    acc[k / 128] = dot2(A.x, w.r[5 * q + 0], acc[k / 128]);
+    acc[(k + 2) / 128] = dot2(A.y, w.r[5 * q + 1], acc[(k + 2) / 128]);
+    acc[(k + 4) / 128] = dot2(A.z, w.r[5 * q + 2], acc[(k + 4) / 128]);
+    acc[(k + 4) / 128] = dot2(B.w, w.r[5 * q + 2], acc[(k + 4) / 128]);
+    acc[(k + 6) / 128] = dot2(B.x, w.r[5 * q + 3], acc[(k + 6) / 128]);
+    acc[(k + 8) / 128] = dot2(B.y, w.r[5 * q + 4], acc[(k + 8) / 128]);
+  });
+}
 
+#ifndef QL_T_RING
+#define QL_T_RING 4  // 16-byte chunks in flight per lane (ternary)
+#endif
+
+// Batch 1 only.  Periods p0..p1-1 of the slab (the last may be partial).
 template <int M>
 __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
-  constexpr int UB = t_ub<M>();
-  constexpr int NU = 128 / UB;  // units per period (even)
+  static_assert(M == 1, "the ternary GEMV runs batch 1");
   if (p0 >= p1) return;
   const int nchunks = (c.K + 79) / 80;
-  const int Pfull = c.K / kPeriodK;
-  const int pe = p1 < Pfull ? p1 : Pfull;
   const uint32_t lane_off = (uint32_t)(c.lane & 15) << 4;
-  // chunks of this wave's periods; later ones read as zero
-  const ChunkSrc src(c.codes, min(nchunks, 8 * p1), c.lane);
-  // ring of 4: chunk ch of a period lives in slot ch & 3; once a chunk's last
-  // byte is addressed its slot takes the chunk four positions later
-  uint4 d[4];
-  sfor<4>([&](auto ch) __attribute__((always_inline)) { d[decltype(ch)::value] = src.load(8 * p0 + decltype(ch)::value); });
-  // Per step U: table reads of unit U+1, x window of unit U+2, dot2 of unit
-  // U, x pairs of unit U+1, one lgkmcnt(0) wait.  Unit u uses buffer u & 1.
-  TBuf<M, UB> A, B;
-  TRaw<M, UB> R0, R1;
-  cu32p xb[M];
-  float acc[M][5];
+  // chunks of the slab; later ones (and the ring's look-ahead past the end) read as zero
+  const ChunkSrc src(c.codes, nchunks, c.lane);
+  const i32x4_t xrs = scalar_rsrc(c.x, (uint32_t)c.K * 2u);
+  // ring of R: chunk ch of a period lives in slot ch % R; once a chunk's last
+  // byte is addressed its slot takes the chunk R positions later
+  constexpr int R = QL_T_RING;
+  static_assert(8 % R == 0, "the ring must divide a period's 8 chunks");
+  uint4 d[R];
+  sfor<R>([&](auto ch) __attribute__((always_inline)) { d[decltype(ch)::value] = src.load(8 * p0 + decltype(ch)::value); });
+  // Per step U: table reads and x window of unit U+1, dot2 of unit U, one
+  // lgkmcnt(0) wait.  Unit u uses entry buffer and window u & 1.
+  TEnt A, B;
+  TWin W0, W1;
+  float acc[5];
   uint32_t dep = 0;
-  if (p0 < pe) {
-    set_xb(xb, c, kPeriodK * p0);
-    t_xraw<M, UB, 0, false>(R0, xb, 0, 0u);
-    lgkm_wait0();
-    t_pairs<M, UB, 0>(A, R0);
-    t_lds<M, UB, 0>(A, d, lane_off, c.lut, 0u);
-    t_xraw<M, UB, 1, false>(R1, xb, 0, 0u);
-    lgkm_wait0();
-  }
-  for (int p = p0; p < pe; ++p) {
+  t_lds<0, R>(A, d, lane_off, c.lut, 0u);
+  t_x<0>(W0, xrs, 2 * kPeriodK * p0, 0u);
+  lgkm_wait0();
+  for (int p = p0; p < p1; ++p) {
     float sc[5];
 #pragma unroll
-    for (int gl = 0; gl < 5; ++gl) sc[gl] = ld_scale(c.scales, 5 * p + gl, c.lane);
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int gl = 0; gl < 5; ++gl) acc[m][gl] = 0.0f;
-    cu32p xn[M];
-    set_xb(xn, c, kPeriodK * (p + 1));
-    const bool more = p + 1 < pe;
-    sfor<NU>([&](auto u) __attribute__((always_inline)) {
+    for (int gl = 0; gl < 5; ++gl) {
+      const int g = 5 * p + gl;
+      const float v = ld_scale(c.scales, g < c.G ? g : c.G - 1, c.lane);
+      sc[gl] = g < c.G ? v : 0.0f;
+      acc[gl] = 0.0f;
+    }
+    const bool more = p + 1 < p1;
+    const int x_off = 2 * kPeriodK * p;
+    sfor<kTUnits>([&](auto u) __attribute__((always_inline)) {
       constexpr int U = decltype(u)::value;
       constexpr bool odd = (U & 1) != 0;
-      auto& cur = odd ? B : A;     // unit U
-      auto& nxt = odd ? A : B;     // unit U+1
-      auto& rn1 = odd ? R0 : R1;   // raw window of unit U+1
-      auto& rn2 = odd ? R1 : R0;   // raw window of unit U+2
-      // 1. table reads of unit U+1
-      if constexpr (U + 1 < NU) {
-        t_lds<M, UB, U + 1>(nxt, d, lane_off, c.lut, dep);
-        constexpr int last_byte = (U + 1) * UB + UB - 1;
+      auto& cur = odd ? B : A;
+      auto& nxt = odd ? A : B;
+      auto& wc = odd ? W1 : W0;
+      auto& wn = odd ? W0 : W1;
+      if constexpr (U + 1 < kTUnits) {
+        t_lds<U + 1, R>(nxt, d, lane_off, c.lut, dep);
+        t_x<U + 1>(wn, xrs, x_off, dep);
+        constexpr int last_byte = (U + 1) * kTUnit + kTUnit - 1;
         if constexpr ((last_byte & 15) == 15) {
           constexpr int ch = last_byte >> 4;
-          d[ch & 3] = src.load(ch < 4 ? 8 * p + ch + 4 : 8 * (p + 1) + ch - 4);
+          d[ch % R] = src.load(ch + R < 8 ? 8 * p + ch + R : 8 * (p + 1) + ch + R - 8);
         }
       } else {
-        if (more) t_lds<M, UB, 0>(nxt, d, lane_off, c.lut, dep);
-      }
-      // 2. x window of unit U+2
-      if constexpr (U + 2 < NU) {
-        t_xraw<M, UB, U + 2, false>(rn2, xb, 0, dep);
-      } else {
-        if (more) t_xraw<M, UB, U + 2 - NU, false>(rn2, xn, 0, dep);
+        if (more) {
+          t_lds<0, R>(nxt, d, lane_off, c.lut, dep);
+          t_x<0>(wn, xrs, x_off + 2 * kPeriodK, dep);
+        }
       }
       sched_fence();
-      // 3. arithmetic of unit U
-      t_compute<M, UB, U>(cur, acc);
-      // 4. x pairs of unit U+1
-      if constexpr (U + 1 < NU) {
-        t_pairs<M, UB, U + 1>(nxt, rn1);
-      } else {
-        if (more) t_pairs<M, UB, 0>(nxt, rn1);
-      }
-      dep = opaque_zero(acc[0][(5 * UB * U) / 128]);
+      t_compute<U>(cur, wc, acc);
+      dep = opaque_zero(acc[(5 * kTUnit * U) / 128]);
       sched_fence();
       lgkm_wait0();
     });
 #pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int gl = 0; gl < 5; ++gl) y[m] = fmaf(sc[gl], acc[m][gl], y[m]);
-#pragma unroll
-    for (int m = 0; m < M; ++m) xb[m] = xn[m];
-  }
-  // last, partial period: trits past K are padding and x past K reads as 0
-  if (p1 > Pfull) {
-    const int p = Pfull;
-    const int kleft = c.K - kPeriodK * p;
-    const int nu = ((kleft + 79) / 80) * (16 / UB);
-    set_xb(xb, c, kPeriodK * p);
-    float sc[5];
-#pragma unroll
-    for (int gl = 0; gl < 5; ++gl) sc[gl] = (5 * p + gl < c.G) ? ld_scale(c.scales, 5 * p + gl, c.lane) : 0.0f;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int gl = 0; gl < 5; ++gl) acc[m][gl] = 0.0f;
-    sfor<NU>([&](auto u) __attribute__((always_inline)) {
-      constexpr int U = decltype(u)::value;
-      if (U < nu) {
-        t_lds<M, UB, U>(A, d, lane_off, c.lut, dep);
-        t_xraw<M, UB, U, true>(R0, xb, kleft, dep);
-        constexpr int last_byte = U * UB + UB - 1;
-        if constexpr ((last_byte & 15) == 15 && (last_byte >> 4) < 4) {
-          constexpr int ch = last_byte >> 4;
-          d[ch] = src.load(8 * p + ch + 4);
-        }
-        lgkm_wait0();
-        t_pairs<M, UB, U>(A, R0);
-        t_compute<M, UB, U>(A, acc);
-        dep = opaque_zero(acc[0][(5 * UB * U) / 128]);
-      }
-    });
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int gl = 0; gl < 5; ++gl) y[m] = fmaf(sc[gl], acc[m][gl], y[m]);
+    for (int gl = 0; gl < 5; ++gl) y[0] = fmaf(sc[gl], acc[gl], y[0]);
   }
 }
 
@@ -672,59 +606,93 @@ __device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, in
 }
 
 // ---------------------------------------------------------------- kernels
-constexpr int kWaves = 8;  // 512 threads; two workgroups (16 waves) per CU
+#ifndef QL_WAVES
+#define QL_WAVES 8
+#endif
+#ifndef QL_WAVES_PER_EU
+#define QL_WAVES_PER_EU 4
+#endif
+#ifndef QL_WG_PER_CU
+#define QL_WG_PER_CU 2
+#endif
+constexpr int kWaves = QL_WAVES;          // waves per workgroup
+constexpr int kWgPerCu = QL_WG_PER_CU;    // resident workgroups per CU (LDS tables: 69 KB each)
 
-// One slab of one descriptor per wave task; persistent workgroups stride over
-// the tasks.  Descriptor fields are re-read per task, which keeps their live
-// ranges short (the kernels stay free of register spills).
+// One wave task: one 64-row slab of one descriptor.  Descriptor fields are
+// re-read per task, which keeps their live ranges short (the kernels stay free
+// of register spills).
 template <int M>
-__device__ __forceinline__ void gemv_tasks(const ql_gemv_desc* __restrict__ descs, int count, int64_t total, int Mact,
-                                           const uint8_t* lut) {
+__device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t, int Mact,
+                                          const uint8_t* lut, int lane) {
+  // descriptor holding slab t: last d with slab_begin <= t
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (descs[mid].slab_begin <= t) lo = mid; else hi = mid - 1;
+  }
+  const ql_gemv_desc& d = descs[lo];
+  const int64_t slab = t - d.slab_begin;
+  const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
+  int gr;
+  const int64_t off = slab_offset(slab, K, d.grid, d.blk_grid, d.blk_off, &gr);
+  float y[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) y[m] = 0.0f;
+  SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off, d.pscales + slab * (int64_t)G8 * kSlab * 8, d.x, K, G,
+               Mact, lane, lut};
+  run_slab<M>(gr, c, 0, (K + kPeriodK - 1) / kPeriodK, y);
+  const int64_t row = slab * kSlab + lane;
+  if (row < d.N)
+    for (int m = 0; m < Mact; ++m) d.y[(int64_t)m * d.N + row] = y[m];
+}
+
+// A single matrix: all slabs cost the same, so waves stride over them.  The
+// descriptor travels in the kernel arguments; `count` (always 1) is a runtime
+// value so its reads stay inside the task loop instead of being hoisted and
+// kept live across it.
+template <int M>
+__global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_kernel(ql_gemv_desc desc, int count, int64_t total, int Mact) {
+  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
+  build_luts(lut);
+  __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t < total; t += (int64_t)gridDim.x * kWaves) {
-    // descriptor holding slab t: last d with slab_begin <= t
-    int lo = 0, hi = count - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (descs[mid].slab_begin <= t) lo = mid; else hi = mid - 1;
-    }
-    const ql_gemv_desc& d = descs[lo];
-    const int64_t slab = t - d.slab_begin;
-    const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
-    int gr;
-    const int64_t off = slab_offset(slab, K, d.grid, d.blk_grid, d.blk_off, &gr);
-    float y[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) y[m] = 0.0f;
-    SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off, d.pscales + slab * (int64_t)G8 * kSlab * 8, d.x, K, G,
-                 Mact, lane, lut};
-    run_slab<M>(gr, c, 0, (K + kPeriodK - 1) / kPeriodK, y);
-    const int64_t row = slab * kSlab + lane;
-    if (row < d.N)
-      for (int m = 0; m < Mact; ++m) d.y[(int64_t)m * d.N + row] = y[m];
+  for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t < total; t += (int64_t)gridDim.x * kWaves)
+    gemv_task<M>(&desc, count, t, Mact, lut, lane);
+}
+
+// Many independent matrices in one persistent launch.  Slab costs differ
+// (row length, grid), so after its first task a wave takes the next one from
+// an atomic ticket counter (sched[0]) when it finishes a task: greedy list
+// scheduling over tasks that the host numbered longest-first.  (A ticket drawn
+// when a task starts would hide the fetch latency but fixes the assignment of
+// the next round at launch time, which balances far worse.)  Every wave then
+// checks out on sched[1]; the last one resets both words, leaving the state
+// zero for the next launch.
+template <int M>
+__global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
+                                                                      int count, int64_t total, int Mact,
+                                                                      uint32_t* __restrict__ sched) {
+  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
+  build_luts(lut);
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t nwaves = gridDim.x * kWaves;
+  int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+  while (t < total) {
+    gemv_task<M>(descs, count, t, Mact, lut, lane);
+    uint32_t ticket = 0;
+    if (lane == 0) ticket = __hip_atomic_fetch_add(sched, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = (int64_t)nwaves + __builtin_amdgcn_readfirstlane(ticket);
   }
-}
-
-// A single matrix: its descriptor travels in the kernel arguments.  `count`
-// (always 1) is a runtime value so the descriptor reads stay inside the task
-// loop instead of being hoisted and kept live across it.
-template <int M>
-__global__ void __launch_bounds__(kWaves * 64, 4) gemv_kernel(ql_gemv_desc desc, int count, int64_t total, int Mact) {
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  build_luts(lut);
-  __syncthreads();
-  gemv_tasks<M>(&desc, count, total, Mact, lut);
-}
-
-// Many independent matrices in one persistent launch.
-template <int M>
-__global__ void __launch_bounds__(kWaves * 64, 4) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
-                                                                      int count, int64_t total, int Mact) {
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  build_luts(lut);
-  __syncthreads();
-  gemv_tasks<M>(descs, count, total, Mact, lut);
+  if (lane == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(sched + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == nwaves - 1) {  // every other wave has drawn its last ticket
+      __hip_atomic_store(sched, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sched + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -749,20 +717,21 @@ hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream) {
   if (M != 1) return hipErrorInvalidValue;
   const int64_t nslabs = ((int64_t)a.N + kSlab - 1) / kSlab;
   const ql_gemv_desc d{a.packed, a.pscales, a.blk_grid, a.blk_off, a.x, a.y, a.N, a.K, a.grid, 0};
-  const int slots = device_cu_count() * 2;  // two resident workgroups per CU
+  const int slots = device_cu_count() * kWgPerCu;
   const int64_t wg_needed = (nslabs + kWaves - 1) / kWaves;
   const int grid = (int)(wg_needed < slots ? wg_needed : slots);
   hipLaunchKernelGGL(gemv_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, d, 1, nslabs, 1);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M,
+hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M, uint32_t* sched,
                                hipStream_t stream) {
   if (M != 1) return hipErrorInvalidValue;
-  const int slots = device_cu_count() * 2;
+  const int slots = device_cu_count() * kWgPerCu;
   const int64_t wg_needed = (total_slabs + kWaves - 1) / kWaves;
   const int grid = (int)(wg_needed < slots ? wg_needed : slots);
-  hipLaunchKernelGGL(gemv_grouped_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, descs, count, total_slabs, 1);
+  hipLaunchKernelGGL(gemv_grouped_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, descs, count, total_slabs, 1,
+                     sched);
   return hipGetLastError();
 }
 

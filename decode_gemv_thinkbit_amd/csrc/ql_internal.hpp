@@ -27,7 +27,7 @@ struct MatArgs {
 };
 
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
-hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M,
+hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M, uint32_t* sched,
                                hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream);

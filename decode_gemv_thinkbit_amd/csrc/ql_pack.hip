@@ -64,11 +64,12 @@ __device__ inline uint32_t row_byte_value(const int8_t* __restrict__ codes, int6
                                           int64_t jj, int gr) {
   const int cmin = grid_cmin(gr);
   if (gr == QL_GRID_T) {
-    // five trits, least significant = lowest k
+    // five trits in input order (least significant = lowest k), then the
+    // byte's stored digit order
     uint32_t v = 0;
 #pragma unroll
     for (int i = 4; i >= 0; --i) v = v * 3 + digit(codes, N, K, n, 5 * jj + i, cmin);
-    return v;
+    return tern_from_input_order(v, jj);
   }
   if (gr == QL_GRID_I2) {
     uint32_t v = 0;
@@ -130,7 +131,7 @@ __device__ inline uint32_t packed_row_byte(const uint8_t* __restrict__ slab, int
 __device__ inline int decode_code(const uint8_t* __restrict__ slab, int64_t r, int64_t k, int64_t K, int gr) {
   uint32_t u;
   if (gr == QL_GRID_T) {
-    uint32_t b = packed_row_byte(slab, r, k / 5);
+    uint32_t b = tern_to_input_order(packed_row_byte(slab, r, k / 5), k / 5);
     const int i = (int)(k % 5);
     for (int t = 0; t < i; ++t) b /= 3;
     u = b % 3;

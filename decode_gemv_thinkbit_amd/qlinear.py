@@ -17,6 +17,7 @@ import torch
 
 GRID_T, GRID_I2, GRID_I3, GRID_MIXED = 0, 1, 2, 3
 GROUP, SLAB, BLOCK = 128, 64, 128
+QL_SCHED_WORDS = 4  # uint32 words of grouped-launch scheduler state
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "libqlinear.so")
@@ -61,7 +62,7 @@ def lib():
         L.qlinear_gemv.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
         L.qlinear_grouped_prepare.argtypes = [vp, ctypes.c_int32]
         L.qlinear_grouped_prepare.restype = i64
-        L.qlinear_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp]
+        L.qlinear_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp, vp]
         L.qlinear_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.qlinear_gemm_workspace_bytes.restype = sz
         L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -266,7 +267,10 @@ class GroupedGemv:
         raw = bytes(memoryview(arr))
         self.count = len(items)
         self.descs = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(items[0][1].device)
+        # task-counter state: zero once here, left zero by every completed launch
+        self.sched = torch.zeros(QL_SCHED_WORDS, dtype=torch.int32, device=items[0][1].device)
 
     def run(self):
-        _check(lib().qlinear_gemv_grouped(_ptr(self.descs), self.count, self.total, self.M, _stream()),
+        _check(lib().qlinear_gemv_grouped(_ptr(self.descs), self.count, self.total, self.M, _ptr(self.sched),
+                                          _stream()),
                "gemv_grouped")

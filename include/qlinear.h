@@ -13,11 +13,16 @@
  * Notation: W is [N][K] (N output rows, K input columns, K % 128 == 0),
  * x is [M][K] bf16, y = x * W^T is [M][N] fp32.
  *
- * Packed layout, version 1 (this project's definition; the pages fix no bit
+ * Packed layout, version 2 (this project's definition; the pages fix no bit
  * order).  u = c - c_min is stored (ternary c+1, 2-bit c+2, 3-bit c+4).
  *   row bytes: ternary 16*ceil(K/80); 2-bit K/4; 3-bit 3K/8.
- *   ternary: byte j of a row = sum_{i<5} u[5j+i] * 3^i (lowest k least
- *            significant); trits past K are padding with c = 0; bytes <= 242.
+ *   ternary: byte j of a row holds inputs 5j..5j+4 as a base-3 number,
+ *            byte = sum_{i<5} u[k(j,i)] * 3^i, with k(j,i) = 5j+i for even j
+ *            and, for odd j, k(j,i) = 5j+1+i (i < 4), k(j,4) = 5j.  Read as a
+ *            pair, bytes 2q, 2q+1 then hold every even-aligned input pair of
+ *            10q..10q+9 as adjacent digits except (10q+4, 10q+5), so a kernel
+ *            can multiply decoded code pairs against aligned activation pairs.
+ *            Trits past K are padding with c = 0; bytes <= 242.
  *   2-bit:   little-endian 32-bit word j holds k = 16j+i at bits [2i, 2i+1].
  *   3-bit:   96-bit triple t (words w0,w1,w2 read as w0 | w1<<32 | w2<<64)
  *            holds k = 32t+i at bits [3i, 3i+2].
@@ -62,7 +67,7 @@ extern "C" {
 #define QL_GROUP 128 /* weights per scale, along K */
 #define QL_SLAB 64   /* rows per interleaved slab */
 #define QL_BLOCK 128 /* rows per grid block */
-#define QL_LAYOUT_VERSION 1
+#define QL_LAYOUT_VERSION 2
 
 typedef enum { QL_GRID_T = 0, QL_GRID_I2 = 1, QL_GRID_I3 = 2, QL_GRID_MIXED = 3 } ql_grid;
 typedef enum { QL_OK = 0, QL_EINVAL = 1, QL_EUNSUPPORTED = 2, QL_EHIP = 3 } ql_status;
@@ -151,15 +156,27 @@ typedef struct {
   int32_t slab_begin;       /* filled by qlinear_grouped_prepare */
 } ql_gemv_desc;
 
-/* Fill slab_begin of every descriptor (host array) and return the total number of 64-row
- * slabs (the task count), or -1 on a bad descriptor. */
+/* Prepare a descriptor list (host array) for qlinear_gemv_grouped: check every entry, sort
+ * the entries by K, largest first (stable; the products are independent, so their order
+ * is free), fill slab_begin and return the total number of 64-row slabs (the task count),
+ * or -1 on a bad descriptor.  Longest-first task order plus dynamic task fetching keeps
+ * the persistent launch balanced when row lengths differ (a K = 12288 row costs three
+ * K = 4096 rows). */
 int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
+
+/* Words of the task-scheduler state of a grouped launch. */
+#define QL_SCHED_WORDS 4
 
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
  * descs (dev), count entries) at batch M = 1 in one persistent launch; other M return
- * QL_EUNSUPPORTED.  The products are independent: no y may alias another entry's x or y. */
+ * QL_EUNSUPPORTED.  Waves take 64-row slab tasks from an atomic counter in `sched`
+ * (dev, QL_SCHED_WORDS uint32, 16-byte aligned, owned by the caller): it must be all
+ * zero when a launch starts, and every launch that runs to completion leaves it zero
+ * again, so one zeroing at allocation serves any number of launches.  Launches that
+ * share one sched buffer must not overlap (enqueue them on one stream).  The products
+ * are independent: no y may alias another entry's x or y. */
 ql_status qlinear_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_slabs, int32_t M,
-                               hipStream_t stream);
+                               uint32_t *sched, hipStream_t stream);
 
 /* Batched GEMM for 1 <= M (tuned for 16..512): tiles of codes are decoded into LDS as bf16
  * (codes are exact in bf16) and contracted on MFMA (bf16 x bf16 -> fp32); the group scale

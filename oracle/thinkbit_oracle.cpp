@@ -18,11 +18,11 @@
 //     scale is the operation the k-quant calibration page
 //     (sotaaz.com/post/quantized-model-less-sure, section "Open question")
 //     shows to reproduce stored codes exactly.
-//   * The packed layout (five trits per byte in base 3, sixteen 2-bit codes
-//     per 32-bit word, thirty-two 3-bit codes per 96-bit triple, 64-row
-//     slabs, 128-row grid blocks) is this project's own definition; the
-//     pages fix no bit order.  It is written out once more, independently,
-//     in the HIP packer.
+//   * The packed layout, version 2 (five trits per byte in base 3 with the
+//     digit order of tern_input below, sixteen 2-bit codes per 32-bit word,
+//     thirty-two 3-bit codes per 96-bit triple, 64-row slabs, 128-row grid
+//     blocks) is this project's own definition; the pages fix no bit order.
+//     It is written out once more, independently, in the HIP packer.
 //
 // Precision: codes are decided from an fp64 quotient; w = c*s is formed in
 // fp32 (exact: at most 11 significant bits); products and sums are fp64,
@@ -83,17 +83,28 @@ inline int code_at(const int8_t* codes, int64_t K, int64_t n, int64_t k) {
   return k < K ? codes[n * K + k] : 0;
 }
 
+// Ternary digit order (layout version 2).  Byte j holds the five inputs
+// 5j..5j+4.  In an even byte, digit i (weight 3^i) is input 5j+i.  In an odd
+// byte, digits 0..3 are inputs 5j+1..5j+4 and digit 4 is input 5j.  Read as a
+// pair, bytes 2q and 2q+1 cover inputs 10q..10q+9, and every even-aligned input
+// pair (2t, 2t+1) except (10q+4, 10q+5) lies inside one byte in digit order;
+// the pages fix no order within a byte, so this one is chosen to line pairs up.
+inline int64_t tern_input(int64_t j, int i) {
+  if ((j & 1) == 0) return 5 * j + i;
+  return i < 4 ? 5 * j + 1 + i : 5 * j;
+}
+
 // Bytes of one row in the grid's own order (before slab interleave).
 void pack_row(int grid, int64_t K, const int8_t* codes, int64_t n, uint8_t* out) {
   const int64_t rb = row_bytes_of(grid, K);
   const int cmin = cmin_of(grid);
   std::memset(out, 0, rb);
   if (grid == GRID_T) {
-    // byte j = sum_{i=0..4} u_{5j+i} * 3^i, u = c + 1 (least significant trit = lowest k)
+    // byte j = sum_{i=0..4} u(tern_input(j, i)) * 3^i, u = c + 1
     for (int64_t j = 0; j < rb; ++j) {
       int v = 0, p = 1;
       for (int i = 0; i < 5; ++i) {
-        v += (code_at(codes, K, n, 5 * j + i) - cmin) * p;
+        v += (code_at(codes, K, n, tern_input(j, i)) - cmin) * p;
         p *= 3;
       }
       out[j] = (uint8_t)v;
@@ -131,7 +142,7 @@ bool unpack_row(int grid, int64_t K, const uint8_t* in, int8_t* row) {
       int v = in[j];
       if (v > 242) return false;
       for (int i = 0; i < 5; ++i) {
-        int64_t k = 5 * j + i;
+        const int64_t k = tern_input(j, i);
         if (k < K) row[k] = (int8_t)(v % 3 + cmin);
         v /= 3;
       }

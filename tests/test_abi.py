@@ -36,7 +36,7 @@ def test_sizes():
     assert ql.packed_scales_len(70, 1280) == 2 * 2 * 64 * 8
     off = ql.block_offsets(300, 384, [0, 2, 1])
     assert list(off) == [0, 128 * 80, 128 * 80 + 128 * 144, 128 * 80 + 128 * 144 + 64 * 96]  # T row 80 B at K=384
-    assert ql.lib().qlinear_version() == 1
+    assert ql.lib().qlinear_version() == 2
 
 
 def test_sizes_match_oracle(ora):
@@ -83,8 +83,10 @@ def test_other_argument_errors():
     assert L.qlinear_pack(4, 128, 3, None, None, FAKE, FAKE, None) == 1
     assert L.qlinear_unpack(4, 128, 9, None, None, FAKE, FAKE, None) == 1
     assert L.qlinear_dequant(4, 128, 0, None, None, None, FAKE, 0, FAKE, None) == 1
-    assert L.qlinear_gemv_grouped(FAKE, 0, 10, 1, None) == 1
-    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 9, None) == 1
+    assert L.qlinear_gemv_grouped(FAKE, 0, 10, 1, FAKE, None) == 1
+    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 9, FAKE, None) == 1
+    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 1, None, None) == 1  # no scheduler state
+    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 1, MISALIGNED, None) == 1
     bad = np.array([0, 7], np.int8)
     with pytest.raises(ql.QLinearError):
         ql.block_offsets(200, 128, bad)
@@ -95,3 +97,20 @@ def test_binding_rejects_host_tensors():
     pw = ql.PackedWeight(torch.zeros(16, dtype=torch.uint8), torch.zeros(8, dtype=torch.bfloat16), 1, 128, 0)
     with pytest.raises(ValueError):
         ql.gemv(torch.zeros(1, 128, dtype=torch.bfloat16), pw)
+
+
+def test_grouped_prepare_orders_longest_rows_first():
+    """prepare sorts entries by K (largest first, stable) and numbers their slabs in that order."""
+    L = ql.lib()
+    shapes = [(100, 4096, 0), (64, 12288, 1), (300, 4096, 2), (1, 128, 0), (130, 12288, 0)]
+    arr = (ql.ql_gemv_desc * len(shapes))()
+    for i, (N, K, g) in enumerate(shapes):
+        arr[i] = ql.ql_gemv_desc(FAKE, FAKE, None, None, FAKE, FAKE, N, K, g, -1)
+        arr[i].slab_begin = i  # tag, overwritten by prepare
+    tags = {(N, K, g): i for i, (N, K, g) in enumerate(shapes)}
+    total = L.qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(shapes))
+    got = [(d.N, d.K, d.grid) for d in arr]
+    assert got == sorted(shapes, key=lambda s: (-s[1], tags[s]))
+    begins = [d.slab_begin for d in arr]
+    assert begins == list(np.cumsum([0] + [(n + 63) // 64 for n, _, _ in got])[:-1])
+    assert total == sum((n + 63) // 64 for n, _, _ in shapes)

@@ -167,6 +167,34 @@ def test_grouped_gemv_parity(ora, dev):
             assert err <= GEMV_TOL and normwise <= TRIP_GEMV, (pw.N, pw.K, err, normwise)
 
 
+def test_grouped_gemv_repeats_and_matches_single_launches(ora, dev):
+    """Tasks are drawn from an atomic counter in longest-first order; every launch leaves the
+    counter zero, repeated launches are bitwise identical, and each product equals the
+    single-matrix launch bitwise (the per-row arithmetic does not depend on which wave runs it)."""
+    note("grouped gemv repeated")
+    cases = [(64, 4096, T), (300, 12288, "mixed"), (1, 640, I3), (4096, 4096, I2), (200, 1280, T), (128, 12288, I3)]
+    items = []
+    for i, (N, K, grid) in enumerate(cases):
+        pw, x, _, _, _ = _gemv_case_dev(dev, N, K, grid, seed=900 + i)
+        items.append((pw, x, torch.full((1, N), float("nan"), device=dev)))
+    grp = ql.GroupedGemv(items)
+    outs = []
+    for _ in range(3):
+        grp.run()
+        torch.cuda.synchronize()
+        assert int(grp.sched.abs().sum().item()) == 0
+        outs.append([y.clone() for _, _, y in items])
+    for (pw, x, y), y1, y2 in zip(items, outs[1], outs[2]):
+        assert torch.equal(y, y1) and torch.equal(y, y2)
+        assert torch.equal(y, ql.gemv(x, pw))
+
+
+def _gemv_case_dev(dev, N, K, grid, seed):
+    g = grid_arg(N, grid, seed=seed)
+    W = synth.weight(N, K, seed=seed, device=dev)
+    return ql.quantize_pack(W, g), synth.activations(1, K, seed=seed + 1, device=dev), None, None, None
+
+
 def test_workload_linear2048_i2(ora, dev):
     """One 2048x2048 linear, uniform 2-bit grid, batch 1, at full size."""
     note("workload linear2048_i2")

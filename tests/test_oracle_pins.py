@@ -186,21 +186,45 @@ def _packed_row(ora, codes_row, grid):
     return np.concatenate([p[c * 1024:c * 1024 + 16] for c in range(rb // 16)])
 
 
+def _tern_input(j, i):
+    """Input index of digit i (weight 3^i) of ternary byte j, layout version 2: even bytes hold
+    inputs 5j..5j+4 in digit order; odd bytes hold inputs 5j+1..5j+4 as digits 0..3 and input 5j
+    as digit 4 (so the input pairs (10q+6, 10q+7) and (10q+8, 10q+9) are digit pairs (0,1), (2,3))."""
+    if j % 2 == 0:
+        return 5 * j + i
+    return 5 * j + 1 + i if i < 4 else 5 * j
+
+
 def test_ternary_every_byte_value(ora):
-    """All 243 trit tuples <-> byte values 0..242; byte = the tuple read as a base-3 number with
-    the lowest k as the least significant digit (Python int(..., 3) as the independent decoder)."""
-    K = 1280  # 256 bytes, exactly 16 chunks
-    for start in range(0, 243, 256):
+    """All 243 trit tuples <-> byte values 0..242, in even and in odd bytes; byte = the tuple read as
+    a base-3 number, digit i taken from input _tern_input(j, i) (Python int(..., 3) as the
+    independent decoder)."""
+    K = 2560  # 512 bytes, exactly 32 chunks
+    for parity in (0, 1):
         codes = np.zeros(K, np.int8)
-        vals = list(range(243))
-        for j, v in enumerate(vals):
+        js = [2 * v + parity for v in range(243)]
+        for v, j in zip(range(243), js):
             digits = np.base_repr(v, 3).zfill(5)[::-1]  # least significant first
-            codes[5 * j:5 * j + 5] = [int(d) - 1 for d in digits]
+            for i in range(5):
+                codes[_tern_input(j, i)] = int(digits[i]) - 1
         row = _packed_row(ora, codes, T)
-        for j, v in enumerate(vals):
-            trits = "".join(str(c + 1) for c in codes[5 * j:5 * j + 5])
-            assert row[j] == v == int(trits[::-1], 3)
+        for v, j in zip(range(243), js):
+            digits = "".join(str(codes[_tern_input(j, i)] + 1) for i in range(5))
+            assert row[j] == v == int(digits[::-1], 3)
         assert np.array_equal(ora.unpack(ora.pack(codes[None], T), 1, K, T)[0], codes)
+
+
+def test_ternary_odd_byte_digit_order(ora):
+    """A single -1 (digit 0) among 0 codes (digit 1) at each input of a byte pair lands on the
+    digit the layout names: byte value 121 - 3^digit."""
+    for k in range(10, 20):
+        codes = np.zeros(128, np.int8)
+        codes[k] = -1
+        row = _packed_row(ora, codes, T)
+        j = k // 5
+        digit = {10: 0, 11: 1, 12: 2, 13: 3, 14: 4, 15: 4, 16: 0, 17: 1, 18: 2, 19: 3}[k]
+        assert row[j] == 121 - 3 ** digit, (k, row[j])
+        assert all(row[i] == 121 for i in range(26) if i != j)
 
 
 def test_ternary_rejects_bytes_above_242(ora):
@@ -218,7 +242,8 @@ def test_ternary_padding(ora):
     assert ora.row_bytes(T, 128) == 32 and ora.row_bytes(T, 4096) == 832 and ora.row_bytes(T, 5120) == 1024
     row = _packed_row(ora, -np.ones(128, np.int8), T)
     assert np.all(row[:25] == 0)
-    assert row[25] == 0 + 0 * 3 + 0 * 9 + 1 * 27 + 1 * 81  # trits 125..127 are -1, 128..129 padding
+    # byte 25 (odd): digits 0..3 = inputs 126..129 (126, 127 are -1; 128, 129 padding), digit 4 = 125
+    assert row[25] == 0 + 0 * 3 + 1 * 9 + 1 * 27 + 0 * 81
     assert np.all(row[26:] == 121)  # five padding digits of 1: 1+3+9+27+81
 
 
