@@ -144,14 +144,23 @@ __device__ __forceinline__ void sfor(F&& f) {
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// A uniform zero that the compiler cannot see through, computed from v.  The
-// next unit's addresses add it, so its loads cannot be hoisted above the
-// arithmetic that produced v (which would keep several units' operands live
-// at once and spill).
-__device__ __forceinline__ uint32_t opaque_zero(float v) {
-  uint32_t z = __builtin_amdgcn_readfirstlane(__float_as_uint(v));
-  asm("s_mov_b32 %0, 0" : "+s"(z));
-  return z;
+// Compiler-only step boundaries (empty asm, no instruction).  pin_v/pin_s
+// claim to rewrite a value, so address arithmetic that reads it (and the loads
+// it feeds) stays below this point.  `after` also reads the step's
+// accumulators, so the step's arithmetic stays above it.  Together they keep
+// one unit of operands in flight: without them the compiler sinks arithmetic
+// below later loads and keeps several units live (and spills).
+__device__ __forceinline__ void pin_v(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin_s(int& v) { asm volatile("" : "+s"(v)); }
+template <int M>
+__device__ __forceinline__ void pin_s(cu32p (&p)[M]) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) asm volatile("" : "+s"(p[m]));
+}
+template <int N>
+__device__ __forceinline__ void after(uint32_t& v, const float (&acc)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v) : "v"(acc[i]));
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -273,9 +282,7 @@ struct TWin {
 
 // LDS table reads of unit U (the addresses come from the chunk ring).
 template <int U, int R>
-__device__ __forceinline__ void t_lds(TEnt& b, const uint4 (&d)[R], uint32_t lane_off0, const uint8_t* lut,
-                                      uint32_t dep) {
-  const uint32_t lane_off = lane_off0 + dep;
+__device__ __forceinline__ void t_lds(TEnt& b, const uint4 (&d)[R], uint32_t lane_off, const uint8_t* lut) {
   sfor<kTUnit>([&](auto bi) __attribute__((always_inline)) {
     constexpr int j = U * kTUnit + decltype(bi)::value;  // byte within the period
     const uint32_t w = word_of(d[(j >> 4) % R], (j & 15) >> 2);
@@ -286,10 +293,10 @@ __device__ __forceinline__ void t_lds(TEnt& b, const uint4 (&d)[R], uint32_t lan
 
 // Scalar loads of unit U's x window (x_off: byte offset of the period in x).
 template <int U>
-__device__ __forceinline__ void t_x(TWin& w, i32x4_t xrs, int x_off, uint32_t dep) {
+__device__ __forceinline__ void t_x(TWin& w, i32x4_t xrs, int x_off) {
   sfor<kTUnitXd / 4>([&](auto i) __attribute__((always_inline)) {
     constexpr int q = decltype(i)::value;
-    const i32x4_t v = ql_sbuf_load_x4(xrs, x_off + (int)dep + 4 * (kTUnitXd * U + 4 * q), 0);
+    const i32x4_t v = ql_sbuf_load_x4(xrs, x_off + 4 * (kTUnitXd * U + 4 * q), 0);
     w.r[4 * q + 0] = (uint32_t)v.x;
     w.r[4 * q + 1] = (uint32_t)v.y;
     w.r[4 * q + 2] = (uint32_t)v.z;
@@ -322,7 +329,7 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
   static_assert(M == 1, "the ternary GEMV runs batch 1");
   if (p0 >= p1) return;
   const int nchunks = (c.K + 79) / 80;
-  const uint32_t lane_off = (uint32_t)(c.lane & 15) << 4;
+  uint32_t lane_off = (uint32_t)(c.lane & 15) << 4;
   // chunks of the slab; later ones (and the ring's look-ahead past the end) read as zero
   const ChunkSrc src(c.codes, nchunks, c.lane);
   const i32x4_t xrs = scalar_rsrc(c.x, (uint32_t)c.K * 2u);
@@ -337,9 +344,8 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
   TEnt A, B;
   TWin W0, W1;
   float acc[5];
-  uint32_t dep = 0;
-  t_lds<0, R>(A, d, lane_off, c.lut, 0u);
-  t_x<0>(W0, xrs, 2 * kPeriodK * p0, 0u);
+  t_lds<0, R>(A, d, lane_off, c.lut);
+  t_x<0>(W0, xrs, 2 * kPeriodK * p0);
   lgkm_wait0();
   for (int p = p0; p < p1; ++p) {
     float sc[5];
@@ -351,7 +357,7 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
       acc[gl] = 0.0f;
     }
     const bool more = p + 1 < p1;
-    const int x_off = 2 * kPeriodK * p;
+    int x_off = 2 * kPeriodK * p;
     sfor<kTUnits>([&](auto u) __attribute__((always_inline)) {
       constexpr int U = decltype(u)::value;
       constexpr bool odd = (U & 1) != 0;
@@ -360,8 +366,8 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
       auto& wc = odd ? W1 : W0;
       auto& wn = odd ? W0 : W1;
       if constexpr (U + 1 < kTUnits) {
-        t_lds<U + 1, R>(nxt, d, lane_off, c.lut, dep);
-        t_x<U + 1>(wn, xrs, x_off, dep);
+        t_lds<U + 1, R>(nxt, d, lane_off, c.lut);
+        t_x<U + 1>(wn, xrs, x_off);
         constexpr int last_byte = (U + 1) * kTUnit + kTUnit - 1;
         if constexpr ((last_byte & 15) == 15) {
           constexpr int ch = last_byte >> 4;
@@ -369,14 +375,15 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
         }
       } else {
         if (more) {
-          t_lds<0, R>(nxt, d, lane_off, c.lut, dep);
-          t_x<0>(wn, xrs, x_off + 2 * kPeriodK, dep);
+          t_lds<0, R>(nxt, d, lane_off, c.lut);
+          t_x<0>(wn, xrs, x_off + 2 * kPeriodK);
         }
       }
       sched_fence();
       t_compute<U>(cur, wc, acc);
-      dep = opaque_zero(acc[(5 * kTUnit * U) / 128]);
+      after(lane_off, acc);
       sched_fence();
+      pin_s(x_off);
       lgkm_wait0();
     });
 #pragma unroll
@@ -397,10 +404,9 @@ struct I2Buf {
 
 // ring: 4 chunks = 2 groups; group slot S (0, 1) holds chunks 2S, 2S+1
 template <int M, int S, int U>
-__device__ __forceinline__ void i2_issue(I2Buf<M>& b, const uint4 (&d)[4], uint32_t lane_off0, const uint8_t* lut,
-                                         const cu32p (&xb)[M], uint32_t dep) {
+__device__ __forceinline__ void i2_issue(I2Buf<M>& b, const uint4 (&d)[4], uint32_t lane_off, const uint8_t* lut,
+                                         const cu32p (&xb)[M]) {
   constexpr int UB = i2_ub<M>();
-  const uint32_t lane_off = lane_off0 + dep;
   sfor<UB>([&](auto bi) __attribute__((always_inline)) {
     constexpr int j = U * UB + decltype(bi)::value;  // byte within the group (0..31)
     const uint32_t w = word_of(d[2 * S + (j >> 4)], (j & 15) >> 2);
@@ -410,7 +416,7 @@ __device__ __forceinline__ void i2_issue(I2Buf<M>& b, const uint4 (&d)[4], uint3
 #pragma unroll
   for (int m = 0; m < M; ++m)
     sfor<2 * UB>([&](auto i) __attribute__((always_inline)) {
-      b.x[m][decltype(i)::value] = (xb[m] + dep)[2 * U * UB + decltype(i)::value];
+      b.x[m][decltype(i)::value] = xb[m][2 * U * UB + decltype(i)::value];
     });
 }
 
@@ -431,15 +437,14 @@ template <int M>
 __device__ void run_i2(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
   constexpr int NU = 32 / i2_ub<M>();  // units per group
   if (g0 >= g1) return;
-  const uint32_t lane_off = (uint32_t)(c.lane & 3) << 3;
+  uint32_t lane_off = (uint32_t)(c.lane & 3) << 3;
   const ChunkSrc src(c.codes, 2 * g1, c.lane);
   uint4 d[4];
   sfor<4>([&](auto q) __attribute__((always_inline)) { d[decltype(q)::value] = src.load(2 * g0 + decltype(q)::value); });
   I2Buf<M> A, B;
   cu32p xb[M];
   set_xb(xb, c, kGroup * g0);
-  uint32_t dep = 0;
-  i2_issue<M, 0, 0>(A, d, lane_off, c.lut, xb, 0u);
+  i2_issue<M, 0, 0>(A, d, lane_off, c.lut, xb);
   lgkm_wait0();
   for (int gb = g0; gb < g1; gb += 2) {
     sfor<2>([&](auto s_) __attribute__((always_inline)) {
@@ -458,15 +463,15 @@ __device__ void run_i2(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
           constexpr bool even = ((S * NU + U) & 1) == 0;  // buffer of this unit
           if constexpr (U + 1 < NU) {
             if constexpr (even)
-              i2_issue<M, S, U + 1>(B, d, lane_off, c.lut, xb, dep);
+              i2_issue<M, S, U + 1>(B, d, lane_off, c.lut, xb);
             else
-              i2_issue<M, S, U + 1>(A, d, lane_off, c.lut, xb, dep);
+              i2_issue<M, S, U + 1>(A, d, lane_off, c.lut, xb);
           } else {
             if (more) {
               if constexpr (even)
-                i2_issue<M, S ^ 1, 0>(B, d, lane_off, c.lut, xn, dep);
+                i2_issue<M, S ^ 1, 0>(B, d, lane_off, c.lut, xn);
               else
-                i2_issue<M, S ^ 1, 0>(A, d, lane_off, c.lut, xn, dep);
+                i2_issue<M, S ^ 1, 0>(A, d, lane_off, c.lut, xn);
             }
             // every byte of this group is addressed: its slot takes group g + 2
             d[2 * S] = src.load(2 * (g + 2));
@@ -477,8 +482,10 @@ __device__ void run_i2(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
             i2_compute<M>(A, acc);
           else
             i2_compute<M>(B, acc);
-          dep = opaque_zero(acc[0]);
+          after(lane_off, acc);
           sched_fence();
+          pin_s(xb);
+          pin_s(xn);
           lgkm_wait0();
         });
 #pragma unroll
@@ -504,14 +511,15 @@ struct I3Buf {
 // triple T (0..3) of group slot S: words 3T..3T+2 of the slot's 3 chunks (12 words)
 template <int M, int S, int U>
 __device__ __forceinline__ void i3_issue(I3Buf<M>& b, const uint4 (&d)[6], const uint8_t* lut, const cu32p (&xb)[M],
-                                         uint32_t dep) {
+                                         uint32_t tok) {
   constexpr int NP = i3_np<M>();
   constexpr int T = (U * NP) / 16;   // triple within the group
   constexpr int P0 = (U * NP) % 16;  // first pair within the triple
   constexpr int wb = 3 * T;          // first word of the triple within the group
-  const uint32_t w0 = word_of(d[3 * S + (wb >> 2)], wb & 3) + dep;
-  const uint32_t w1 = word_of(d[3 * S + ((wb + 1) >> 2)], (wb + 1) & 3) + dep;
-  const uint32_t w2 = word_of(d[3 * S + ((wb + 2) >> 2)], (wb + 2) & 3) + dep;
+  uint32_t w0 = word_of(d[3 * S + (wb >> 2)], wb & 3);
+  uint32_t w1 = word_of(d[3 * S + ((wb + 1) >> 2)], (wb + 1) & 3);
+  uint32_t w2 = word_of(d[3 * S + ((wb + 2) >> 2)], (wb + 2) & 3);
+  asm volatile("" : "+v"(w0), "+v"(w1), "+v"(w2) : "v"(tok));  // table reads stay in this step
   sfor<NP>([&](auto pi) __attribute__((always_inline)) {
     constexpr int P = P0 + decltype(pi)::value;
     b.e[decltype(pi)::value] = lds_b32(lut + kI3Lut + i3_field_x4<P>(w0, w1, w2));
@@ -519,7 +527,7 @@ __device__ __forceinline__ void i3_issue(I3Buf<M>& b, const uint4 (&d)[6], const
 #pragma unroll
   for (int m = 0; m < M; ++m)
     sfor<NP>([&](auto i) __attribute__((always_inline)) {
-      b.x[m][decltype(i)::value] = (xb[m] + dep)[16 * T + P0 + decltype(i)::value];
+      b.x[m][decltype(i)::value] = xb[m][16 * T + P0 + decltype(i)::value];
     });
 }
 
@@ -542,8 +550,8 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
   I3Buf<M> A, B;
   cu32p xb[M];
   set_xb(xb, c, kGroup * g0);
-  uint32_t dep = 0;
-  i3_issue<M, 0, 0>(A, d, c.lut, xb, 0u);
+  uint32_t tok = 0;  // step token: rewritten (as far as the compiler knows) after each step's arithmetic
+  i3_issue<M, 0, 0>(A, d, c.lut, xb, tok);
   lgkm_wait0();
   for (int gb = g0; gb < g1; gb += 2) {
     sfor<2>([&](auto s_) __attribute__((always_inline)) {
@@ -562,15 +570,15 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
           constexpr bool even = ((S * NU + U) & 1) == 0;
           if constexpr (U + 1 < NU) {
             if constexpr (even)
-              i3_issue<M, S, U + 1>(B, d, c.lut, xb, dep);
+              i3_issue<M, S, U + 1>(B, d, c.lut, xb, tok);
             else
-              i3_issue<M, S, U + 1>(A, d, c.lut, xb, dep);
+              i3_issue<M, S, U + 1>(A, d, c.lut, xb, tok);
           } else {
             if (more) {
               if constexpr (even)
-                i3_issue<M, S ^ 1, 0>(B, d, c.lut, xn, dep);
+                i3_issue<M, S ^ 1, 0>(B, d, c.lut, xn, tok);
               else
-                i3_issue<M, S ^ 1, 0>(A, d, c.lut, xn, dep);
+                i3_issue<M, S ^ 1, 0>(A, d, c.lut, xn, tok);
             }
 #pragma unroll
             for (int q = 0; q < 3; ++q) d[3 * S + q] = src.load(3 * (g + 2) + q);
@@ -580,8 +588,10 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
             i3_compute<M>(A, acc);
           else
             i3_compute<M>(B, acc);
-          dep = opaque_zero(acc[0]);
+          after(tok, acc);
           sched_fence();
+          pin_s(xb);
+          pin_s(xn);
           lgkm_wait0();
         });
 #pragma unroll
