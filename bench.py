@@ -14,8 +14,10 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -23,6 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Sources whose code decides the GEMV kernel's memory traffic; a traffic figure
+# measured with rocprofv3 counters is reported only while their hash matches.
+KERNEL_SOURCES = ["decode_gemv_thinkbit_amd/csrc/ql_gemv.hip", "decode_gemv_thinkbit_amd/csrc/ql_device.hpp",
+                  "decode_gemv_thinkbit_amd/csrc/ql_internal.hpp"]
+TRAFFIC_SUMMARY = "profiles/gemv_grouped_qwen3_8b_pass.md"
 METRIC = "packed-weight GB/s & % HBM peak, batch-1 GEMV; µs per 8B-shape decode weight pass"
 
 
@@ -57,6 +64,39 @@ def build_pass(wl, wl_index, M, dev):
             log(f"  packed layers 0..{layer}")
     torch.cuda.synchronize()
     return items, meta, stored, xs
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken on these sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+kernel_sources_sha256:\s*([0-9a-f]+)", open(path).read())
+    if not m:
+        return None, "summary has no traffic line"
+    if m.group(2) != kernel_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    return int(m.group(1)), "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy"
+
+
+def calibrate_copy(mib: int):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
 
 
 def algorithmic_bytes(items, M):
@@ -147,11 +187,17 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     from decode_gemv_thinkbit_amd import configs
@@ -199,8 +245,10 @@ def main():
     }
     alg = codes_b + x_b + y_b
     ach = alg / (avg_kern_ms * 1e-3) / 1e9
+    traffic, traffic_src = measured_traffic()
     result["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                          "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                          "traffic_source": traffic_src, "kernel_sources_sha256": kernel_source_hash(),
                           "kernel": "gemv_grouped_kernel<1>", "algorithmic_bytes": alg,
                           "avg_kernel_us": round(avg_kern_ms * 1e3, 2)}
     if not args.no_parity:

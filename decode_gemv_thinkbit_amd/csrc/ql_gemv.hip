@@ -35,10 +35,12 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------- LDS tables
-constexpr int kTLut = 0;                    // 243 rows x 256 B (16 replicas x 16 B)
-constexpr int kI2Lut = 243 * 256;           // 256 rows x 32 B (4 replicas x 8 B)
-constexpr int kI3Lut = kI2Lut + 256 * 32;   // 64 entries x 4 B
-constexpr int kLutBytes = kI3Lut + 64 * 4;  // 70656
+// The 3-bit table sits at offset 0, so its addresses need no base; the other
+// two bases fit the 16-bit immediate offset of the LDS read instructions.
+constexpr int kI3Lut = 0;                   // 64 entries x 4 B
+constexpr int kTLut = 64 * 4;               // 243 rows x 256 B (16 replicas x 16 B)
+constexpr int kI2Lut = kTLut + 243 * 256;   // 256 rows x 32 B (4 replicas x 8 B)
+constexpr int kLutBytes = kI2Lut + 256 * 32;  // 70656
 
 __device__ void build_luts(uint8_t* smem) {
   for (int e = threadIdx.x; e < 243 * 16; e += blockDim.x) {
