@@ -28,7 +28,7 @@ typedef uint32_t u32x4g_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTileN = 128;    // rows per workgroup (one grid block)
 constexpr int kPad = 136;      // bf16 per LDS tile row (128 + 8: rows start on different banks)
-constexpr int kThreads = 256;  // 4 waves: 2 row halves x 2 token halves
+constexpr int kThreads = 512;  // 8 waves
 
 // Decode tables (LDS), entries in input order:
 //   ternary even / odd stored byte -> (c0,c1) (c2,c3) (c4,0) 0   [16 B]
@@ -93,21 +93,19 @@ __device__ __forceinline__ uint32_t dword_of(const u32x4g_t& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Write 32 dwords (64 bf16 codes) to an LDS tile row.
-__device__ __forceinline__ void put64(uint16_t* dst, const uint32_t (&o)[32]) {
+// Write 16 dwords (32 bf16 codes) to an LDS tile row.
+__device__ __forceinline__ void put32(uint16_t* dst, const uint32_t (&o)[16]) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
+  for (int q = 0; q < 4; ++q)
     *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
 }
 
-// Ternary: codes of period-local inputs [K0, K0+64) of one row (K0 even, compile-time).
+// Ternary: codes of period-local inputs [K0, K0+32) of one row (K0 even, compile-time)
+// from the row's chunks (K0/5)/16 and ((K0+31)/5)/16 of the period.
 template <int K0>
-__device__ __forceinline__ void decode_t64(const uint8_t* slab, int r, int64_t p, const uint8_t* lut, uint16_t* dst) {
-  constexpr int J0 = K0 / 5, J1 = (K0 + 63) / 5;  // bytes covering the range
-  constexpr int C0 = J0 / 16, C1 = J1 / 16;       // their chunks (at most two)
-  u32x4g_t ch[2];
-  ch[0] = row_chunk(slab, r, 8 * p + C0);
-  ch[1] = C1 != C0 ? row_chunk(slab, r, 8 * p + C1) : ch[0];
+__device__ __forceinline__ void decode_t32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+  constexpr int J0 = K0 / 5, J1 = (K0 + 31) / 5;  // bytes covering the range
+  constexpr int C0 = J0 / 16;
   u32x4g_t e[J1 - J0 + 1];
   gfor<J1 - J0 + 1>([&](auto ji) __attribute__((always_inline)) {
     constexpr int j = J0 + decltype(ji)::value;
@@ -115,8 +113,8 @@ __device__ __forceinline__ void decode_t64(const uint8_t* slab, int r, int64_t p
     const uint32_t b = (w >> (8 * (j & 3))) & 0xFFu;
     e[decltype(ji)::value] = *(lq4p)(lut + ((j & 1) ? kLutT1 : kLutT0) + b * 16);
   });
-  uint32_t o[32];
-  gfor<32>([&](auto pi) __attribute__((always_inline)) {
+  uint32_t o[16];
+  gfor<16>([&](auto pi) __attribute__((always_inline)) {
     constexpr int k = K0 + 2 * decltype(pi)::value;
     constexpr int j = k / 5 - J0, t = k % 5;
     if constexpr (t == 0) o[decltype(pi)::value] = e[j].x;
@@ -125,35 +123,34 @@ __device__ __forceinline__ void decode_t64(const uint8_t* slab, int r, int64_t p
     else if constexpr (t == 3) o[decltype(pi)::value] = __builtin_amdgcn_alignbit(e[j].z, e[j].y, 16);
     else o[decltype(pi)::value] = __builtin_amdgcn_perm(e[j + 1].x, e[j].z, 0x05040100u);
   });
-  put64(dst, o);
+  put32(dst, o);
 }
 
-// 2-bit: codes [128g + 64h, +64) of one row = chunk 2g+h.
-__device__ __forceinline__ void decode_i2_64(const uint8_t* slab, int r, int64_t chunk, const uint8_t* lut,
-                                             uint16_t* dst) {
-  const u32x4g_t v = row_chunk(slab, r, chunk);
-  uint32_t o[32];
-  gfor<16>([&](auto bi) __attribute__((always_inline)) {
-    constexpr int j = decltype(bi)::value;
-    const uint32_t b = (dword_of(v, j >> 2) >> (8 * (j & 3))) & 0xFFu;
+// 2-bit: codes [128g + 32q, +32) of one row = bytes 8(q&1).. of chunk 2g + q/2 (ch[0]).
+template <int Q>
+__device__ __forceinline__ void decode_i2_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+  uint32_t o[16];
+  gfor<8>([&](auto bi) __attribute__((always_inline)) {
+    constexpr int j = 8 * (Q & 1) + decltype(bi)::value;  // byte within the chunk
+    const uint32_t b = (dword_of(ch[0], j >> 2) >> (8 * (j & 3))) & 0xFFu;
     const u32x2g_t q = *(lq2p)(lut + kLutI2 + b * 8);
-    o[2 * j] = q.x;
-    o[2 * j + 1] = q.y;
+    o[2 * decltype(bi)::value] = q.x;
+    o[2 * decltype(bi)::value + 1] = q.y;
   });
-  put64(dst, o);
+  put32(dst, o);
 }
 
-// 3-bit: codes [128g + 64h, +64) of one row = two 96-bit triples (24 bytes).
-template <int H>
-__device__ __forceinline__ void decode_i3_64(const uint8_t* slab, int r, int64_t g, const uint8_t* lut, uint16_t* dst) {
-  const u32x4g_t a = row_chunk(slab, r, 3 * g + H), b = row_chunk(slab, r, 3 * g + H + 1);
-  // H = 0: bytes 0..23 of the group = a.xyzw, b.xy; H = 1: bytes 24..47 = a.zw, b.xyzw
-  const uint32_t w[6] = {H ? a.z : a.x, H ? a.w : a.y, H ? b.x : a.z, H ? b.y : a.w, H ? b.z : b.x, H ? b.w : b.y};
-  uint32_t o[32];
-  gfor<32>([&](auto pi) __attribute__((always_inline)) {
+// 3-bit: codes [128g + 32q, +32) of one row = the 96-bit triple at group bytes 12q..12q+11,
+// inside chunks 3g + (12q)/16 (ch[0]) and the next one (ch[1]).
+template <int Q>
+__device__ __forceinline__ void decode_i3_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+  constexpr int B0 = 12 * Q - 16 * ((12 * Q) / 16);  // first byte of the triple within ch[0]
+  const uint32_t cw[8] = {ch[0].x, ch[0].y, ch[0].z, ch[0].w, ch[1].x, ch[1].y, ch[1].z, ch[1].w};
+  const uint32_t w0 = cw[B0 / 4], w1 = cw[B0 / 4 + 1], w2 = cw[B0 / 4 + 2];
+  uint32_t o[16];
+  gfor<16>([&](auto pi) __attribute__((always_inline)) {
     constexpr int P = decltype(pi)::value;
-    constexpr int t = P / 16, bit = 6 * (P % 16);  // triple, first bit of the 6-bit field
-    const uint32_t w0 = w[3 * t], w1 = w[3 * t + 1], w2 = w[3 * t + 2];
+    constexpr int bit = 6 * P;  // first bit of the 6-bit field
     uint32_t f;
     if constexpr (bit + 6 <= 32) f = (w0 >> bit) & 63u;
     else if constexpr (bit < 32) f = __builtin_amdgcn_alignbit(w1, w0, bit) & 63u;
@@ -162,15 +159,41 @@ __device__ __forceinline__ void decode_i3_64(const uint8_t* slab, int r, int64_t
     else f = (w2 >> (bit - 64)) & 63u;
     o[P] = *(lq1p)(lut + kLutI3 + f * 4);
   });
-  put64(dst, o);
+  put32(dst, o);
 }
 
-// One workgroup: row block blockIdx.x (2 slabs), tokens [m0, m0 + 32*MB), groups of split blockIdx.z.
-template <int MB>
-__global__ void __launch_bounds__(kThreads, 2) gemm_kernel(MatArgs a, int M, int nsplit, float* __restrict__ part) {
-  constexpr int MT = 32 * MB;  // tokens per workgroup
+// Workgroup barrier that orders LDS only: the next group's global loads stay
+// in flight across it (a plain __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// One group's operands in registers, loaded a step ahead of their use.
+struct Stage {
+  u32x4g_t xv[4];  // 32 bf16 of one token
+  u32x4g_t ch[2];  // code chunks covering this thread's quarter of the group
+  uint32_t sc;     // bf16 scale of row tid (threads < 128)
+};
+
+// One workgroup: row block blockIdx.x (2 slabs), tokens [m0, m0 + MT), groups of split blockIdx.z.
+// 8 waves: WR row slices of 128/WR rows x 8/WR token slices of 32 tokens... (MT = 256/WR).
+// Per group: codes staged in registers are decoded into LDS with the x tile and
+// scales; after one barrier the next group's global loads are issued and the
+// MFMAs and the scale epilogue of this group run from LDS, so the loads' latency
+// hides behind the matrix work.
+#ifndef QL_GEMM_WAVES_PER_EU
+#define QL_GEMM_WAVES_PER_EU 2
+#endif
+template <int WR>
+__global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(MatArgs a, int M, int nsplit, float* __restrict__ part) {
+  constexpr int WM = 8 / WR;         // token slices
+  constexpr int RB = 8 / WR;         // 16-row blocks per wave (128 / WR rows)
+  constexpr int MB = 2;              // 16-token blocks per wave
+  constexpr int MT = 16 * MB * WM;   // tokens per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t wt[kTileN * kPad];
   __shared__ __attribute__((aligned(16))) uint16_t xt[MT * kPad];
+  __shared__ __attribute__((aligned(16))) float sct[kTileN];
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
   gemm_build_luts(lut);
 
@@ -186,105 +209,149 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(MatArgs a, int M, int
   const uint8_t* slab0 = a.packed + off0;
   const uint8_t* slab1 = (2 * blk + 1 < nslabs) ? slab0 + (int64_t)kSlab * row_bytes(gr, K) : nullptr;
 
-  // decode mapping: waves 0,1 take inputs [0,64) of the group, waves 2,3 inputs [64,128)
-  const int dr = tid & 127, dh = tid >> 7;
+  // decode mapping: row dr, quarter dq (wave-uniform) of the group's 128 inputs
+  const int dr = tid & 127, dq = __builtin_amdgcn_readfirstlane(tid >> 7);
   const uint8_t* dslab = dr < kSlab ? slab0 : slab1;
   const int dslab_r = dr & (kSlab - 1);
-  uint16_t* drow = wt + dr * kPad + 64 * dh;
+  uint16_t* drow = wt + dr * kPad + 32 * dq;
+  // x mapping: token xt_t, quarter xt_q
+  const int xt_t = tid >> 2, xt_q = tid & 3;
+  const bool x_ok = xt_t < MT && m0 + xt_t < M;
+  const uint16_t* xrow = a.x + (int64_t)(x_ok ? m0 + xt_t : 0) * K + 32 * xt_q;
+  const int64_t sc_n = blk * kTileN + tid;
 
-  // MFMA mapping: wave (wr, wm) computes rows 64wr..64wr+63 x tokens (MT/2)wm..
-  const int wr = wave & 1, wm = wave >> 1;
-  f32x4_t acc[4][MB];
+  Stage st;
+  auto load = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+    for (int q = 0; q < 4; ++q) {
+      st.xv[q] = u32x4g_t{0u, 0u, 0u, 0u};
+      if (x_ok) st.xv[q] = *(gq4p)(xrow + (int64_t)g * kGroup + 8 * q);
+    }
+    if (gr == QL_GRID_T) {
+      const int64_t p = g / 5;
+      const int k0 = 128 * (g - 5 * (int)p) + 32 * dq;
+      const int c0 = (k0 / 5) / 16, c1 = ((k0 + 31) / 5) / 16;
+      st.ch[0] = row_chunk(dslab, dslab_r, 8 * p + c0);
+      st.ch[1] = row_chunk(dslab, dslab_r, 8 * p + c1);
+    } else if (gr == QL_GRID_I2) {
+      // every branch writes both slots: stores to one slot or the other would be
+      // merged into one store with a computed address, which keeps st in memory
+      st.ch[0] = row_chunk(dslab, dslab_r, 2 * (int64_t)g + (dq >> 1));
+      st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
+    } else {
+      const int c0 = (12 * dq) / 16;
+      st.ch[0] = row_chunk(dslab, dslab_r, 3 * (int64_t)g + c0);
+      st.ch[1] = row_chunk(dslab, dslab_r, 3 * (int64_t)g + (c0 < 2 ? c0 + 1 : c0));
+    }
+    st.sc = 0;
+    if (tid < kTileN && sc_n < a.N) st.sc = a.pscales[pscale_index(sc_n, g, G8)];
+  };
+  // x tile and scales of the staged group into LDS
+  auto put_x = [&]() __attribute__((always_inline)) {
+    if (xt_t < MT) {
+      uint16_t* dst = xt + xt_t * kPad + 32 * xt_q;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4g_t*>(dst + 8 * q) = st.xv[q];
+    }
+    if (tid < kTileN) sct[tid] = bf16_bits_to_f32(st.sc);
+  };
+
+  // MFMA mapping: wave (wr, wm) computes rows (128/WR)wr.. x tokens 32wm..
+  const int wr = wave % WR, wm = wave / WR;
+  f32x4_t acc[RB][MB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4_t{0, 0, 0, 0};
 
-  auto step = [&](int g) __attribute__((always_inline)) {
-    // x tile: token t, half h -> 64 bf16 (8 x 16 B)
-    for (int task = tid; task < 2 * MT; task += kThreads) {
-      const int t = task >> 1, h = task & 1;
-      uint16_t* dst = xt + t * kPad + 64 * h;
-      const bool ok = m0 + t < M;
-      const uint16_t* src = a.x + (int64_t)(ok ? m0 + t : 0) * K + (int64_t)g * kGroup + 64 * h;
+  // after the staged group is in LDS: prefetch the next one, then multiply this one
+  auto mma = [&](int g) __attribute__((always_inline)) {
+    lds_barrier();
+    if (g + 1 < g_hi) load(g + 1);
+    f32x4_t pr[RB][MB];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        u32x4g_t v = {0u, 0u, 0u, 0u};
-        if (ok) v = *(gq4p)(src + 8 * q);
-        *reinterpret_cast<u32x4g_t*>(dst + 8 * q) = v;
-      }
-    }
-    __syncthreads();
-    f32x4_t pr[4][MB];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) pr[rb][mb] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kk = 32 * ks + 8 * (lane >> 4);
-      bf16x8_t av[4], bv[MB];
+      bf16x8_t av[RB], bv[MB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        av[rb] = *reinterpret_cast<const bf16x8_t*>(wt + (64 * wr + 16 * rb + (lane & 15)) * kPad + kk);
+      for (int rb = 0; rb < RB; ++rb)
+        av[rb] = *reinterpret_cast<const bf16x8_t*>(wt + ((128 / WR) * wr + 16 * rb + (lane & 15)) * kPad + kk);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        bv[mb] = *reinterpret_cast<const bf16x8_t*>(xt + ((MT / 2) * wm + 16 * mb + (lane & 15)) * kPad + kk);
+        bv[mb] = *reinterpret_cast<const bf16x8_t*>(xt + (32 * wm + 16 * mb + (lane & 15)) * kPad + kk);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           pr[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rb], bv[mb], pr[rb][mb], 0, 0, 0);
     }
     // D lane l: rows 4*(l/16)+i of the 16-row block, token l%16 of the 16-token block
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(sct + (128 / WR) * wr + 16 * rb + 4 * (lane >> 4));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t n = blk * kTileN + 64 * wr + 16 * rb + 4 * (lane >> 4) + i;
-        const float s = n < a.N ? bf16_bits_to_f32(a.pscales[pscale_index(n, g, G8)]) : 0.0f;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[rb][mb][i] = fmaf(s, pr[rb][mb][i], acc[rb][mb][i]);
-      }
+        for (int mb = 0; mb < MB; ++mb) acc[rb][mb][i] = fmaf(s4[i], pr[rb][mb][i], acc[rb][mb][i]);
     }
-    __syncthreads();
+    lds_barrier();
+  };
+
+  // decode of the staged group (dq is wave-uniform: one branch per wave)
+  auto decode_t = [&](auto ii) __attribute__((always_inline)) {
+    constexpr int i = decltype(ii)::value;
+    if (dq == 0) decode_t32<128 * i>(st.ch, lut, drow);
+    else if (dq == 1) decode_t32<128 * i + 32>(st.ch, lut, drow);
+    else if (dq == 2) decode_t32<128 * i + 64>(st.ch, lut, drow);
+    else decode_t32<128 * i + 96>(st.ch, lut, drow);
   };
 
   __syncthreads();  // tables ready
+  if (g_lo < g_hi) load(g_lo);
   if (gr == QL_GRID_T) {
     // periods of 640 inputs: the byte positions of every group are compile-time
     for (int64_t p = g_lo / 5; 5 * p < g_hi; ++p) {
       gfor<5>([&](auto ii) __attribute__((always_inline)) {
-        constexpr int i = decltype(ii)::value;
-        const int g = (int)(5 * p) + i;
+        const int g = (int)(5 * p) + decltype(ii)::value;
         if (g >= g_lo && g < g_hi) {
-          if (dh == 0) decode_t64<128 * i>(dslab, dslab_r, p, lut, drow);
-          else decode_t64<128 * i + 64>(dslab, dslab_r, p, lut, drow);
-          step(g);
+          decode_t(ii);
+          put_x();
+          mma(g);
         }
       });
     }
   } else if (gr == QL_GRID_I2) {
     for (int g = g_lo; g < g_hi; ++g) {
-      decode_i2_64(dslab, dslab_r, 2 * g + dh, lut, drow);
-      step(g);
+      if (dq == 0) decode_i2_32<0>(st.ch, lut, drow);
+      else if (dq == 1) decode_i2_32<1>(st.ch, lut, drow);
+      else if (dq == 2) decode_i2_32<2>(st.ch, lut, drow);
+      else decode_i2_32<3>(st.ch, lut, drow);
+      put_x();
+      mma(g);
     }
   } else {
     for (int g = g_lo; g < g_hi; ++g) {
-      if (dh == 0) decode_i3_64<0>(dslab, dslab_r, g, lut, drow);
-      else decode_i3_64<1>(dslab, dslab_r, g, lut, drow);
-      step(g);
+      if (dq == 0) decode_i3_32<0>(st.ch, lut, drow);
+      else if (dq == 1) decode_i3_32<1>(st.ch, lut, drow);
+      else if (dq == 2) decode_i3_32<2>(st.ch, lut, drow);
+      else decode_i3_32<3>(st.ch, lut, drow);
+      put_x();
+      mma(g);
     }
   }
 
   // store: y directly, or this split's partial sums
   float* out = nsplit > 1 ? part + (int64_t)z * M * a.N : a.y;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int64_t n = blk * kTileN + 64 * wr + 16 * rb + 4 * (lane >> 4);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t n = blk * kTileN + (128 / WR) * wr + 16 * rb + 4 * (lane >> 4);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int t = m0 + (MT / 2) * wm + 16 * mb + (lane & 15);
+      const int t = m0 + 32 * wm + 16 * mb + (lane & 15);
       if (t >= M) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -304,12 +371,14 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(const float* __restric
 }
 
 namespace {
-int token_blocks(int64_t M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
+// row slices per workgroup: 8 (32 tokens), 4 (64 tokens) or 2 (128 tokens)
+int row_slices(int64_t M) { return M <= 32 ? 8 : (M <= 64 ? 4 : 2); }
+int64_t tile_tokens(int64_t M) { return 256 / row_slices(M); }
 
 // K splits that bring the launch to about two workgroups per CU (at least two
 // groups per split); 1 when the matrix alone fills the device.
 int choose_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t mt = 32 * token_blocks(M);
+  const int64_t mt = tile_tokens(M);
   const int64_t tiles = ((N + kTileN - 1) / kTileN) * ((M + mt - 1) / mt);
   const int64_t want = 2 * (int64_t)device_cu_count();
   int64_t s = (want + tiles - 1) / tiles;
@@ -328,15 +397,16 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream) {
   int s = choose_splits(M, a.N, a.K);
   if (s > 1 && (!workspace || ws_bytes < (size_t)s * M * a.N * sizeof(float))) s = 1;
-  const int mbk = token_blocks(M);
-  const dim3 grid((unsigned)((a.N + kTileN - 1) / kTileN), (unsigned)((M + 32 * mbk - 1) / (32 * mbk)), (unsigned)s);
+  const int wr = row_slices(M);
+  const int64_t mt = tile_tokens(M);
+  const dim3 grid((unsigned)((a.N + kTileN - 1) / kTileN), (unsigned)((M + mt - 1) / mt), (unsigned)s);
   float* part = static_cast<float*>(workspace);
-  if (mbk == 1)
-    hipLaunchKernelGGL(gemm_kernel<1>, grid, dim3(kThreads), 0, stream, a, M, s, part);
-  else if (mbk == 2)
-    hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(kThreads), 0, stream, a, M, s, part);
-  else
+  if (wr == 8)
+    hipLaunchKernelGGL(gemm_kernel<8>, grid, dim3(kThreads), 0, stream, a, M, s, part);
+  else if (wr == 4)
     hipLaunchKernelGGL(gemm_kernel<4>, grid, dim3(kThreads), 0, stream, a, M, s, part);
+  else
+    hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(kThreads), 0, stream, a, M, s, part);
   if (s > 1) {
     const int64_t n = (int64_t)M * a.N;
     const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
