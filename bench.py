@@ -9,7 +9,9 @@ codes, scales, activations) are resident in HBM before the timed region.
 Prints one JSON line: packed-weight GB/s of the pass (stored code + scale
 bytes / time per pass), microseconds per pass, the roofline of the GEMV
 kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload.  A "gemm" object adds the batched path on one
+Qwen3-8B-shaped layer (mixed grids, M = 64 / 256 / 512): microseconds per layer
+and MFMA utilisation against the dense bf16 peak.
 """
 from __future__ import annotations
 
@@ -179,6 +181,57 @@ def cpu_baseline(wl, wl_index, M, budget_s=20.0):
             "us_per_pass_extrapolated": round(sec * wl.layers * 1e6, 1)}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def gemm_leg(dev, Ms=(64, 256, 512), reps=10):
+    """The batched path on one Qwen3-8B-shaped layer (mixed grids): microseconds per
+    layer and MFMA utilisation (useful 2*M*N*K flops / time / dense bf16 peak)."""
+    import torch
+    from decode_gemv_thinkbit_amd import configs
+    from decode_gemv_thinkbit_amd import qlinear as ql
+    from decode_gemv_thinkbit_amd import synth
+
+    wl = configs.WORKLOADS["qwen3_8b_gemm"]
+    wi = list(configs.WORKLOADS).index(wl.name)
+    alloc = synth.allocation(wl, 0)
+    mats = []
+    for mi, lin in enumerate(wl.linears):
+        W = synth.weight(lin.N, lin.K, synth.weight_seed(wi, 0, mi), device=dev)
+        mats.append((lin, ql.quantize_pack(W, alloc[lin.name])))
+        del W
+    out = []
+    for M in Ms:
+        xs = {K: synth.activations(M, K, synth.seed_of(3, wi, K, M), device=dev) for K in (4096, 12288)}
+        ys = [torch.empty((M, lin.N), dtype=torch.float32, device=dev) for lin, _ in mats]
+        ws_bytes = max(int(ql.lib().qlinear_gemm_workspace_bytes(M, lin.N, lin.K)) for lin, _ in mats)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def layer():
+            for (lin, pw), y in zip(mats, ys):
+                ql.gemm(xs[lin.K], pw, out=y, workspace=ws)
+
+        for _ in range(3):
+            layer()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(st)
+        for _ in range(reps):
+            layer()
+        e.record(st)
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) * 1e3 / reps
+        flops = 2 * M * sum(lin.N * lin.K for lin, _ in mats)
+        tf = flops / (us * 1e-6) / 1e12
+        out.append({"M": M, "us_per_layer": round(us, 2), "tflops": round(tf, 1),
+                    "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "stored_bytes": sum(pw.nbytes for _, pw in mats)})
+        log(f"gemm M={M}: {us:.1f} us per 8B layer, {tf:.1f} TFLOP/s ({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA)")
+    return {"workload": "qwen3_8b_layer mixed grids", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "kernels": "gemm_kernel (+ gemm_reduce_kernel when K is split)", "points": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +240,7 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the batched (MFMA) leg")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -256,6 +310,10 @@ def main():
         result["parity"] = {"max_err_over_row_norm": err, "normwise_sampled": nw, "matrices": nmat,
                             "tolerance": 2e-3, "ok": err <= 2e-3}
         log(f"parity on sampled rows of {nmat} matrices: {err:.3g} (normwise {nw:.3g})")
+    if not args.no_gemm:
+        del grp, items
+        torch.cuda.empty_cache()
+        result["gemm"] = gemm_leg(dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample...")
         result["cpu_baseline"] = cpu_baseline(wl, wl_index, M)
