@@ -11,7 +11,9 @@ bytes / time per pass), microseconds per pass, the roofline of the GEMV
 kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed on a bounded
 sample of the same workload.  A "gemm" object adds the batched path on one
 Qwen3-8B-shaped layer (mixed grids, M = 64 / 256 / 512): microseconds per layer
-and MFMA utilisation against the dense bf16 peak.
+and MFMA utilisation against the dense bf16 peak; "container_ab" times the
+Qwen3-8B pass and the Qwen3-14B stack (M = 1) once more with the same codes stored
+in 4-bit containers, the format published checkpoints use.
 """
 from __future__ import annotations
 
@@ -66,6 +68,79 @@ def build_pass(wl, wl_index, M, dev):
             log(f"  packed layers 0..{layer}")
     torch.cuda.synchronize()
     return items, meta, stored, xs
+
+
+def build_container_pass(wl, wl_index, xs, dev):
+    """The same pass (same seeds, grids and activations) stored as 4-bit containers."""
+    import torch
+    from decode_gemv_thinkbit_amd import qlinear as ql
+    from decode_gemv_thinkbit_amd import synth
+
+    items, stored = [], 0
+    for layer in range(wl.layers):
+        alloc = synth.allocation(wl, layer)
+        for mi, lin in enumerate(wl.linears):
+            W = synth.weight(lin.N, lin.K, synth.weight_seed(wl_index, layer, mi), device=dev)
+            codes, scales = ql.quantize(W, alloc[lin.name])
+            del W
+            cw = ql.c4_pack(codes, scales)
+            del codes, scales
+            y = torch.empty((1, lin.N), dtype=torch.float32, device=dev)
+            items.append((cw, xs[(layer, lin.x_slot)], y))
+            stored += cw.nbytes
+    torch.cuda.synchronize()
+    return items, stored
+
+
+def time_grouped(grp, warmup, steps):
+    """(wall ms per launch, mean kernel ms from HIP events on the launch stream)."""
+    import torch
+
+    for _ in range(warmup):
+        grp.run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record(st)
+        grp.run()
+        e.record(st)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, sum(s.elapsed_time(e) for s, e in evs) / steps
+
+
+def container_ab(wl_name, dev, warmup, steps, native=None):
+    """Native packing against 4-bit containers on one pass at batch 1: both grouped launches,
+    same codes, scales and activations.  native = (ms per pass, stored bytes) if measured."""
+    import torch
+    from decode_gemv_thinkbit_amd import configs
+    from decode_gemv_thinkbit_amd import qlinear as ql
+
+    wl = configs.WORKLOADS[wl_name]
+    wi = list(configs.WORKLOADS).index(wl_name)
+    items, meta, stored, xs = build_pass(wl, wi, 1, dev)
+    if native is None:
+        native = (time_grouped(ql.GroupedGemv(items), warmup, steps)[0], stored)
+    c_items, c_stored = build_container_pass(wl, wi, xs, dev)
+    del items
+    torch.cuda.empty_cache()
+    c_ms, _ = time_grouped(ql.GroupedGemv(c_items), warmup, steps)
+    err, nw, nmat = parity_sample(c_items, meta, 1, dev, rows_per=16)
+    n_ms, n_stored = native
+    out = {"workload": wl_name, "M": 1,
+           "native": {"us_per_pass": round(n_ms * 1e3, 2), "stored_bytes": n_stored,
+                      "gbs": round(n_stored / (n_ms * 1e-3) / 1e9, 1)},
+           "container_4bit": {"us_per_pass": round(c_ms * 1e3, 2), "stored_bytes": c_stored,
+                              "gbs": round(c_stored / (c_ms * 1e-3) / 1e9, 1),
+                              "parity_max_err_over_row_norm": err, "parity_ok": err <= 2e-3},
+           "bytes_ratio": round(c_stored / n_stored, 3), "speedup_native": round(c_ms / n_ms, 3)}
+    log(f"A/B {wl_name}: native {n_ms * 1e3:.1f} us ({n_stored / 1e9:.3f} GB), containers {c_ms * 1e3:.1f} us "
+        f"({c_stored / 1e9:.3f} GB): native {c_ms / n_ms:.2f}x faster")
+    del c_items
+    torch.cuda.empty_cache()
+    return out
 
 
 def kernel_source_hash() -> str:
@@ -241,6 +316,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the batched (MFMA) leg")
+    ap.add_argument("--no-ab", action="store_true", help="skip the 4-bit container A/B leg")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -310,9 +386,13 @@ def main():
         result["parity"] = {"max_err_over_row_norm": err, "normwise_sampled": nw, "matrices": nmat,
                             "tolerance": 2e-3, "ok": err <= 2e-3}
         log(f"parity on sampled rows of {nmat} matrices: {err:.3g} (normwise {nw:.3g})")
+    del grp, items
+    torch.cuda.empty_cache()
+    if not args.no_ab:
+        result["container_ab"] = [container_ab(args.workload, dev, args.warmup, args.steps,
+                                               native=(ms_step, stored)),
+                                  container_ab("qwen3_14b_stack", dev, args.warmup, args.steps)]
     if not args.no_gemm:
-        del grp, items
-        torch.cuda.empty_cache()
         result["gemm"] = gemm_leg(dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample...")

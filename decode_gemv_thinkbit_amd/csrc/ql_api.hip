@@ -171,10 +171,13 @@ ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t* 
 
 int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
   if (!descs || count <= 0) return fail(QL_EINVAL, "empty descriptor list"), -1;
+  const bool containers = descs[0].grid == QL_GRID_C4;
   for (int32_t i = 0; i < count; ++i) {
     const ql_gemv_desc& d = descs[i];
     if (check_shape(d.N, d.K) != QL_OK) return -1;
-    if (check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
+    if ((d.grid == QL_GRID_C4) != containers)
+      return fail(QL_EINVAL, "descriptor %d: a list must not mix 4-bit containers and native grids", i), -1;
+    if (!containers && check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
     if (check_ptrs({d.packed, d.pscales, d.x, d.y}) != QL_OK) return -1;
   }
   // longest rows first: the tail of the launch is then made of short tasks
@@ -200,6 +203,54 @@ ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t
 }
 
 size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return ql::gemm_workspace_bytes(M, N, K); }
+
+// ---------------------------------------------------------------- 4-bit container baseline
+int64_t qlinear_c4_bytes(int64_t N, int64_t K) {
+  if (check_shape(N, K) != QL_OK) return 0;
+  return ((N + QL_SLAB - 1) / QL_SLAB) * QL_SLAB * (K / 2);
+}
+
+ql_status qlinear_c4_pack(int64_t N, int64_t K, const int8_t* codes, void* c4, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_ptrs({codes, c4}));
+  return hip_status(ql::launch_c4_pack(N, K, codes, static_cast<uint8_t*>(c4), stream), "c4_pack launch");
+}
+
+ql_status qlinear_c4_unpack(int64_t N, int64_t K, const void* c4, int8_t* codes, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_ptrs({c4, codes}));
+  return hip_status(ql::launch_c4_unpack(N, K, static_cast<const uint8_t*>(c4), codes, stream), "c4_unpack launch");
+}
+
+ql_status qlinear_c4_to_packed(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                               const void* c4, void* packed, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, blk_off, true));
+  QL_TRY(check_ptrs({c4, packed}));
+  return hip_status(ql::launch_c4_to_packed(N, K, grid, blk_grid, blk_off, static_cast<const uint8_t*>(c4),
+                                            static_cast<uint8_t*>(packed), stream),
+                    "c4_to_packed launch");
+}
+
+ql_status qlinear_c4_gemv(int64_t M, int64_t N, int64_t K, const void* c4, const uint16_t* pscales, const uint16_t* x,
+                          float* y, hipStream_t stream) {
+  if (M != 1) return fail(QL_EUNSUPPORTED, "the container GEMV runs batch 1 only (M=%lld)", (long long)M);
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_ptrs({c4, pscales, x, y}));
+  if (N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "N and K must be below 2^31");
+  const ql::MatArgs a{static_cast<const uint8_t*>(c4), pscales, nullptr, nullptr, x, y, (int32_t)N, (int32_t)K,
+                      QL_GRID_C4};
+  return hip_status(ql::launch_c4_gemv(a, stream), "c4_gemv launch");
+}
+
+ql_status qlinear_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int32_t M,
+                                  uint32_t* sched, hipStream_t stream) {
+  if (M != 1) return fail(QL_EUNSUPPORTED, "the container GEMV runs batch 1 only (M=%d)", M);
+  if (count <= 0 || total_slabs <= 0 || total_slabs >= ((int64_t)1 << 31))
+    return fail(QL_EINVAL, "bad count (%d) or slab total (%lld)", count, (long long)total_slabs);
+  QL_TRY(check_ptrs({descs, sched}));
+  return hip_status(ql::launch_c4_gemv_grouped(descs, count, total_slabs, sched, stream), "c4 grouped gemv launch");
+}
 
 ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
                        const void* packed, const uint16_t* pscales, const uint16_t* x, float* y, void* workspace,

@@ -38,6 +38,19 @@ __host__ __device__ inline int64_t row_bytes(int grid, int64_t K) {
   return 3 * K / 8;
 }
 
+// 4-bit container baseline: code c (-8..7) of row n, input k as a two's
+// complement nibble.  Row bytes K/2; byte i of a row holds inputs 2i (low
+// nibble) and 2i+1 (high nibble); rows are interleaved in 64-row slabs exactly
+// like the packed layout (bytes 16c..16c+15 of slab row r at c*1024 + r*16).
+__host__ __device__ inline int64_t c4_byte_offset(int64_t K, int64_t n, int64_t k) {
+  const int64_t i = k >> 1;
+  return (n / kSlab) * (int64_t)kSlab * (K / 2) + (i >> 4) * kSlabChunkBytes + (n % kSlab) * kChunkBytes + (i & 15);
+}
+__host__ __device__ inline int c4_code_at(const uint8_t* c4, int64_t K, int64_t n, int64_t k) {
+  const uint32_t nib = (c4[c4_byte_offset(K, n, k)] >> (4 * (k & 1))) & 0xFu;
+  return (int)nib - (int)((nib & 8u) << 1);
+}
+
 // Byte offset of slab `s` in a packed matrix (uniform grid, or per-block tables).
 __device__ inline int64_t slab_offset(int64_t s, int64_t K, int grid, const int8_t* blk_grid,
                                       const int64_t* blk_off, int* grid_out) {

@@ -9,6 +9,10 @@ hipError_t launch_quantize(int64_t N, int64_t K, int grid, const int8_t* blk_gri
                            uint16_t* scales, hipStream_t stream);
 hipError_t launch_pack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
                        const int8_t* codes, uint8_t* packed, hipStream_t stream);
+hipError_t launch_c4_to_packed(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                               const uint8_t* c4, uint8_t* packed, hipStream_t stream);
+hipError_t launch_c4_pack(int64_t N, int64_t K, const int8_t* codes, uint8_t* c4, hipStream_t stream);
+hipError_t launch_c4_unpack(int64_t N, int64_t K, const uint8_t* c4, int8_t* codes, hipStream_t stream);
 // mode 0: int8 codes, 1: fp32 c*s, 2: bf16 bits of c*s
 hipError_t launch_unpack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
                          const uint8_t* packed, const uint16_t* pscales, int mode, void* out, hipStream_t stream);
@@ -29,6 +33,9 @@ struct MatArgs {
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M, uint32_t* sched,
                                hipStream_t stream);
+hipError_t launch_c4_gemv(const MatArgs& a, hipStream_t stream);
+hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, uint32_t* sched,
+                                  hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream);
 

@@ -51,17 +51,28 @@ hipError_t launch_quantize(int64_t N, int64_t K, int grid, const int8_t* blk_gri
 }
 
 // ---------------------------------------------------------------- pack
+// Where the packer reads codes: an int8 array [N][K], or a 4-bit container
+// (the converter from container checkpoints).
+struct I8Codes {
+  const int8_t* __restrict__ p;
+  __device__ int at(int64_t K, int64_t n, int64_t k) const { return p[n * K + k]; }
+};
+struct C4Codes {
+  const uint8_t* __restrict__ p;
+  __device__ int at(int64_t K, int64_t n, int64_t k) const { return c4_code_at(p, K, n, k); }
+};
+
 // Digit u = c - c_min of row n at input k; rows past N and trits past K are
 // padding with c = 0.
-__device__ inline uint32_t digit(const int8_t* __restrict__ codes, int64_t N, int64_t K, int64_t n, int64_t k,
-                                 int cmin) {
-  const int c = (n < N && k < K) ? codes[n * K + k] : 0;
+template <class Src>
+__device__ inline uint32_t digit(const Src& codes, int64_t N, int64_t K, int64_t n, int64_t k, int cmin) {
+  const int c = (n < N && k < K) ? codes.at(K, n, k) : 0;
   return (uint32_t)(c - cmin);
 }
 
 // Byte jj of row n in its grid's row order.
-__device__ inline uint32_t row_byte_value(const int8_t* __restrict__ codes, int64_t N, int64_t K, int64_t n,
-                                          int64_t jj, int gr) {
+template <class Src>
+__device__ inline uint32_t row_byte_value(const Src& codes, int64_t N, int64_t K, int64_t n, int64_t jj, int gr) {
   const int cmin = grid_cmin(gr);
   if (gr == QL_GRID_T) {
     // five trits in input order (least significant = lowest k), then the
@@ -90,10 +101,10 @@ __device__ inline uint32_t row_byte_value(const int8_t* __restrict__ codes, int6
 }
 
 // One thread per (padded row, 16-byte chunk).
+template <class Src>
 __global__ void __launch_bounds__(256) pack_kernel(int64_t N, int64_t K, int grid, const int8_t* __restrict__ blk_grid,
-                                                   const int64_t* __restrict__ blk_off,
-                                                   const int8_t* __restrict__ codes, uint8_t* __restrict__ packed,
-                                                   int64_t max_chunks) {
+                                                   const int64_t* __restrict__ blk_off, Src codes,
+                                                   uint8_t* __restrict__ packed, int64_t max_chunks) {
   const int64_t S = (N + kSlab - 1) / kSlab;
   const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= S * kSlab * max_chunks) return;
@@ -113,13 +124,66 @@ __global__ void __launch_bounds__(256) pack_kernel(int64_t N, int64_t K, int gri
   *reinterpret_cast<uint4*>(packed + off + c * kSlabChunkBytes + r * kChunkBytes) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-hipError_t launch_pack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
-                       const int8_t* codes, uint8_t* packed, hipStream_t stream) {
+template <class Src>
+static hipError_t launch_pack_from(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                                   Src codes, uint8_t* packed, hipStream_t stream) {
   const int64_t S = (N + kSlab - 1) / kSlab;
   const int64_t max_chunks = row_bytes(QL_GRID_I3, K) / kChunkBytes;  // the widest grid
   const int64_t items = S * kSlab * max_chunks;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, N, K, grid, blk_grid,
-                     blk_off, codes, packed, max_chunks);
+  hipLaunchKernelGGL(pack_kernel<Src>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, N, K, grid,
+                     blk_grid, blk_off, codes, packed, max_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                       const int8_t* codes, uint8_t* packed, hipStream_t stream) {
+  return launch_pack_from(N, K, grid, blk_grid, blk_off, I8Codes{codes}, packed, stream);
+}
+
+hipError_t launch_c4_to_packed(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                               const uint8_t* c4, uint8_t* packed, hipStream_t stream) {
+  return launch_pack_from(N, K, grid, blk_grid, blk_off, C4Codes{c4}, packed, stream);
+}
+
+// ---------------------------------------------------------------- 4-bit containers
+// One thread per (padded row, 16-byte chunk = 32 codes): nibble i of word q
+// holds input 32c + 8q + i.
+__global__ void __launch_bounds__(256) c4_pack_kernel(int64_t N, int64_t K, const int8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ c4) {
+  const int64_t nch = K / 32;
+  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= ((N + kSlab - 1) / kSlab) * kSlab * nch) return;
+  const int64_t np = item / nch, c = item % nch;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int code = np < N ? codes[np * K + 32 * c + 8 * q + i] : 0;
+      v |= ((uint32_t)code & 0xFu) << (4 * i);
+    }
+    w[q] = v;
+  }
+  *reinterpret_cast<uint4*>(c4 + c4_byte_offset(K, np, 32 * c)) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ void __launch_bounds__(256) c4_unpack_kernel(int64_t N, int64_t K, const uint8_t* __restrict__ c4,
+                                                        int8_t* __restrict__ codes) {
+  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= N * K) return;
+  codes[item] = (int8_t)c4_code_at(c4, K, item / K, item % K);
+}
+
+hipError_t launch_c4_pack(int64_t N, int64_t K, const int8_t* codes, uint8_t* c4, hipStream_t stream) {
+  const int64_t items = ((N + kSlab - 1) / kSlab) * kSlab * (K / 32);
+  hipLaunchKernelGGL(c4_pack_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, N, K, codes, c4);
+  return hipGetLastError();
+}
+
+hipError_t launch_c4_unpack(int64_t N, int64_t K, const uint8_t* c4, int8_t* codes, hipStream_t stream) {
+  const int64_t items = N * K;
+  hipLaunchKernelGGL(c4_unpack_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, N, K, c4, codes);
   return hipGetLastError();
 }
 

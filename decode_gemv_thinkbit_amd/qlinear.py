@@ -16,6 +16,7 @@ import numpy as np
 import torch
 
 GRID_T, GRID_I2, GRID_I3, GRID_MIXED = 0, 1, 2, 3
+GRID_C4 = 4  # 4-bit container baseline (not a ThinkBit grid)
 GROUP, SLAB, BLOCK = 128, 64, 128
 QL_SCHED_WORDS = 4  # uint32 words of grouped-launch scheduler state
 
@@ -66,9 +67,17 @@ def lib():
         L.qlinear_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.qlinear_gemm_workspace_bytes.restype = sz
         L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qlinear_c4_bytes.argtypes = [i64, i64]
+        L.qlinear_c4_bytes.restype = i64
+        L.qlinear_c4_pack.argtypes = [i64, i64, vp, vp, vp]
+        L.qlinear_c4_unpack.argtypes = [i64, i64, vp, vp, vp]
+        L.qlinear_c4_to_packed.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
+        L.qlinear_c4_gemv.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
+        L.qlinear_c4_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp, vp]
         for name in ("qlinear_block_offsets", "qlinear_quantize", "qlinear_pack", "qlinear_pack_scales",
                      "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
-                     "qlinear_gemv_grouped", "qlinear_gemm"):
+                     "qlinear_gemv_grouped", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
+                     "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -203,6 +212,60 @@ def dequant(pw: PackedWeight, out_bf16: bool = False) -> torch.Tensor:
     return out
 
 
+# ---------------------------------------------------------------- 4-bit containers (baseline)
+@dataclass
+class C4Weight:
+    """A weight stored as 4-bit containers (codes as two's complement nibbles), with the
+    same packed scale array as the native layout."""
+    c4: torch.Tensor          # uint8 container bytes
+    pscales: torch.Tensor     # bfloat16, packed scale array
+    N: int
+    K: int
+
+    @property
+    def nbytes(self) -> int:
+        return self.c4.numel() + 2 * self.pscales.numel()
+
+
+def c4_pack(codes: torch.Tensor, scales: torch.Tensor) -> C4Weight:
+    _dev(codes, torch.int8, "codes")
+    _dev(scales, torch.bfloat16, "scales")
+    N, K = codes.shape
+    if tuple(scales.shape) != (N, K // GROUP):
+        raise ValueError("scales must be [N, K/128]")
+    size = int(lib().qlinear_c4_bytes(N, K))
+    if size <= 0:
+        raise ValueError(f"invalid shape {N}x{K}")
+    c4 = torch.empty(size, dtype=torch.uint8, device=codes.device)
+    _check(lib().qlinear_c4_pack(N, K, _ptr(codes), _ptr(c4), _stream()), "c4_pack")
+    ps = torch.empty(packed_scales_len(N, K), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().qlinear_pack_scales(N, K, _ptr(scales), _ptr(ps), _stream()), "pack_scales")
+    return C4Weight(c4, ps, N, K)
+
+
+def c4_unpack(cw: C4Weight) -> torch.Tensor:
+    codes = torch.empty((cw.N, cw.K), dtype=torch.int8, device=cw.c4.device)
+    _check(lib().qlinear_c4_unpack(cw.N, cw.K, _ptr(cw.c4), _ptr(codes), _stream()), "c4_unpack")
+    return codes
+
+
+def c4_to_packed(cw: C4Weight, grid) -> PackedWeight:
+    """Convert a container checkpoint to the native packed layout (codes must fit the grid)."""
+    g, bg, bo, size = _grid_tables(cw.N, cw.K, grid, cw.c4.device)
+    packed = torch.empty(size, dtype=torch.uint8, device=cw.c4.device)
+    _check(lib().qlinear_c4_to_packed(cw.N, cw.K, g, _ptr(bg), _ptr(bo), _ptr(cw.c4), _ptr(packed), _stream()),
+           "c4_to_packed")
+    return PackedWeight(packed, cw.pscales, cw.N, cw.K, g, bg, bo)
+
+
+def c4_gemv(x: torch.Tensor, cw: C4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [1, N] fp32 = x [1, K] bf16 times the container weight transposed (batch 1)."""
+    x, M, out = _xy(x, cw, out)
+    _check(lib().qlinear_c4_gemv(M, cw.N, cw.K, _ptr(cw.c4), _ptr(cw.pscales), _ptr(x), _ptr(out), _stream()),
+           "c4_gemv")
+    return out
+
+
 # ---------------------------------------------------------------- products
 def _xy(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor]):
     _dev(x, torch.bfloat16, "x")
@@ -244,22 +307,29 @@ class GroupedGemv:
     """One persistent launch over many independent (x, W, y) products with the same M."""
 
     def __init__(self, items):
-        """items: list of (PackedWeight, x [M,K] bf16, y [M,N] fp32)."""
+        """items: list of (PackedWeight or C4Weight, x [M,K] bf16, y [M,N] fp32); all of one kind."""
         if not items:
             raise ValueError("no items")
         self.items = items
         self.M = items[0][1].shape[0] if items[0][1].dim() == 2 else 1
+        self.containers = isinstance(items[0][0], C4Weight)
         arr = (ql_gemv_desc * len(items))()
         for i, (pw, x, y) in enumerate(items):
+            if isinstance(pw, C4Weight) != self.containers:
+                raise ValueError("a grouped launch takes either containers or packed weights, not both")
             _dev(x, torch.bfloat16, "x")
             _dev(y, torch.float32, "y")
             m = x.shape[0] if x.dim() == 2 else 1
             if m != self.M or x.shape[-1] != pw.K or y.numel() != m * pw.N:
                 raise ValueError(f"item {i}: shapes do not match")
-            arr[i] = ql_gemv_desc(pw.packed.data_ptr(), pw.pscales.data_ptr(),
-                                  pw.blk_grid.data_ptr() if pw.blk_grid is not None else None,
-                                  pw.blk_off.data_ptr() if pw.blk_off is not None else None,
-                                  x.data_ptr(), y.data_ptr(), pw.N, pw.K, pw.grid, 0)
+            if self.containers:
+                arr[i] = ql_gemv_desc(pw.c4.data_ptr(), pw.pscales.data_ptr(), None, None, x.data_ptr(),
+                                      y.data_ptr(), pw.N, pw.K, GRID_C4, 0)
+            else:
+                arr[i] = ql_gemv_desc(pw.packed.data_ptr(), pw.pscales.data_ptr(),
+                                      pw.blk_grid.data_ptr() if pw.blk_grid is not None else None,
+                                      pw.blk_off.data_ptr() if pw.blk_off is not None else None,
+                                      x.data_ptr(), y.data_ptr(), pw.N, pw.K, pw.grid, 0)
         total = lib().qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(items))
         if total < 0:
             _check(1, "grouped_prepare")
@@ -271,6 +341,5 @@ class GroupedGemv:
         self.sched = torch.zeros(QL_SCHED_WORDS, dtype=torch.int32, device=items[0][1].device)
 
     def run(self):
-        _check(lib().qlinear_gemv_grouped(_ptr(self.descs), self.count, self.total, self.M, _ptr(self.sched),
-                                          _stream()),
-               "gemv_grouped")
+        fn = lib().qlinear_c4_gemv_grouped if self.containers else lib().qlinear_gemv_grouped
+        _check(fn(_ptr(self.descs), self.count, self.total, self.M, _ptr(self.sched), _stream()), "gemv_grouped")

@@ -156,7 +156,8 @@ typedef struct {
   int32_t slab_begin;       /* filled by qlinear_grouped_prepare */
 } ql_gemv_desc;
 
-/* Prepare a descriptor list (host array) for qlinear_gemv_grouped: check every entry, sort
+/* Prepare a descriptor list (host array) for qlinear_gemv_grouped (or, for a list of 4-bit
+ * containers, qlinear_c4_gemv_grouped; a list must not mix the two): check every entry, sort
  * the entries by K, largest first (stable; the products are independent, so their order
  * is free), fill slab_begin and return the total number of 64-row slabs (the task count),
  * or -1 on a bad descriptor.  Longest-first task order plus dynamic task fetching keeps
@@ -188,6 +189,52 @@ ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t *
                        const int64_t *blk_off, const void *packed, const uint16_t *pscales,
                        const uint16_t *x, float *y, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/* ---------------------------------------------------------------- 4-bit container baseline
+ *
+ * The summary page (onedev.kr/papers/1416, section "Premises & limits") says the
+ * published checkpoints hold the 1.6/2/3-bit codewords in 4-bit containers, and that this
+ * forfeits the memory and speed advantage.  These entry points store and multiply that
+ * format on the same GPU, so the two can be compared on equal terms:
+ *   container: code c (-8..7; every ThinkBit grid fits) as a two's complement nibble,
+ *              row bytes K/2, byte i of a row holding input 2i in its low nibble and
+ *              input 2i+1 in its high nibble; rows interleaved in 64-row slabs exactly as
+ *              the packed layout (bytes 16c..16c+15 of slab row r at c*1024 + r*16), so the
+ *              only difference to the packed layout is the number of bits per code.
+ *              Size ceil(N/64)*64*K/2 bytes; rows past N are zero.
+ *   scales:    the same packed scale array as the native layout.
+ * QL_GRID_C4 marks a container in a ql_gemv_desc; it is not a ThinkBit grid and the native
+ * entry points reject it. */
+#define QL_GRID_C4 4
+
+/* Container size of an N x K matrix (bytes); 0 if the shape is invalid. */
+int64_t qlinear_c4_bytes(int64_t N, int64_t K);
+
+/* Codes int8 [N][K] (dev, each in -8..7) -> container (dev, qlinear_c4_bytes). */
+ql_status qlinear_c4_pack(int64_t N, int64_t K, const int8_t *codes, void *c4, hipStream_t stream);
+
+/* Container (dev) -> codes int8 [N][K] (dev). */
+ql_status qlinear_c4_unpack(int64_t N, int64_t K, const void *c4, int8_t *codes, hipStream_t stream);
+
+/* Converter from a container checkpoint to the native packed layout: reads every code from
+ * the container and writes it as qlinear_pack would (grid, blk_grid, blk_off as there; the
+ * codes must lie in their block's grid).  packed (dev) has the packed size. */
+ql_status qlinear_c4_to_packed(int64_t N, int64_t K, int grid, const int8_t *blk_grid,
+                               const int64_t *blk_off, const void *c4, void *packed,
+                               hipStream_t stream);
+
+/* Batch-1 GEMV on a container: y[n] = sum_k c[n][k] * s[n][k/128] * x[k], M must be 1.
+ * Same numerics as qlinear_gemv (exact c*x products, fp32 sums per group, one scale
+ * multiply per group).  c4, pscales, x, y (dev). */
+ql_status qlinear_c4_gemv(int64_t M, int64_t N, int64_t K, const void *c4, const uint16_t *pscales,
+                          const uint16_t *x, float *y, hipStream_t stream);
+
+/* Grouped batch-1 GEMV over containers: as qlinear_gemv_grouped, for a descriptor list
+ * whose every entry has grid QL_GRID_C4 and packed pointing at a container (prepared by
+ * qlinear_grouped_prepare, which rejects lists mixing containers and native grids).
+ * Entries of another grid are skipped on the device (their y is not written). */
+ql_status qlinear_c4_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_slabs, int32_t M,
+                                  uint32_t *sched, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,10 @@ def lib():
         L.ora_dequant.restype = None
         L.ora_gemv.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
         L.ora_gemv.restype = None
+        L.ora_c4_bytes.argtypes = [i64, i64]
+        L.ora_c4_bytes.restype = i64
+        L.ora_c4_pack.argtypes = [i64, i64, vp, vp]
+        L.ora_c4_unpack.argtypes = [i64, i64, vp, vp]
         L.ora_gemv_packed.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32]
         _lib = L
     return _lib
@@ -177,6 +181,28 @@ def unpack(packed: np.ndarray, N: int, K: int, grid) -> np.ndarray:
         raise ValueError("invalid ternary byte (> 242)")
     if rc != 0:
         raise ValueError("bad shape or grid")
+    return codes
+
+
+def c4_pack(codes: np.ndarray) -> np.ndarray:
+    """Codes [N][K] (each in -8..7) -> the 4-bit container (two's complement nibbles,
+    lower input in the low nibble, 64-row slab interleave as the packed layout)."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    N, K = codes.shape
+    out = np.empty(int(lib().ora_c4_bytes(N, K)), dtype=np.uint8)
+    rc = lib().ora_c4_pack(N, K, _p(codes), _p(out))
+    if rc == -3:
+        raise ValueError("code outside -8..7")
+    if rc != 0:
+        raise ValueError("bad shape")
+    return out
+
+
+def c4_unpack(c4: np.ndarray, N: int, K: int) -> np.ndarray:
+    c4 = np.ascontiguousarray(c4, dtype=np.uint8)
+    codes = np.empty((N, K), dtype=np.int8)
+    if lib().ora_c4_unpack(N, K, _p(c4), _p(codes)) != 0:
+        raise ValueError("bad shape")
     return codes
 
 

@@ -23,6 +23,9 @@
 //     thirty-two 3-bit codes per 96-bit triple, 64-row slabs, 128-row grid
 //     blocks) is this project's own definition; the pages fix no bit order.
 //     It is written out once more, independently, in the HIP packer.
+//   * The 4-bit container the summary page (section "Premises & limits")
+//     says published checkpoints use, as the baseline format: codes as
+//     two's complement nibbles in the same slab interleave.
 //
 // Precision: codes are decided from an fp64 quotient; w = c*s is formed in
 // fp32 (exact: at most 11 significant bits); products and sums are fp64,
@@ -423,6 +426,59 @@ int ora_gemv_packed(int64_t M, int64_t N, int64_t K, const int8_t* blk_grid, con
     }
   });
   return bad ? -2 : 0;
+}
+
+// ---------------------------------------------------------------- 4-bit containers
+// The summary page (section "Premises & limits") says the published
+// checkpoints store the 1.6/2/3-bit codewords in 4-bit containers.  The
+// container here: the code itself as a 4-bit two's complement nibble (any
+// code in -8..7), two per byte, the lower input index in the low nibble; row
+// bytes K/2; rows interleaved in 64-row slabs chunk-major exactly as the
+// packed layout.  The pages give no nibble order; this one is the project's.
+int64_t ora_c4_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % kGroup) return 0;
+  return nslabs_of(N) * kSlab * (K / 2);
+}
+
+// Returns 0, -1 for a bad shape, -3 for a code outside -8..7.
+int ora_c4_pack(int64_t N, int64_t K, const int8_t* codes, uint8_t* out) {
+  if (!ora_c4_bytes(N, K)) return -1;
+  const int64_t rb = K / 2;
+  std::vector<uint8_t> row(rb);
+  for (int64_t n = 0; n < nslabs_of(N) * kSlab; ++n) {
+    for (int64_t i = 0; i < rb; ++i) {
+      int lo = 0, hi = 0;
+      if (n < N) {
+        lo = codes[n * K + 2 * i];
+        hi = codes[n * K + 2 * i + 1];
+      }
+      if (lo < -8 || lo > 7 || hi < -8 || hi > 7) return -3;
+      // two's complement nibbles: -1 -> 15, -8 -> 8
+      const unsigned nl = (unsigned)(lo < 0 ? lo + 16 : lo), nh = (unsigned)(hi < 0 ? hi + 16 : hi);
+      row[i] = (uint8_t)(nl + 16 * nh);
+    }
+    uint8_t* dst = out + (n / kSlab) * kSlab * rb;
+    for (int64_t c = 0; c < rb / kChunk; ++c)
+      std::memcpy(dst + c * kSlab * kChunk + (n % kSlab) * kChunk, row.data() + c * kChunk, kChunk);
+  }
+  return 0;
+}
+
+int ora_c4_unpack(int64_t N, int64_t K, const uint8_t* in, int8_t* codes) {
+  if (!ora_c4_bytes(N, K)) return -1;
+  const int64_t rb = K / 2;
+  std::vector<uint8_t> row(rb);
+  for (int64_t n = 0; n < N; ++n) {
+    const uint8_t* src = in + (n / kSlab) * kSlab * rb;
+    for (int64_t c = 0; c < rb / kChunk; ++c)
+      std::memcpy(row.data() + c * kChunk, src + c * kSlab * kChunk + (n % kSlab) * kChunk, kChunk);
+    for (int64_t i = 0; i < rb; ++i) {
+      const int nl = row[i] % 16, nh = row[i] / 16;
+      codes[n * K + 2 * i] = (int8_t)(nl >= 8 ? nl - 16 : nl);
+      codes[n * K + 2 * i + 1] = (int8_t)(nh >= 8 ? nh - 16 : nh);
+    }
+  }
+  return 0;
 }
 
 }  // extern "C"

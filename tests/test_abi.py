@@ -114,3 +114,30 @@ def test_grouped_prepare_orders_longest_rows_first():
     begins = [d.slab_begin for d in arr]
     assert begins == list(np.cumsum([0] + [(n + 63) // 64 for n, _, _ in got])[:-1])
     assert total == sum((n + 63) // 64 for n, _, _ in shapes)
+
+
+def test_container_sizes_and_argument_errors():
+    L = ql.lib()
+    assert L.qlinear_c4_bytes(130, 256) == 3 * 64 * 128
+    assert L.qlinear_c4_bytes(130, 100) == 0
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
+    assert L.qlinear_c4_gemv(2, 64, 128, p, p, p, p, None) == 2      # batch 1 only
+    assert L.qlinear_c4_gemv(1, 64, 100, p, p, p, p, None) == 1      # K % 128
+    assert L.qlinear_c4_gemv(1, 64, 128, None, p, p, p, None) == 1   # null container
+    assert L.qlinear_c4_pack(64, 128, ctypes.c_void_p(8), p, None) == 1  # misaligned
+    assert L.qlinear_c4_to_packed(64, 128, 4, None, None, p, p, None) == 1  # 4 is not a ThinkBit grid
+    assert L.qlinear_c4_gemv_grouped(p, 1, 1, 4, p, None) == 2
+    assert L.qlinear_c4_gemv_grouped(p, 1, 1, 1, None, None) == 1
+    assert L.qlinear_pack(64, 128, ql.GRID_C4, None, None, p, p, None) == 1  # native rejects containers
+
+
+def test_grouped_prepare_rejects_mixed_container_lists():
+    L = ql.lib()
+    arr = (ql.ql_gemv_desc * 2)()
+    arr[0] = ql.ql_gemv_desc(16, 32, None, None, 48, 64, 64, 128, ql.GRID_C4, 0)
+    arr[1] = ql.ql_gemv_desc(16, 32, None, None, 48, 64, 64, 256, ql.GRID_I2, 0)
+    assert L.qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), 2) == -1
+    assert b"mix" in L.qlinear_last_error()
+    arr[1] = ql.ql_gemv_desc(16, 32, None, None, 48, 64, 64, 256, ql.GRID_C4, 0)
+    assert L.qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), 2) == 2
+    assert arr[0].K == 256 and arr[0].slab_begin == 0 and arr[1].slab_begin == 1

@@ -419,3 +419,68 @@ def test_rel_err_definition(ora):
     yg = np.array([[3.0, 4.5], [0.0, 1.0]])
     e, nw = ora.rel_err(yg, y64)
     assert e == pytest.approx(0.5 / 5.0) and nw == pytest.approx(0.5 / np.sqrt(26))
+
+
+# ---------------------------------------------------------------- 4-bit container baseline
+# The container is this project's definition of the format the summary page
+# (section "Premises & limits") says published checkpoints use: each code as a
+# two's complement nibble, the lower input in the low nibble, rows in the same
+# 64-row slab interleave as the packed layout.  Pins: literal bytes worked out
+# by hand from that definition, positions in the slab interleave, the size
+# (4 + 16/128 = 4.125 bits per weight with scales), exhaustive round trips.
+
+def test_c4_hand_computed_bytes(ora):
+    codes = np.zeros((1, 128), np.int8)
+    codes[0, :8] = [-1, 2, -8, 7, 3, -4, 0, -2]
+    b = ora.c4_pack(codes)
+    # -1 -> 0xF, 2 -> 0x2 => 0x2F; -8 -> 0x8, 7 -> 0x7 => 0x78; 3, -4 (0xC) => 0xC3; 0, -2 (0xE) => 0xE0
+    assert list(b[:4]) == [0x2F, 0x78, 0xC3, 0xE0]
+    assert not b[4:].any()
+
+
+def test_c4_slab_positions(ora):
+    N, K = 130, 256
+    codes = np.zeros((N, K), np.int8)
+    codes[5, 70] = -3     # row 5, byte 35 (high nibble... input 70 is even -> low nibble)
+    codes[5, 71] = 1      # same byte, high nibble
+    codes[129, 255] = 6   # slab 2, row 1, byte 127 (high nibble)
+    b = ora.c4_pack(codes)
+    assert len(b) == 3 * 64 * 128 and ora.lib().ora_c4_bytes(N, K) == len(b)
+    # byte 35 of row 5: chunk 2 (bytes 32..47), offset 3 -> 2*1024 + 5*16 + 3
+    assert b[2 * 1024 + 5 * 16 + 3] == (13 + 16 * 1)
+    # slab 2 starts at 2 * 64 * 128; byte 127 of row 1: chunk 7, offset 15
+    assert b[2 * 64 * 128 + 7 * 1024 + 1 * 16 + 15] == 6 * 16
+    assert np.count_nonzero(b) == 2
+
+
+def test_c4_bits_per_weight(ora):
+    N, K = 4096, 4096
+    c4 = ora.lib().ora_c4_bytes(N, K)
+    sc = 2 * ora.lib().ora_packed_scales_len(N, K)
+    assert (c4 + sc) * 8 / (N * K) == 4.125
+
+
+@pytest.mark.parametrize("pos", range(32))
+def test_c4_every_value_at_every_chunk_position(ora, pos):
+    codes = np.zeros((16, 128), np.int8)
+    for v in range(-8, 8):
+        codes[v + 8, pos] = v
+        codes[v + 8, 32 + pos] = -1 - v  # and its complement in the next chunk
+    b = ora.c4_pack(codes)
+    assert np.array_equal(ora.c4_unpack(b, 16, 128), codes)
+    for v in range(-8, 8):
+        r = v + 8
+        byte = b[(pos // 2) // 16 * 1024 + r * 16 + (pos // 2) % 16]
+        nib = (byte >> 4) if pos % 2 else (byte & 15)
+        assert nib == (v & 15)
+
+
+def test_c4_random_round_trip_and_range(ora):
+    rng = np.random.default_rng(5)
+    codes = rng.integers(-8, 8, (70, 384)).astype(np.int8)
+    assert np.array_equal(ora.c4_unpack(ora.c4_pack(codes), 70, 384), codes)
+    for bad in (-9, 8):
+        c = codes.copy()
+        c[3, 7] = bad
+        with pytest.raises(ValueError):
+            ora.c4_pack(c)
