@@ -227,6 +227,8 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
   static_assert(M == 1, "the ternary GEMV runs batch 1");
   if (p0 >= p1) return;
   const int nchunks = (c.K + 79) / 80;
+  // the row's chunks end in the first half of its last period (p1 - 1)
+  const bool last_half = nchunks - 8 * (p1 - 1) <= 4;
   uint32_t lane_off = (uint32_t)(c.lane & 15) << 4;
   // chunks of the slab; later ones (and the ring's look-ahead past the end) read as zero
   const ChunkSrc src(c.codes, nchunks, c.lane);
@@ -256,7 +258,7 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
     }
     const bool more = p + 1 < p1;
     int x_off = 2 * kPeriodK * p;
-    sfor<kTUnits>([&](auto u) __attribute__((always_inline)) {
+    auto step = [&](auto u) __attribute__((always_inline)) {
       constexpr int U = decltype(u)::value;
       constexpr bool odd = (U & 1) != 0;
       auto& cur = odd ? B : A;
@@ -283,7 +285,12 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
       sched_fence();
       pin_s(x_off);
       lgkm_wait0();
-    });
+    };
+    // The second half-period of the last period is skipped when the row ends
+    // in its first half (all of it would be padding against zero activations).
+    sfor<kTUnits / 2>(step);
+    if (more || !last_half)
+      sfor_from<kTUnits / 2, kTUnits / 2>(step);
 #pragma unroll
     for (int gl = 0; gl < 5; ++gl) y[0] = fmaf(sc[gl], acc[gl], y[0]);
   }

@@ -25,6 +25,15 @@ template <int N, class F>
 __device__ __forceinline__ void sfor(F&& f) {
   sfor_impl(f, std::make_integer_sequence<int, N>{});
 }
+// f(B), f(B+1), ..., f(B+N-1) with compile-time arguments
+template <int B, class F, int... I>
+__device__ __forceinline__ void sfor_from_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, B + I>{}), ...);
+}
+template <int B, int N, class F>
+__device__ __forceinline__ void sfor_from(F&& f) {
+  sfor_from_impl<B>(f, std::make_integer_sequence<int, N>{});
+}
 
 // s_waitcnt lgkmcnt(0), leaving vmcnt/expcnt alone.
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
