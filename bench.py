@@ -13,7 +13,8 @@ sample of the same workload.  A "gemm" object adds the batched path on one
 Qwen3-8B-shaped layer (mixed grids, M = 64 / 256 / 512): microseconds per layer
 and MFMA utilisation against the dense bf16 peak; "container_ab" times the
 Qwen3-8B pass and the Qwen3-14B stack (M = 1) once more with the same codes stored
-in 4-bit containers, the format published checkpoints use.
+in 4-bit containers, the format published checkpoints use; "allocator" allocates the
+8B pass's grids by the Lagrangian knapsack and runs the pass with them.
 """
 from __future__ import annotations
 
@@ -41,8 +42,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_pass(wl, wl_index, M, dev):
-    """Quantize and pack every linear of the workload on the GPU; return items and bookkeeping."""
+def build_pass(wl, wl_index, M, dev, tables=None):
+    """Quantize and pack every linear of the workload on the GPU; return items and bookkeeping.
+    tables: {layer: {linear: grid per 128-row block}} in place of the seeded mixed allocation."""
     import torch
     from decode_gemv_thinkbit_amd import qlinear as ql
     from decode_gemv_thinkbit_amd import synth
@@ -51,7 +53,7 @@ def build_pass(wl, wl_index, M, dev):
     stored = 0
     xs = {}
     for layer in range(wl.layers):
-        alloc = synth.allocation(wl, layer)
+        alloc = synth.allocation(wl, layer) if tables is None else tables[layer]
         for slot in ("attn", "o", "mlp", "down"):
             K = next(l.K for l in wl.linears if l.x_slot == slot)
             xs[(layer, slot)] = synth.activations(M, K, synth.x_seed(wl_index, layer, slot, M), device=dev)
@@ -141,6 +143,51 @@ def container_ab(wl_name, dev, warmup, steps, native=None):
     del c_items
     torch.cuda.empty_cache()
     return out
+
+
+def allocator_leg(dev, warmup, steps, budget_bits=2.0):
+    """Grid allocation of the Qwen3-8B pass by the Lagrangian knapsack (128-row block units,
+    q/k kept at >= 2 bits): GPU noise time, host solve time, the resulting mix, and the pass
+    run with those grids."""
+    import numpy as np
+    import torch
+    from decode_gemv_thinkbit_amd import allocation, configs
+    from decode_gemv_thinkbit_amd import qlinear as ql
+    from decode_gemv_thinkbit_amd import synth
+
+    wl = configs.WORKLOADS["qwen3_8b_pass"]
+    wi = list(configs.WORKLOADS).index(wl.name)
+    st = torch.cuda.current_stream()
+    noise_ms = 0.0
+    for layer in range(wl.layers):
+        for mi, lin in enumerate(wl.linears):
+            W = synth.weight(lin.N, lin.K, synth.weight_seed(wi, layer, mi), device=dev)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(st)
+            ql.rtn_noise(W)
+            e.record(st)
+            e.synchronize()
+            noise_ms += s.elapsed_time(e)
+            del W
+    units = allocation.workload_units(wl, wi, dev)
+    t0 = time.perf_counter()
+    grids, lam = ql.allocate(units.weights, units.sensitivity, units.noise, units.allowed, budget_bits)
+    solve_ms = (time.perf_counter() - t0) * 1e3
+    sh = allocation.shares(units, grids)
+    bits = float((units.weights * np.array([np.log2(3.0) + 0.125, 2.125, 3.125])[grids]).sum() / units.weights.sum())
+    tables = allocation.tables_from(units, grids, wl)
+    items, _, stored, _ = build_pass(wl, wi, 1, dev, tables=tables)
+    ms, _ = time_grouped(ql.GroupedGemv(items), warmup, steps)
+    del items
+    torch.cuda.empty_cache()
+    log(f"allocator: {len(grids)} units, noise {noise_ms:.1f} ms (GPU), solve {solve_ms:.1f} ms (host), "
+        f"T {sh[0]:.3f} I2 {sh[1]:.3f} I3 {sh[2]:.3f}, {bits:.4f} bits/weight; pass {ms * 1e3:.1f} us")
+    return {"workload": wl.name, "units": "128-row blocks", "count": int(len(grids)), "budget_bits": budget_bits,
+            "noise_gpu_ms": round(noise_ms, 2), "solve_host_ms": round(solve_ms, 2), "lambda": lam,
+            "shares": {"T": round(sh[0], 4), "I2": round(sh[1], 4), "I3": round(sh[2], 4)},
+            "bits_per_weight": round(bits, 5),
+            "pass_us": round(ms * 1e3, 2), "pass_stored_bytes": stored,
+            "pass_gbs": round(stored / (ms * 1e-3) / 1e9, 1)}
 
 
 def kernel_source_hash() -> str:
@@ -317,6 +364,7 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the batched (MFMA) leg")
     ap.add_argument("--no-ab", action="store_true", help="skip the 4-bit container A/B leg")
+    ap.add_argument("--no-alloc", action="store_true", help="skip the grid allocation leg")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -392,6 +440,8 @@ def main():
         result["container_ab"] = [container_ab(args.workload, dev, args.warmup, args.steps,
                                                native=(ms_step, stored)),
                                   container_ab("qwen3_14b_stack", dev, args.warmup, args.steps)]
+    if not args.no_alloc:
+        result["allocator"] = allocator_leg(dev, args.warmup, args.steps)
     if not args.no_gemm:
         result["gemm"] = gemm_leg(dev)
     if not args.no_cpu_baseline:

@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 
 #include "ql_internal.hpp"
@@ -203,6 +204,33 @@ ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t
 }
 
 size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return ql::gemm_workspace_bytes(M, N, K); }
+
+// ---------------------------------------------------------------- grid allocation
+ql_status qlinear_rtn_noise(int64_t N, int64_t K, const float* W, double* noise, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_ptrs({W, noise}));
+  return hip_status(ql::launch_rtn_noise(N, K, W, noise, stream), "rtn_noise launch");
+}
+
+ql_status qlinear_allocate(const ql_alloc_unit* units, int64_t count, double budget_bits, const double* grid_bits,
+                           int8_t* grid_out, double* lambda_out) {
+  if (!units || !grid_out || count <= 0) return fail(QL_EINVAL, "allocate needs units, an output and count > 0");
+  static const double kDefaultBits[3] = {1.584962500721156 + 0.125, 2.125, 3.125};  // log2(3) + 1/8, ...
+  const double* bits = grid_bits ? grid_bits : kDefaultBits;
+  for (int g = 0; g < 3; ++g)
+    if (!(bits[g] > 0.0) || !std::isfinite(bits[g])) return fail(QL_EINVAL, "grid_bits[%d] must be positive", g);
+  if (!(budget_bits > 0.0) || !std::isfinite(budget_bits)) return fail(QL_EINVAL, "budget must be positive");
+  for (int64_t i = 0; i < count; ++i) {
+    const ql_alloc_unit& u = units[i];
+    bool ok = u.weights > 0 && u.sensitivity >= 0.0 && std::isfinite(u.sensitivity) && (u.allowed & 7u) &&
+              !(u.allowed & ~7u);
+    for (int g = 0; g < 3; ++g) ok = ok && u.noise[g] >= 0.0 && std::isfinite(u.noise[g]);
+    if (!ok) return fail(QL_EINVAL, "unit %lld: bad weights, sensitivity, noise or allowed mask", (long long)i);
+  }
+  if (ql::allocate_grids(units, count, budget_bits, bits, grid_out, lambda_out) != 0)
+    return fail(QL_EINVAL, "budget %.4f bits per weight is below the cheapest allowed grids", budget_bits);
+  return QL_OK;
+}
 
 // ---------------------------------------------------------------- 4-bit container baseline
 int64_t qlinear_c4_bytes(int64_t N, int64_t K) {

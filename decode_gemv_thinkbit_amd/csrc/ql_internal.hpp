@@ -39,6 +39,11 @@ hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int6
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+hipError_t launch_rtn_noise(int64_t N, int64_t K, const float* W, double* noise, hipStream_t stream);
+// 0, -2 when the cheapest allowed grids exceed the budget
+int allocate_grids(const ql_alloc_unit* units, int64_t count, double budget, const double* bits, int8_t* out,
+                   double* lam_out);
+
 int device_cu_count();
 
 }  // namespace ql

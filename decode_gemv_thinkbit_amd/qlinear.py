@@ -37,6 +37,11 @@ class ql_gemv_desc(ctypes.Structure):
                 ("slab_begin", ctypes.c_int32)]
 
 
+class ql_alloc_unit(ctypes.Structure):
+    _fields_ = [("weights", ctypes.c_int64), ("sensitivity", ctypes.c_double), ("noise", ctypes.c_double * 3),
+                ("allowed", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
 def lib():
     """Load libqlinear.so; raise if it has not been built."""
     global _lib
@@ -67,6 +72,8 @@ def lib():
         L.qlinear_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.qlinear_gemm_workspace_bytes.restype = sz
         L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qlinear_rtn_noise.argtypes = [i64, i64, vp, vp, vp]
+        L.qlinear_allocate.argtypes = [vp, i64, ctypes.c_double, vp, vp, vp]
         L.qlinear_c4_bytes.argtypes = [i64, i64]
         L.qlinear_c4_bytes.restype = i64
         L.qlinear_c4_pack.argtypes = [i64, i64, vp, vp, vp]
@@ -77,7 +84,8 @@ def lib():
         for name in ("qlinear_block_offsets", "qlinear_quantize", "qlinear_pack", "qlinear_pack_scales",
                      "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
                      "qlinear_gemv_grouped", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
-                     "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped"):
+                     "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped", "qlinear_rtn_noise",
+                     "qlinear_allocate"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -210,6 +218,43 @@ def dequant(pw: PackedWeight, out_bf16: bool = False) -> torch.Tensor:
     _check(lib().qlinear_dequant(pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
                                  _ptr(pw.pscales), 1 if out_bf16 else 0, _ptr(out), _stream()), "dequant")
     return out
+
+
+# ---------------------------------------------------------------- grid allocation (offline)
+ALL_GRIDS, AT_LEAST_2BIT = 0b111, 0b110  # allowed-grid masks
+
+
+def rtn_noise(W: torch.Tensor) -> torch.Tensor:
+    """float64 [ceil(N/128), 3] on the device: per 128-row block, sum of (w - c*s)^2 of the
+    round-to-nearest quantization onto T, I2, I3."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    out = torch.empty((n_blocks(N), 3), dtype=torch.float64, device=W.device)
+    _check(lib().qlinear_rtn_noise(N, K, _ptr(W), _ptr(out), _stream()), "rtn_noise")
+    return out
+
+
+def allocate(weights, sensitivity, noise, allowed, budget_bits: float, grid_bits=None):
+    """Lagrangian multiple-choice knapsack over units (host): (grid per unit int8, multiplier)."""
+    weights = np.asarray(weights, dtype=np.int64)
+    count = len(weights)
+    sensitivity = np.asarray(sensitivity, dtype=np.float64).reshape(count)
+    noise = np.asarray(noise, dtype=np.float64).reshape(count, 3)
+    allowed = np.broadcast_to(np.asarray(allowed, dtype=np.uint32), (count,))
+    units = (ql_alloc_unit * count)()
+    for i in range(count):
+        units[i].weights = int(weights[i])
+        units[i].sensitivity = float(sensitivity[i])
+        for g in range(3):
+            units[i].noise[g] = float(noise[i, g])
+        units[i].allowed = int(allowed[i])
+    out = np.empty(count, dtype=np.int8)
+    lam = ctypes.c_double(0.0)
+    bits = None if grid_bits is None else np.ascontiguousarray(grid_bits, dtype=np.float64)
+    _check(lib().qlinear_allocate(ctypes.cast(units, ctypes.c_void_p), count, float(budget_bits),
+                                  None if bits is None else bits.ctypes.data_as(ctypes.c_void_p),
+                                  out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(lam)), "allocate")
+    return out, lam.value
 
 
 # ---------------------------------------------------------------- 4-bit containers (baseline)

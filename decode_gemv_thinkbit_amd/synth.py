@@ -9,6 +9,8 @@ check receive exactly the arrays it returns.
   summary page serves are not available; these stand in for them with the
   same shapes.
 * Activations: x ~ N(0, 1), rounded to bf16 by torch.
+* Output gradients for the allocator's sensitivities: N(0, sigma^2) with a
+  log-normal sigma per linear (``output_gradient``).
 * Mixed allocation (summary page onedev.kr/papers/1416, section "How it
   differs": 75.3 % ternary, 6.0 % 2-bit, 18.7 % 3-bit of a layer's weights;
   query/key kept at >= 2 bits, here forced to 3 bits): per layer, every
@@ -99,6 +101,17 @@ def realized_shares(wl: Workload) -> dict:
                 tot[int(g)] += min(BLOCK_ROWS, l.N - b * BLOCK_ROWS) * l.K
     s = sum(tot.values())
     return {k: v / s for k, v in tot.items()}
+
+
+def output_gradient(N: int, wl_index: int, layer: int, mat: int, device="cpu") -> torch.Tensor:
+    """Synthetic output gradient of one linear, fp32 [N]: N(0, sigma^2) per element with a
+    per-linear log-normal sigma = exp(z / 2), z ~ N(0, 1).  (The real gradients come from
+    calibration data on a trained model, which this build does not have.)"""
+    rng = np.random.default_rng(seed_of(5, wl_index, layer, mat))
+    sigma = float(np.exp(0.5 * rng.standard_normal()))
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(6, wl_index, layer, mat))
+    return torch.randn(N, generator=g, device=device, dtype=torch.float32) * sigma
 
 
 def weight_seed(wl_index: int, layer: int, mat: int) -> int:

@@ -190,6 +190,39 @@ ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t *
                        const uint16_t *x, float *y, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* ---------------------------------------------------------------- grid allocation (offline)
+ *
+ * Summary page, section "How it differs", stage 1 (Allocate): the sensitivity S of a layer
+ * (product of the squared norms of its input activations and of its output gradients) times
+ * the rounding noise of a grid approximates the loss increase of storing the layer on that
+ * grid; one grid per layer is chosen under a bit budget for the whole decoder, a
+ * multiple-choice knapsack solved by Lagrangian relaxation.  A unit here is any set of rows
+ * the caller groups (a linear, or a 128-row grid block of one). */
+typedef struct {
+  int64_t weights;      /* weights in the unit, > 0 */
+  double sensitivity;   /* S >= 0 */
+  double noise[3];      /* rounding noise of grids T, I2, I3 (each >= 0), e.g. from qlinear_rtn_noise */
+  uint32_t allowed;     /* bit g set: grid g may be chosen (nonzero; e.g. 6 keeps a unit at >= 2 bits) */
+  uint32_t reserved;    /* 0 */
+} ql_alloc_unit;
+
+/* Rounding noise of round-to-nearest (the rule of qlinear_quantize) onto each grid, per
+ * 128-row block: noise[b*3 + g] = sum over block b's weights of (w - c*s)^2 in fp64.
+ * W (dev) fp32 [N][K]; noise (dev) double [ceil(N/128)][3].  Deterministic. */
+ql_status qlinear_rtn_noise(int64_t N, int64_t K, const float *W, double *noise, hipStream_t stream);
+
+/* Lagrangian multiple-choice knapsack (host only, no GPU).  For a multiplier lam >= 0 every
+ * unit takes the allowed grid minimising S*noise[g] + lam*weights*grid_bits[g] (ties to fewer
+ * bits); the result is the assignment at the smallest lam whose total bits fit
+ * budget_bits * (sum of weights).  That assignment is optimal among all assignments using no
+ * more bits than it does (it may leave part of the budget unused: the relaxation's gap).
+ *   units (host, count); grid_bits (host, 3 values, bits per weight of T, I2, I3 including
+ *   the scale; NULL = log2(3) + 1/8, 2 + 1/8, 3 + 1/8); grid_out (host, count) receives the
+ *   grid of each unit; lambda_out (host, may be NULL) the multiplier.
+ * Returns QL_EINVAL on bad input or when even the cheapest allowed grids exceed the budget. */
+ql_status qlinear_allocate(const ql_alloc_unit *units, int64_t count, double budget_bits, const double *grid_bits,
+                           int8_t *grid_out, double *lambda_out);
+
 /* ---------------------------------------------------------------- 4-bit container baseline
  *
  * The summary page (onedev.kr/papers/1416, section "Premises & limits") says the

@@ -76,6 +76,9 @@ def lib():
         L.ora_c4_bytes.restype = i64
         L.ora_c4_pack.argtypes = [i64, i64, vp, vp]
         L.ora_c4_unpack.argtypes = [i64, i64, vp, vp]
+        L.ora_rtn_noise.argtypes = [i64, i64, vp, vp]
+        L.ora_block_sensitivity.argtypes = [i64, vp, i64, vp, vp]
+        L.ora_allocate.argtypes = [i64, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
         L.ora_gemv_packed.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i32]
         _lib = L
     return _lib
@@ -273,3 +276,48 @@ def rel_err(y_gpu: np.ndarray, y64: np.ndarray) -> tuple[float, float]:
     per_row = np.max(np.abs(d), axis=1) / rown
     tot = np.linalg.norm(y64)
     return float(per_row.max()), float(np.linalg.norm(d) / (tot if tot else 1.0))
+
+
+# ---------------------------------------------------------------- grid allocation
+# Bits per weight of each grid for the budget: code bits plus one bf16 scale per
+# 128 weights; ternary carries log2(3) bits of information per code.
+GRID_BITS = np.array([np.log2(3.0) + 16 / 128, 2 + 16 / 128, 3 + 16 / 128])
+
+
+def rtn_noise(W: np.ndarray) -> np.ndarray:
+    """[ceil(N/128)][3]: sum over each 128-row block of (w - c*s)^2 for the T, I2, I3
+    round-to-nearest quantizations (fp64)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    out = np.empty((n_blocks(N), 3), dtype=np.float64)
+    if lib().ora_rtn_noise(N, K, _p(W), _p(out)) != 0:
+        raise ValueError("bad shape or non-finite weight")
+    return out
+
+
+def block_sensitivity(x_bf16: np.ndarray, grad: np.ndarray) -> np.ndarray:
+    """S per 128-row block: ||x||^2 * sum of the block's squared output gradients (fp64)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1)
+    g = np.ascontiguousarray(grad, dtype=np.float32).reshape(-1)
+    out = np.empty(n_blocks(len(g)), dtype=np.float64)
+    if lib().ora_block_sensitivity(len(x), _p(x), len(g), _p(g), _p(out)) != 0:
+        raise ValueError("bad shape")
+    return out
+
+
+def allocate(n, S, E, allowed, budget: float, bits=None) -> tuple[np.ndarray, float]:
+    """Lagrangian multiple-choice knapsack: grid per unit and the multiplier used."""
+    n = np.ascontiguousarray(n, dtype=np.int64)
+    S = np.ascontiguousarray(S, dtype=np.float64)
+    E = np.ascontiguousarray(E, dtype=np.float64).reshape(len(n), 3)
+    allowed = np.ascontiguousarray(allowed, dtype=np.uint32)
+    bits = np.ascontiguousarray(GRID_BITS if bits is None else bits, dtype=np.float64)
+    out = np.empty(len(n), dtype=np.int8)
+    lam = ctypes.c_double(0.0)
+    rc = lib().ora_allocate(len(n), _p(n), _p(S), _p(E), _p(allowed), _p(bits), float(budget), _p(out),
+                            ctypes.byref(lam))
+    if rc == -2:
+        raise ValueError("budget below the cheapest allowed grids")
+    if rc != 0:
+        raise ValueError("bad allocation input")
+    return out, lam.value

@@ -23,6 +23,9 @@
 //     thirty-two 3-bit codes per 96-bit triple, 64-row slabs, 128-row grid
 //     blocks) is this project's own definition; the pages fix no bit order.
 //     It is written out once more, independently, in the HIP packer.
+//   * The grid allocation of the same page, section "How it differs"
+//     (stage 1): rounding noise per grid, and a multiple-choice knapsack
+//     over grids under a bit budget solved by Lagrangian relaxation.
 //   * The 4-bit container the summary page (section "Premises & limits")
 //     says published checkpoints use, as the baseline format: codes as
 //     two's complement nibbles in the same slab interleave.
@@ -479,6 +482,127 @@ int ora_c4_unpack(int64_t N, int64_t K, const uint8_t* in, int8_t* codes) {
     }
   }
   return 0;
+}
+
+// ---------------------------------------------------------------- grid allocation
+// Summary page, section "How it differs", stage 1 (Allocate): a layer's
+// sensitivity S (product of the squared norms of its input activations and
+// of its output gradients, a Kronecker-factored curvature estimate) times the
+// rounding noise of each grid approximates the loss increase of giving the
+// layer that grid; ternary / 2-bit / 3-bit are chosen per layer under a bit
+// budget for the whole decoder as a multiple-choice knapsack, solved by
+// Lagrangian relaxation.
+
+// Rounding noise of round-to-nearest onto each grid, per 128-row block:
+// noise[b*3 + g] = sum over the block's weights of (w - c*s)^2, with c and s
+// from the quantizer above, summed in fp64 in ascending (row, input) order.
+int ora_rtn_noise(int64_t N, int64_t K, const float* W, double* noise) {
+  if (N <= 0 || K <= 0 || K % kGroup) return -1;
+  const int64_t G = K / kGroup;
+  std::vector<int8_t> codes(K);
+  std::vector<uint16_t> scales(G);
+  for (int64_t b = 0; b < nblocks_of(N); ++b)
+    for (int grid = 0; grid < 3; ++grid) {
+      const int8_t rg = (int8_t)grid;
+      double sum = 0.0;
+      for (int64_t n = b * kBlock; n < std::min<int64_t>(N, (b + 1) * kBlock); ++n) {
+        if (ora_quantize(1, K, &rg, W + n * K, codes.data(), scales.data())) return -1;
+        for (int64_t k = 0; k < K; ++k) {
+          const double e = (double)W[n * K + k] - (double)codes[k] * (double)bf16_to_f32(scales[k / kGroup]);
+          sum += e * e;
+        }
+      }
+      noise[b * 3 + grid] = sum;
+    }
+  return 0;
+}
+
+// Sensitivity of every 128-row block of a linear: the squared norm of its
+// input activation times the squared norm of the block's output gradient,
+// each summed in fp64 in ascending index order.
+int ora_block_sensitivity(int64_t K, const uint16_t* x_bf16, int64_t N, const float* grad, double* S) {
+  if (K <= 0 || N <= 0) return -1;
+  double xs = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    const double v = (double)bf16_to_f32(x_bf16[k]);
+    xs += v * v;
+  }
+  for (int64_t b = 0; b < nblocks_of(N); ++b) {
+    double gs = 0.0;
+    for (int64_t n = b * kBlock; n < std::min<int64_t>(N, (b + 1) * kBlock); ++n) gs += (double)grad[n] * (double)grad[n];
+    S[b] = xs * gs;
+  }
+  return 0;
+}
+
+// Multiple-choice knapsack by Lagrangian relaxation.  Unit i has n[i]
+// weights, sensitivity S[i], noise E[i*3 + g] and a mask of allowed grids.
+// For a multiplier lam >= 0 every unit independently takes the allowed grid
+// minimising S*E[g] + lam*(n*bits[g]), scanning grids in increasing bits and
+// keeping the first minimum (ties go to fewer bits).  The bits used fall as
+// lam grows, and a unit's choice changes only where two of its costs cross,
+// so the assignments are constant between consecutive crossings.  Each such
+// interval is tried at one interior point (0, the midpoints, twice the last
+// crossing; interior so that no cost comparison sits on a rounding tie), in
+// increasing order, and the first whose total bits fit budget * sum(n) is
+// returned with that multiplier.  Returns 0, -1 for bad input, -2 if even the
+// cheapest allowed grids exceed the budget.
+namespace {
+double unit_cost(double S, double E, double lam, int64_t n, double bits) { return S * E + lam * ((double)n * bits); }
+
+int pick(int64_t n, double S, const double* E, uint32_t allowed, const double* bits, const int* order, double lam) {
+  int best = -1;
+  double bc = 0.0;
+  for (int t = 0; t < 3; ++t) {
+    const int g = order[t];
+    if (!(allowed >> g & 1u)) continue;
+    const double c = unit_cost(S, E[g], lam, n, bits[g]);
+    if (best < 0 || c < bc) {
+      best = g;
+      bc = c;
+    }
+  }
+  return best;
+}
+}  // namespace
+
+int ora_allocate(int64_t count, const int64_t* n, const double* S, const double* E, const uint32_t* allowed,
+                 const double* bits, double budget, int8_t* out, double* lam_out) {
+  if (count <= 0) return -1;
+  int order[3] = {0, 1, 2};
+  std::sort(order, order + 3, [&](int a, int b) { return bits[a] < bits[b] || (bits[a] == bits[b] && a < b); });
+  double total_n = 0.0;
+  for (int64_t i = 0; i < count; ++i) {
+    if (n[i] <= 0 || !(S[i] >= 0.0) || !(allowed[i] & 7u)) return -1;
+    for (int g = 0; g < 3; ++g)
+      if (!(E[i * 3 + g] >= 0.0)) return -1;
+    total_n += (double)n[i];
+  }
+  const double cap = budget * total_n;
+  std::vector<double> cand{0.0};
+  for (int64_t i = 0; i < count; ++i)
+    for (int a = 0; a < 3; ++a)
+      for (int b = 0; b < 3; ++b) {
+        if (!(allowed[i] >> a & 1u) || !(allowed[i] >> b & 1u) || !(bits[a] < bits[b])) continue;
+        const double lam = (S[i] * E[i * 3 + a] - S[i] * E[i * 3 + b]) / ((double)n[i] * (bits[b] - bits[a]));
+        if (lam > 0.0) cand.push_back(lam);
+      }
+  std::sort(cand.begin(), cand.end());
+  cand.erase(std::unique(cand.begin(), cand.end()), cand.end());
+  std::vector<double> pts{0.0};
+  for (size_t j = 1; j < cand.size(); ++j)
+    pts.push_back(j + 1 < cand.size() ? 0.5 * (cand[j] + cand[j + 1]) : 2.0 * cand[j]);
+  if (cand.size() > 1) pts.insert(pts.begin() + 1, 0.5 * cand[1]);
+  for (double lam : pts) {
+    double used = 0.0;
+    for (int64_t i = 0; i < count; ++i) used += (double)n[i] * bits[pick(n[i], S[i], E + 3 * i, allowed[i], bits, order, lam)];
+    if (used <= cap) {
+      for (int64_t i = 0; i < count; ++i) out[i] = (int8_t)pick(n[i], S[i], E + 3 * i, allowed[i], bits, order, lam);
+      if (lam_out) *lam_out = lam;
+      return 0;
+    }
+  }
+  return -2;
 }
 
 }  // extern "C"
