@@ -232,6 +232,66 @@ ql_status qlinear_allocate(const ql_alloc_unit* units, int64_t count, double bud
   return QL_OK;
 }
 
+// ---------------------------------------------------------------- LittleBit
+static bool lb_shape_ok(int64_t d_out, int64_t d_in, int64_t rank) {
+  return d_out > 0 && d_in > 0 && rank > 0 && d_in % 128 == 0 && d_out <= kMaxDim && d_in <= kMaxDim &&
+         rank <= d_out + d_in && rank <= kMaxDim;
+}
+
+double qlinear_lb_bpw(int64_t d_out, int64_t d_in, int64_t rank) {
+  if (d_out <= 0 || d_in <= 0 || rank < 0) return 0.0;
+  return ((2.0 * rank + 32.0) * (double)(d_out + d_in) + 32.0 * rank) / ((double)d_out * (double)d_in);
+}
+
+int64_t qlinear_lb_rank(int64_t d_out, int64_t d_in, double bpw) {
+  if (d_out <= 0 || d_in <= 0 || !(bpw > 0.0)) return 0;
+  // b(r) is linear in r: solve, then step to the largest r with b(r) <= bpw
+  const double per = (2.0 * (double)(d_out + d_in) + 32.0) / ((double)d_out * (double)d_in);
+  int64_t r = (int64_t)std::floor((bpw - qlinear_lb_bpw(d_out, d_in, 0)) / per);
+  if (r < 0) r = 0;
+  while (r > 0 && qlinear_lb_bpw(d_out, d_in, r) > bpw) --r;
+  while (qlinear_lb_bpw(d_out, d_in, r + 1) <= bpw) ++r;
+  return r;
+}
+
+int64_t qlinear_lb_u_bytes(int64_t d_out, int64_t rank) {
+  if (d_out <= 0 || rank <= 0 || d_out > kMaxDim || rank > kMaxDim) return 0;
+  return (d_out + QL_SLAB - 1) / QL_SLAB * QL_SLAB * ql::lb_u_row_bytes(rank);
+}
+
+int64_t qlinear_lb_v_bytes(int64_t d_in, int64_t rank) {
+  if (d_in <= 0 || d_in % 128 || rank <= 0 || d_in > kMaxDim || rank > kMaxDim) return 0;
+  return 2 * ql::lb_latent_rows(rank) * (d_in / 8);
+}
+
+ql_status qlinear_lb_pack(int64_t d_out, int64_t d_in, int64_t rank, const int8_t* u_signs, const int8_t* v_signs,
+                          void* u_bits, void* v_bits, hipStream_t stream) {
+  if (!lb_shape_ok(d_out, d_in, rank))
+    return fail(QL_EINVAL, "bad LittleBit shape (d_out=%lld, d_in=%lld, rank=%lld; d_in %% 128 == 0)",
+                (long long)d_out, (long long)d_in, (long long)rank);
+  QL_TRY(check_ptrs({u_signs, v_signs, u_bits, v_bits}));
+  return hip_status(ql::launch_lb_pack(d_out, d_in, rank, u_signs, v_signs, static_cast<uint8_t*>(u_bits),
+                                       static_cast<uint8_t*>(v_bits), stream),
+                    "lb_pack launch");
+}
+
+size_t qlinear_lb_workspace_bytes(int64_t d_out, int64_t d_in, int64_t rank) {
+  if (!lb_shape_ok(d_out, d_in, rank)) return 0;
+  return ql::lb_workspace_bytes(d_out, d_in, rank);
+}
+
+ql_status qlinear_lb_gemv(const ql_littlebit* w, const uint16_t* x, float* y, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!w) return fail(QL_EINVAL, "null LittleBit weight");
+  if (!lb_shape_ok(w->d_out, w->d_in, w->rank))
+    return fail(QL_EINVAL, "bad LittleBit shape (d_out=%d, d_in=%d, rank=%d; d_in %% 128 == 0)", w->d_out, w->d_in,
+                w->rank);
+  QL_TRY(check_ptrs({w->u_bits, w->v_bits, w->g, w->l, w->h, x, y, workspace}));
+  const size_t need = ql::lb_workspace_bytes(w->d_out, w->d_in, w->rank);
+  if (workspace_bytes < need) return fail(QL_EINVAL, "workspace too small (%zu < %zu)", workspace_bytes, need);
+  return hip_status(ql::launch_lb_gemv(*w, x, y, workspace, stream), "lb_gemv launch");
+}
+
 // ---------------------------------------------------------------- 4-bit container baseline
 int64_t qlinear_c4_bytes(int64_t N, int64_t K) {
   if (check_shape(N, K) != QL_OK) return 0;

@@ -44,6 +44,13 @@ hipError_t launch_rtn_noise(int64_t N, int64_t K, const float* W, double* noise,
 int allocate_grids(const ql_alloc_unit* units, int64_t count, double budget, const double* bits, int8_t* out,
                    double* lam_out);
 
+int64_t lb_latent_rows(int64_t r);
+int64_t lb_u_row_bytes(int64_t r);
+size_t lb_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r);
+hipError_t launch_lb_pack(int64_t d_out, int64_t d_in, int64_t r, const int8_t* u_signs, const int8_t* v_signs,
+                          uint8_t* u_bits, uint8_t* v_bits, hipStream_t stream);
+hipError_t launch_lb_gemv(const ql_littlebit& w, const uint16_t* x, float* y, void* ws, hipStream_t stream);
+
 int device_cu_count();
 
 }  // namespace ql

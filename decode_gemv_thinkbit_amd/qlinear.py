@@ -42,6 +42,12 @@ class ql_alloc_unit(ctypes.Structure):
                 ("allowed", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
+class ql_littlebit(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("u_bits", ctypes.c_void_p), ("v_bits", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("l", ctypes.c_void_p), ("h", ctypes.c_void_p)]
+
+
 def lib():
     """Load libqlinear.so; raise if it has not been built."""
     global _lib
@@ -74,6 +80,18 @@ def lib():
         L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qlinear_rtn_noise.argtypes = [i64, i64, vp, vp, vp]
         L.qlinear_allocate.argtypes = [vp, i64, ctypes.c_double, vp, vp, vp]
+        L.qlinear_lb_bpw.argtypes = [i64, i64, i64]
+        L.qlinear_lb_bpw.restype = ctypes.c_double
+        L.qlinear_lb_rank.argtypes = [i64, i64, ctypes.c_double]
+        L.qlinear_lb_rank.restype = i64
+        L.qlinear_lb_u_bytes.argtypes = [i64, i64]
+        L.qlinear_lb_u_bytes.restype = i64
+        L.qlinear_lb_v_bytes.argtypes = [i64, i64]
+        L.qlinear_lb_v_bytes.restype = i64
+        L.qlinear_lb_pack.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
+        L.qlinear_lb_workspace_bytes.argtypes = [i64, i64, i64]
+        L.qlinear_lb_workspace_bytes.restype = sz
+        L.qlinear_lb_gemv.argtypes = [vp, vp, vp, vp, sz, vp]
         L.qlinear_c4_bytes.argtypes = [i64, i64]
         L.qlinear_c4_bytes.restype = i64
         L.qlinear_c4_pack.argtypes = [i64, i64, vp, vp, vp]
@@ -85,7 +103,7 @@ def lib():
                      "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
                      "qlinear_gemv_grouped", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
                      "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped", "qlinear_rtn_noise",
-                     "qlinear_allocate"):
+                     "qlinear_allocate", "qlinear_lb_pack", "qlinear_lb_gemv"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -255,6 +273,80 @@ def allocate(weights, sensitivity, noise, allowed, budget_bits: float, grid_bits
                                   None if bits is None else bits.ctypes.data_as(ctypes.c_void_p),
                                   out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(lam)), "allocate")
     return out, lam.value
+
+
+# ---------------------------------------------------------------- LittleBit (binary factorized)
+def lb_bpw(d_out: int, d_in: int, rank: int) -> float:
+    return float(lib().qlinear_lb_bpw(d_out, d_in, rank))
+
+
+def lb_rank(d_out: int, d_in: int, bpw: float) -> int:
+    return int(lib().qlinear_lb_rank(d_out, d_in, float(bpw)))
+
+
+@dataclass
+class LittleBitWeight:
+    """A two-path LittleBit linear: packed signs and bf16 scales on the device."""
+    u_bits: torch.Tensor   # uint8
+    v_bits: torch.Tensor   # uint8
+    g: torch.Tensor        # bf16 [2, d_in]
+    l: torch.Tensor        # bf16 [2, rank]
+    h: torch.Tensor        # bf16 [2, d_out]
+    d_out: int
+    d_in: int
+    rank: int
+
+    @property
+    def nbytes(self) -> int:
+        """Stored bytes: sign buffers (padding included) and the three scale vectors."""
+        return self.u_bits.numel() + self.v_bits.numel() + 2 * (self.g.numel() + self.l.numel() + self.h.numel())
+
+    def desc(self) -> ql_littlebit:
+        return ql_littlebit(self.d_out, self.d_in, self.rank, 0, self.u_bits.data_ptr(), self.v_bits.data_ptr(),
+                            self.g.data_ptr(), self.l.data_ptr(), self.h.data_ptr())
+
+
+def lb_pack(u_signs: torch.Tensor, v_signs: torch.Tensor, g: torch.Tensor, l: torch.Tensor,
+            h: torch.Tensor) -> LittleBitWeight:
+    """u_signs int8 [2, d_out, r], v_signs int8 [2, d_in, r] (+-1); g, l, h bf16 [2, *]."""
+    _dev(u_signs, torch.int8, "u_signs")
+    _dev(v_signs, torch.int8, "v_signs")
+    for t, name in ((g, "g"), (l, "l"), (h, "h")):
+        _dev(t, torch.bfloat16, name)
+    _, d_out, r = u_signs.shape
+    d_in = v_signs.shape[1]
+    if tuple(v_signs.shape) != (2, d_in, r) or tuple(g.shape) != (2, d_in) or tuple(l.shape) != (2, r) or \
+            tuple(h.shape) != (2, d_out):
+        raise ValueError("inconsistent LittleBit shapes")
+    ub = int(lib().qlinear_lb_u_bytes(d_out, r))
+    vb = int(lib().qlinear_lb_v_bytes(d_in, r))
+    if ub <= 0 or vb <= 0:
+        raise ValueError(f"invalid LittleBit shape {d_out}x{d_in}, rank {r}")
+    u_bits = torch.empty(ub, dtype=torch.uint8, device=u_signs.device)
+    v_bits = torch.empty(vb, dtype=torch.uint8, device=u_signs.device)
+    _check(lib().qlinear_lb_pack(d_out, d_in, r, _ptr(u_signs), _ptr(v_signs), _ptr(u_bits), _ptr(v_bits),
+                                 _stream()), "lb_pack")
+    return LittleBitWeight(u_bits, v_bits, g, l, h, d_out, d_in, r)
+
+
+def lb_gemv(x: torch.Tensor, lw: LittleBitWeight, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [d_out] fp32 of the LittleBit linear at batch 1 (x [d_in] or [1, d_in] bf16)."""
+    _dev(x, torch.bfloat16, "x")
+    if x.numel() != lw.d_in:
+        raise ValueError(f"x has {x.numel()} elements, the linear takes {lw.d_in}")
+    if out is None:
+        out = torch.empty(lw.d_out, dtype=torch.float32, device=x.device)
+    else:
+        _dev(out, torch.float32, "out")
+        if out.numel() != lw.d_out:
+            raise ValueError("out must hold d_out values")
+    need = int(lib().qlinear_lb_workspace_bytes(lw.d_out, lw.d_in, lw.rank))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    d = lw.desc()
+    _check(lib().qlinear_lb_gemv(ctypes.byref(d), _ptr(x), _ptr(out), _ptr(workspace), need, _stream()), "lb_gemv")
+    return out
 
 
 # ---------------------------------------------------------------- 4-bit containers (baseline)

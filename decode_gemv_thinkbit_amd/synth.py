@@ -9,6 +9,8 @@ check receive exactly the arrays it returns.
   summary page serves are not available; these stand in for them with the
   same shapes.
 * Activations: x ~ N(0, 1), rounded to bf16 by torch.
+* LittleBit parameters (``littlebit_params``): random signs and log-normal
+  scales of the page's shapes.
 * Output gradients for the allocator's sensitivities: N(0, sigma^2) with a
   log-normal sigma per linear (``output_gradient``).
 * Mixed allocation (summary page onedev.kr/papers/1416, section "How it
@@ -112,6 +114,26 @@ def output_gradient(N: int, wl_index: int, layer: int, mat: int, device="cpu") -
     g = torch.Generator(device=device)
     g.manual_seed(seed_of(6, wl_index, layer, mat))
     return torch.randn(N, generator=g, device=device, dtype=torch.float32) * sigma
+
+
+def littlebit_params(d_out: int, d_in: int, r: int, seed: int, device="cpu"):
+    """Seeded parameters of a two-path LittleBit linear: signs +-1 with probability 1/2
+    (int8 [2, d_out, r] and [2, d_in, r]); bf16 scales g = exp(0.25 z) [2, d_in],
+    l = exp(0.5 z) / sqrt(r) [2, r], h = 0.02 exp(0.25 z) [2, d_out], z ~ N(0, 1).
+    (Trained LittleBit checkpoints are not available; kernel time does not depend on the
+    values.)"""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def signs(*shape):
+        return (torch.randint(0, 2, shape, generator=gen, device=device, dtype=torch.int8) * 2 - 1).to(torch.int8)
+
+    u = signs(2, d_out, r)
+    v = signs(2, d_in, r)
+    g = torch.exp(0.25 * torch.randn(2, d_in, generator=gen, device=device)).to(torch.bfloat16)
+    l = (torch.exp(0.5 * torch.randn(2, r, generator=gen, device=device)) / float(np.sqrt(r))).to(torch.bfloat16)
+    h = (0.02 * torch.exp(0.25 * torch.randn(2, d_out, generator=gen, device=device))).to(torch.bfloat16)
+    return u, v, g, l, h
 
 
 def weight_seed(wl_index: int, layer: int, mat: int) -> int:

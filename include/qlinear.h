@@ -223,6 +223,53 @@ ql_status qlinear_rtn_noise(int64_t N, int64_t K, const float *W, double *noise,
 ql_status qlinear_allocate(const ql_alloc_unit *units, int64_t count, double budget_bits, const double *grid_bits,
                            int8_t *grid_out, double *lambda_out);
 
+/* ---------------------------------------------------------------- LittleBit (binary factorized linear)
+ *
+ * LittleBit digest page (seosoyoung.eiaserinnys.me/digest/littlebit-ultra-low-bit-quantization),
+ * sections "LittleBit's structure" and "Rank sets the BPW": a linear W (d_out x d_in) is the sum
+ * of a primary and a residual path, each diag(h) U_sign diag(l) V_sign^T diag(g) with +-1
+ * matrices U_sign (d_out x r), V_sign (d_in x r) and 16-bit scales h (d_out), g (d_in), l (r);
+ * y = sum over paths of ((((x . g) V_sign) . l) U_sign^T) . h.  Bits per original weight:
+ * b = ((2r + 32)(d_out + d_in) + 32r) / (d_out d_in).
+ * Layout (this project's): a sign is one bit, 1 for -1; bit t of byte B of a row is element
+ * 8B + t; rows are interleaved in 64-row slabs as the packed layout (bytes 16c..16c+15 of slab
+ * row q at c*1024 + q*16).
+ *   v_bits: V_sign^T as latent rows of d_in bits: path 0's r rows, then path 1's, each path
+ *           padded to a multiple of 64 rows (qlinear_lb_v_bytes).
+ *   u_bits: d_out rows, each path 0's r bits then path 1's, each part padded to a multiple of
+ *           128 bits (qlinear_lb_u_bytes).  Padding bits and rows are 0.
+ *   scales: bf16 bits g [2][d_in], l [2][r], h [2][d_out] (path 0 first).
+ * Requirements: d_in % 128 == 0, d_out >= 1, rank >= 1. */
+typedef struct {
+  int32_t d_out, d_in, rank;  /* rank r of each path */
+  int32_t reserved;           /* 0 */
+  const void *u_bits;         /* (dev) */
+  const void *v_bits;         /* (dev) */
+  const uint16_t *g;          /* (dev) bf16 [2][d_in] */
+  const uint16_t *l;          /* (dev) bf16 [2][rank] */
+  const uint16_t *h;          /* (dev) bf16 [2][d_out] */
+} ql_littlebit;
+
+/* Bits per original weight of a two-path LittleBit linear of rank r (host, no GPU). */
+double qlinear_lb_bpw(int64_t d_out, int64_t d_in, int64_t rank);
+/* Largest rank whose bits per weight do not exceed bpw (0 if none). */
+int64_t qlinear_lb_rank(int64_t d_out, int64_t d_in, double bpw);
+/* Sizes of the two sign buffers (bytes); 0 if the shape is invalid. */
+int64_t qlinear_lb_u_bytes(int64_t d_out, int64_t rank);
+int64_t qlinear_lb_v_bytes(int64_t d_in, int64_t rank);
+
+/* Pack signs into the layout above.  u_signs (dev) int8 [2][d_out][rank], v_signs (dev) int8
+ * [2][d_in][rank], entries +-1 (anything negative counts as -1); u_bits, v_bits (dev). */
+ql_status qlinear_lb_pack(int64_t d_out, int64_t d_in, int64_t rank, const int8_t *u_signs,
+                          const int8_t *v_signs, void *u_bits, void *v_bits, hipStream_t stream);
+
+/* Batch-1 product y [d_out] fp32 = the two-path LittleBit linear applied to x [d_in] bf16.
+ * Products are exact (sign flips of bf16 values), sums fp32 in a fixed order: deterministic.
+ * w (host struct holding device pointers); workspace (dev) of qlinear_lb_workspace_bytes. */
+size_t qlinear_lb_workspace_bytes(int64_t d_out, int64_t d_in, int64_t rank);
+ql_status qlinear_lb_gemv(const ql_littlebit *w, const uint16_t *x, float *y, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- 4-bit container baseline
  *
  * The summary page (onedev.kr/papers/1416, section "Premises & limits") says the

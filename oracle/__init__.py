@@ -76,6 +76,17 @@ def lib():
         L.ora_c4_bytes.restype = i64
         L.ora_c4_pack.argtypes = [i64, i64, vp, vp]
         L.ora_c4_unpack.argtypes = [i64, i64, vp, vp]
+        L.ora_lb_bpw.argtypes = [i64, i64, i64]
+        L.ora_lb_bpw.restype = ctypes.c_double
+        L.ora_lb_rank.argtypes = [i64, i64, ctypes.c_double]
+        L.ora_lb_rank.restype = i64
+        L.ora_lb_u_bytes.argtypes = [i64, i64]
+        L.ora_lb_u_bytes.restype = i64
+        L.ora_lb_v_bytes.argtypes = [i64, i64]
+        L.ora_lb_v_bytes.restype = i64
+        L.ora_lb_pack.argtypes = [i64, i64, i64, vp, vp, vp, vp]
+        L.ora_lb_unpack.argtypes = [i64, i64, i64, vp, vp, vp, vp]
+        L.ora_lb_gemv.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.ora_rtn_noise.argtypes = [i64, i64, vp, vp]
         L.ora_block_sensitivity.argtypes = [i64, vp, i64, vp, vp]
         L.ora_allocate.argtypes = [i64, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
@@ -321,3 +332,50 @@ def allocate(n, S, E, allowed, budget: float, bits=None) -> tuple[np.ndarray, fl
     if rc != 0:
         raise ValueError("bad allocation input")
     return out, lam.value
+
+
+# ---------------------------------------------------------------- LittleBit
+def lb_bpw(d_out: int, d_in: int, r: int) -> float:
+    return float(lib().ora_lb_bpw(d_out, d_in, r))
+
+
+def lb_rank(d_out: int, d_in: int, bpw: float) -> int:
+    return int(lib().ora_lb_rank(d_out, d_in, float(bpw)))
+
+
+def lb_pack(u_signs: np.ndarray, v_signs: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """u_signs int8 [2][d_out][r], v_signs int8 [2][d_in][r] (+-1) -> (u_bits, v_bits)."""
+    u = np.ascontiguousarray(u_signs, dtype=np.int8)
+    v = np.ascontiguousarray(v_signs, dtype=np.int8)
+    _, d_out, r = u.shape
+    d_in = v.shape[1]
+    ub = np.empty(int(lib().ora_lb_u_bytes(d_out, r)), np.uint8)
+    vb = np.empty(int(lib().ora_lb_v_bytes(d_in, r)), np.uint8)
+    rc = lib().ora_lb_pack(d_out, d_in, r, _p(u), _p(v), _p(ub), _p(vb))
+    if rc == -3:
+        raise ValueError("sign other than +-1")
+    if rc != 0:
+        raise ValueError("bad shape")
+    return ub, vb
+
+
+def lb_unpack(u_bits: np.ndarray, v_bits: np.ndarray, d_out: int, d_in: int, r: int):
+    u = np.empty((2, d_out, r), np.int8)
+    v = np.empty((2, d_in, r), np.int8)
+    if lib().ora_lb_unpack(d_out, d_in, r, _p(np.ascontiguousarray(u_bits, np.uint8)),
+                           _p(np.ascontiguousarray(v_bits, np.uint8)), _p(u), _p(v)) != 0:
+        raise ValueError("bad shape")
+    return u, v
+
+
+def lb_gemv(u_signs, v_signs, g, l, h, x) -> np.ndarray:
+    """fp64 y [d_out] of the two-path LittleBit linear at batch 1 (bf16 bits for g, l, h, x)."""
+    u = np.ascontiguousarray(u_signs, dtype=np.int8)
+    v = np.ascontiguousarray(v_signs, dtype=np.int8)
+    _, d_out, r = u.shape
+    d_in = v.shape[1]
+    y = np.empty(d_out, np.float64)
+    arrs = [np.ascontiguousarray(a, dtype=np.uint16) for a in (g, l, h, x)]
+    if lib().ora_lb_gemv(d_out, d_in, r, _p(u), _p(v), *[_p(a) for a in arrs], _p(y)) != 0:
+        raise ValueError("bad shape")
+    return y

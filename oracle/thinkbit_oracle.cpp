@@ -23,6 +23,9 @@
 //     thirty-two 3-bit codes per 96-bit triple, 64-row slabs, 128-row grid
 //     blocks) is this project's own definition; the pages fix no bit order.
 //     It is written out once more, independently, in the HIP packer.
+//   * LittleBit (digest page seosoyoung.eiaserinnys.me/digest/littlebit-
+//     ultra-low-bit-quantization): the two-path binary factorized linear,
+//     its bits-per-weight formula and its forward pass.
 //   * The grid allocation of the same page, section "How it differs"
 //     (stage 1): rounding noise per grid, and a multiple-choice knapsack
 //     over grids under a bit budget solved by Lagrangian relaxation.
@@ -479,6 +482,120 @@ int ora_c4_unpack(int64_t N, int64_t K, const uint8_t* in, int8_t* codes) {
       const int nl = row[i] % 16, nh = row[i] / 16;
       codes[n * K + 2 * i] = (int8_t)(nl >= 8 ? nl - 16 : nl);
       codes[n * K + 2 * i + 1] = (int8_t)(nh >= 8 ? nh - 16 : nh);
+    }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------- LittleBit
+// LittleBit digest page (seosoyoung.eiaserinnys.me/digest/littlebit-ultra-
+// low-bit-quantization), sections "LittleBit's structure" and "Rank sets the
+// BPW".  A linear W (d_out x d_in) is the sum of two paths (primary and
+// residual) of the same form diag(h) U_sign diag(l) V_sign^T diag(g):
+// U_sign (d_out x r) and V_sign (d_in x r) hold +-1, h (d_out), g (d_in) and
+// l (r) are 16-bit scales (bf16 here).  The forward pass never forms W:
+// Z = ((X . g) V_sign) . l, Y = (Z U_sign^T) . h, summed over the paths.
+// Storage per path is two r-column binary matrices and three scale vectors,
+// so the bits per original weight are
+//   b = ((2r + 32)(d_out + d_in) + 32 r) / (d_out d_in)
+// and a target b fixes r (the largest r whose b does not exceed it).
+double ora_lb_bpw(int64_t d_out, int64_t d_in, int64_t r) {
+  return ((2.0 * r + 32.0) * (double)(d_out + d_in) + 32.0 * r) / ((double)d_out * (double)d_in);
+}
+
+int64_t ora_lb_rank(int64_t d_out, int64_t d_in, double bpw) {
+  int64_t r = 0;
+  while (ora_lb_bpw(d_out, d_in, r + 1) <= bpw) ++r;
+  return r;
+}
+
+// Bit layout (this project's; the page only says the signs are packed into
+// 32-bit words): a sign is one bit, 1 for -1.  Each binary matrix is stored
+// as rows of bits along the dimension the product sums over: V_sign^T as r
+// rows of d_in bits per path (the latent rows, path 0 then path 1, each path
+// padded to a multiple of 64 rows), U_sign as d_out rows holding path 0's r
+// bits then path 1's, each path's part padded to a multiple of 128 bits.  Bit
+// t of byte B of a row is element 8B + t.  Rows are interleaved in 64-row
+// slabs exactly as the packed layout (bytes 16c..16c+15 of slab row q at
+// c*1024 + q*16); padding bits and rows are 0.
+int64_t ora_lb_latent_rows(int64_t r) { return (r + 63) / 64 * 64; }          // rows per path in V^T
+int64_t ora_lb_u_row_bytes(int64_t r) { return 2 * ((r + 127) / 128) * 16; }  // both paths
+
+namespace {
+void put_bit(uint8_t* buf, int64_t row_bytes, int64_t row, int64_t bit) {
+  const int64_t B = bit / 8;
+  uint8_t* slab = buf + (row / kSlab) * kSlab * row_bytes;
+  slab[(B / kChunk) * kSlab * kChunk + (row % kSlab) * kChunk + B % kChunk] |= (uint8_t)(1u << (bit % 8));
+}
+int get_bit(const uint8_t* buf, int64_t row_bytes, int64_t row, int64_t bit) {
+  const int64_t B = bit / 8;
+  const uint8_t* slab = buf + (row / kSlab) * kSlab * row_bytes;
+  return slab[(B / kChunk) * kSlab * kChunk + (row % kSlab) * kChunk + B % kChunk] >> (bit % 8) & 1;
+}
+}  // namespace
+
+int64_t ora_lb_v_bytes(int64_t d_in, int64_t r) { return 2 * ora_lb_latent_rows(r) * (d_in / 8); }
+int64_t ora_lb_u_bytes(int64_t d_out, int64_t r) { return nslabs_of(d_out) * kSlab * ora_lb_u_row_bytes(r); }
+
+// u_signs int8 [2][d_out][r], v_signs int8 [2][d_in][r], entries +-1.
+// Returns 0, -1 for a bad shape, -3 for an entry other than +-1.
+int ora_lb_pack(int64_t d_out, int64_t d_in, int64_t r, const int8_t* u_signs, const int8_t* v_signs,
+                uint8_t* u_bits, uint8_t* v_bits) {
+  if (d_out <= 0 || d_in <= 0 || d_in % kGroup || r <= 0) return -1;
+  std::memset(u_bits, 0, ora_lb_u_bytes(d_out, r));
+  std::memset(v_bits, 0, ora_lb_v_bytes(d_in, r));
+  const int64_t RP = ora_lb_latent_rows(r), urb = ora_lb_u_row_bytes(r), half = urb / 2;
+  for (int p = 0; p < 2; ++p) {
+    for (int64_t n = 0; n < d_out; ++n)
+      for (int64_t j = 0; j < r; ++j) {
+        const int8_t s = u_signs[(p * d_out + n) * r + j];
+        if (s != 1 && s != -1) return -3;
+        if (s < 0) put_bit(u_bits, urb, n, 8 * half * p + j);
+      }
+    for (int64_t i = 0; i < d_in; ++i)
+      for (int64_t j = 0; j < r; ++j) {
+        const int8_t s = v_signs[(p * d_in + i) * r + j];
+        if (s != 1 && s != -1) return -3;
+        if (s < 0) put_bit(v_bits, d_in / 8, p * RP + j, i);
+      }
+  }
+  return 0;
+}
+
+// Inverse of ora_lb_pack (signs +-1).
+int ora_lb_unpack(int64_t d_out, int64_t d_in, int64_t r, const uint8_t* u_bits, const uint8_t* v_bits,
+                  int8_t* u_signs, int8_t* v_signs) {
+  if (d_out <= 0 || d_in <= 0 || d_in % kGroup || r <= 0) return -1;
+  const int64_t RP = ora_lb_latent_rows(r), urb = ora_lb_u_row_bytes(r), half = urb / 2;
+  for (int p = 0; p < 2; ++p) {
+    for (int64_t n = 0; n < d_out; ++n)
+      for (int64_t j = 0; j < r; ++j)
+        u_signs[(p * d_out + n) * r + j] = get_bit(u_bits, urb, n, 8 * half * p + j) ? -1 : 1;
+    for (int64_t i = 0; i < d_in; ++i)
+      for (int64_t j = 0; j < r; ++j) v_signs[(p * d_in + i) * r + j] = get_bit(v_bits, d_in / 8, p * RP + j, i) ? -1 : 1;
+  }
+  return 0;
+}
+
+// The forward pass of both paths in fp64, in the page's order: t = x . g,
+// z = (V_sign^T t) . l, y = sum over paths of (U_sign z) . h.  Scales and x
+// are bf16 bits (g, h [2][d]; l [2][r]); y [d_out].
+int ora_lb_gemv(int64_t d_out, int64_t d_in, int64_t r, const int8_t* u_signs, const int8_t* v_signs,
+                const uint16_t* g, const uint16_t* l, const uint16_t* h, const uint16_t* x, double* y) {
+  if (d_out <= 0 || d_in <= 0 || r <= 0) return -1;
+  for (int64_t n = 0; n < d_out; ++n) y[n] = 0.0;
+  std::vector<double> t(d_in), z(r);
+  for (int p = 0; p < 2; ++p) {
+    for (int64_t i = 0; i < d_in; ++i) t[i] = (double)bf16_to_f32(x[i]) * (double)bf16_to_f32(g[p * d_in + i]);
+    for (int64_t j = 0; j < r; ++j) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < d_in; ++i) acc += (double)v_signs[(p * d_in + i) * r + j] * t[i];
+      z[j] = acc * (double)bf16_to_f32(l[p * r + j]);
+    }
+    for (int64_t n = 0; n < d_out; ++n) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < r; ++j) acc += (double)u_signs[(p * d_out + n) * r + j] * z[j];
+      y[n] += acc * (double)bf16_to_f32(h[p * d_out + n]);
     }
   }
   return 0;
