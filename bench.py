@@ -14,7 +14,9 @@ Qwen3-8B-shaped layer (mixed grids, M = 64 / 256 / 512): microseconds per layer
 and MFMA utilisation against the dense bf16 peak; "container_ab" times the
 Qwen3-8B pass and the Qwen3-14B stack (M = 1) once more with the same codes stored
 in 4-bit containers, the format published checkpoints use; "allocator" allocates the
-8B pass's grids by the Lagrangian knapsack and runs the pass with them.
+8B pass's grids by the Lagrangian knapsack and runs the pass with them; "littlebit"
+times the two-path binary factorized GEMV at the LittleBit page's shapes against a
+dense bf16 matmul.
 """
 from __future__ import annotations
 
@@ -188,6 +190,66 @@ def allocator_leg(dev, warmup, steps, budget_bits=2.0):
             "bits_per_weight": round(bits, 5),
             "pass_us": round(ms * 1e3, 2), "pass_stored_bytes": stored,
             "pass_gbs": round(stored / (ms * 1e-3) / 1e9, 1)}
+
+
+def littlebit_leg(dev, reps=100, shapes=((28672, 8192), (11008, 4096), (8192, 8192)),
+                  bpws=(0.1, 0.3, 0.55, 1.0)):
+    """Batch-1 LittleBit GEMV at the digest page's kernel shapes (Llama2-70B MLP and attention,
+    Llama2-7B MLP) against a dense bf16 torch.matmul of the same shape.  Both rotate through
+    enough copies of the weights to exceed 600 MB, so every call streams its weight from HBM,
+    and both run as a replayed HIP graph of `reps` calls."""
+    import torch
+    from decode_gemv_thinkbit_amd import qlinear as ql
+    from decode_gemv_thinkbit_amd import synth
+
+    st = torch.cuda.current_stream()
+
+    def timed(fn, copies):
+        # captured in a HIP graph and replayed, so host launch overhead does not
+        # stand between the kernels
+        for i in range(min(3, copies)):
+            fn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                fn(i % copies)
+        graph.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(st)
+        graph.replay()
+        e.record(st)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / reps
+
+    out = []
+    for do, di in shapes:
+        x = synth.activations(1, di, 17, device=dev).view(-1)
+        nd = max(2, -(-600_000_000 // (do * di * 2)))
+        Ws = [torch.randn(do, di, device=dev).to(torch.bfloat16) for _ in range(nd)]
+        x2 = x.view(di, 1)
+        dense_us = timed(lambda i: torch.matmul(Ws[i], x2), nd)
+        del Ws
+        torch.cuda.empty_cache()
+        for b in bpws:
+            r = ql.lb_rank(do, di, b)
+            lw0 = ql.lb_pack(*synth.littlebit_params(do, di, r, 23, device=dev))
+            copies = max(2, min(256, -(-600_000_000 // lw0.nbytes)))
+            lws = [lw0] + [ql.LittleBitWeight(lw0.u_bits.clone(), lw0.v_bits.clone(), lw0.g.clone(), lw0.l.clone(),
+                                              lw0.h.clone(), do, di, r) for _ in range(copies - 1)]
+            y = torch.empty(do, dtype=torch.float32, device=dev)
+            ws = torch.empty(int(ql.lib().qlinear_lb_workspace_bytes(do, di, r)), dtype=torch.uint8, device=dev)
+            us = timed(lambda i: ql.lb_gemv(x, lws[i], out=y, workspace=ws), copies)
+            out.append({"d_out": do, "d_in": di, "bpw": b, "rank": r, "us": round(us, 2),
+                        "stored_bytes": lw0.nbytes, "gbs": round(lw0.nbytes / (us * 1e-6) / 1e9, 1),
+                        "dense_bf16_us": round(dense_us, 2), "speedup_vs_dense": round(dense_us / us, 2)})
+            log(f"littlebit {do}x{di} bpw {b} (r={r}): {us:.1f} us, {lw0.nbytes / 1e6:.2f} MB; "
+                f"dense bf16 {dense_us:.1f} us -> {dense_us / us:.2f}x")
+            del lws, lw0
+            torch.cuda.empty_cache()
+    return {"batch": 1, "dense_baseline": "torch.matmul bf16 (weights rotated past the cache)",
+            "timing": f"HIP graph of {reps} calls, replayed once", "points": out}
 
 
 def kernel_source_hash() -> str:
@@ -365,6 +427,7 @@ def main():
     ap.add_argument("--no-gemm", action="store_true", help="skip the batched (MFMA) leg")
     ap.add_argument("--no-ab", action="store_true", help="skip the 4-bit container A/B leg")
     ap.add_argument("--no-alloc", action="store_true", help="skip the grid allocation leg")
+    ap.add_argument("--no-littlebit", action="store_true", help="skip the LittleBit leg")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -444,6 +507,8 @@ def main():
         result["allocator"] = allocator_leg(dev, args.warmup, args.steps)
     if not args.no_gemm:
         result["gemm"] = gemm_leg(dev)
+    if not args.no_littlebit:
+        result["littlebit"] = littlebit_leg(dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample...")
         result["cpu_baseline"] = cpu_baseline(wl, wl_index, M)

@@ -18,9 +18,10 @@
 //   lb_reduce_kernel  z = l . (sum of the slices, in slice order), split into
 //                     three bf16 terms hi + mid + lo that reproduce z to fp32
 //                     accuracy;
-//   lb_output_kernel  one wave per 64 output rows: a table turns a sign byte
-//                     into four (+-1, +-1) bf16 pairs, dotted with the three z
-//                     terms (exact), fp32 sums per path, times h.
+//   lb_output_kernel  one workgroup per 64 output rows, its waves splitting the
+//                     latent dimension: a table turns a sign byte into four
+//                     (+-1, +-1) bf16 pairs, dotted with the three z terms
+//                     (exact), fp32 sums per path, times h.
 // Every product is exact; only fp32 summation rounds, in a fixed order, so the
 // result is deterministic.
 #include "ql_internal.hpp"
@@ -72,31 +73,32 @@ __global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, 
   build_sign_masks(lut);
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int nslabs = 2 * RP / kSlab;
-  const int task = blockIdx.x * kLbWaves + wave;
-  if (task >= nslabs * nslices) return;
-  const int slab = task / nslices, q = task % nslices;
-  const int path = slab / (RP / kSlab);
+  const int ntasks = 2 * RP / kSlab * nslices;
   const int rb = d_in / 8, nchunks = rb / kChunkBytes;
-  const int c0 = q * slice_chunks, c1 = (c0 + slice_chunks < nchunks) ? c0 + slice_chunks : nchunks;
-  const ChunkSrc src(v_bits + (int64_t)slab * kSlab * rb, nchunks, lane);
   const cu32p xp = (cu32p)x;
-  const cu32p gp = (cu32p)(g + (int64_t)path * d_in);
   const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
-  float acc = 0.0f;
-  for (int c = c0; c < c1; ++c) {
-    const uint4 d = src.load(c);
+  // persistent: the table is built once per workgroup, tasks stride over the waves
+  for (int task = blockIdx.x * kLbWaves + wave; task < ntasks; task += gridDim.x * kLbWaves) {
+    const int slab = task / nslices, q = task % nslices;
+    const int path = slab / (RP / kSlab);
+    const int c0 = q * slice_chunks, c1 = (c0 + slice_chunks < nchunks) ? c0 + slice_chunks : nchunks;
+    const ChunkSrc src(v_bits + (int64_t)slab * kSlab * rb, nchunks, lane);
+    const cu32p gp = (cu32p)(g + (int64_t)path * d_in);
+    float acc = 0.0f;
+    for (int c = c0; c < c1; ++c) {
+      const uint4 d = src.load(c);
+#pragma unroll 8  // (full unrolling holds 128 x and g dwords in SGPRs and spills)
+      for (int B = 0; B < 16; ++B) {
+        const u32x4_t e = lds_b128(lut + lut_addr(d, B, lane_off));
 #pragma unroll
-    for (int B = 0; B < 16; ++B) {
-      const u32x4_t e = lds_b128(lut + lut_addr(d, B, lane_off));
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int P = 64 * c + 4 * B + k;  // input pair (2P, 2P+1)
-        acc = dot2(gp[P] ^ e[k], xp[P], acc);
+        for (int k = 0; k < 4; ++k) {
+          const int P = 64 * c + 4 * B + k;  // input pair (2P, 2P+1)
+          acc = dot2(gp[P] ^ e[k], xp[P], acc);
+        }
       }
     }
+    partial[(int64_t)q * 2 * RP + slab * kSlab + lane] = acc;
   }
-  partial[(int64_t)q * 2 * RP + slab * kSlab + lane] = acc;
 }
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return f32_to_bf16_bits(f); }
@@ -116,6 +118,7 @@ __global__ void __launch_bounds__(256) lb_reduce_kernel(int32_t r, int32_t RP, i
     float z = 0.0f;
     if (j < r) {
       float s = 0.0f;
+#pragma unroll 16  // loads issued ahead of the in-order adds
       for (int q = 0; q < nslices; ++q) s += partial[(int64_t)q * 2 * RP + path * RP + j];
       z = s * bf16_bits_to_f32(l[path * r + j]);
     }
@@ -132,42 +135,63 @@ __global__ void __launch_bounds__(256) lb_reduce_kernel(int32_t r, int32_t RP, i
   for (int k = 0; k < 3; ++k) zs[(int64_t)t * 3 + k] = term[k];
 }
 
-// y[n] = h0[n] * sum_j s0(n, j) z0_j + h1[n] * sum_j s1(n, j) z1_j
+// y[n] = h0[n] * sum_j s0(n, j) z0_j + h1[n] * sum_j s1(n, j) z1_j.  A
+// workgroup owns one 64-row slab; its four waves split the row's latent chunks
+// (path 0's, then path 1's) into contiguous quarters, so every wave's z
+// operands stay wave-uniform (scalar loads), and the quarters' per-path sums
+// are added through LDS in wave order.
 __global__ void __launch_bounds__(kLbWaves * 64) lb_output_kernel(int32_t d_out, int32_t urb, int32_t ZP,
                                                                   const uint8_t* __restrict__ u_bits,
                                                                   const uint32_t* __restrict__ zs,
                                                                   const uint16_t* __restrict__ h,
                                                                   float* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLbLutBytes];
+  __shared__ float part[kLbWaves][2][kSlab];
   build_pm_ones(lut);
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int slab = blockIdx.x * kLbWaves + wave;
-  if (slab >= (d_out + kSlab - 1) / kSlab) return;
   const int half_chunks = urb / 2 / kChunkBytes;  // chunks of one path's part of a row
-  const ChunkSrc src(u_bits + (int64_t)slab * kSlab * urb, 2 * half_chunks, lane);
+  const int nch = 2 * half_chunks;
+  const int c0 = nch * wave / kLbWaves, c1 = nch * (wave + 1) / kLbWaves;
   const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
+  const int nslabs = (d_out + kSlab - 1) / kSlab;
+  // persistent: the table is built once per workgroup, slabs stride over the workgroups
+  for (int slab = blockIdx.x; slab < nslabs; slab += gridDim.x) {
+  const ChunkSrc src(u_bits + (int64_t)slab * kSlab * urb, nch, lane);
   float acc[2] = {0.0f, 0.0f};
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int cc = c0; cc < c1; ++cc) {
+    const int p = cc >= half_chunks, c = cc - p * half_chunks;
     const cu32p zp = (cu32p)(zs + (int64_t)p * ZP * 3);
-    for (int c = 0; c < half_chunks; ++c) {
-      const uint4 d = src.load(p * half_chunks + c);
+    const uint4 d = src.load(cc);
+    float a = 0.0f;
 #pragma unroll 4  // (full unrolling keeps 192 z dwords of a chunk in SGPRs and spills)
-      for (int B = 0; B < 16; ++B) {
-        const u32x4_t e = lds_b128(lut + lut_addr(d, B, lane_off));
+    for (int B = 0; B < 16; ++B) {
+      const u32x4_t e = lds_b128(lut + lut_addr(d, B, lane_off));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int P = 64 * c + 4 * B + k;  // latent pair (2P, 2P+1)
-          acc[p] = dot2(e[k], zp[3 * P], acc[p]);
-          acc[p] = dot2(e[k], zp[3 * P + 1], acc[p]);
-          acc[p] = dot2(e[k], zp[3 * P + 2], acc[p]);
-        }
+      for (int k = 0; k < 4; ++k) {
+        const int P = 64 * c + 4 * B + k;  // latent pair (2P, 2P+1)
+        a = dot2(e[k], zp[3 * P], a);
+        a = dot2(e[k], zp[3 * P + 1], a);
+        a = dot2(e[k], zp[3 * P + 2], a);
       }
     }
+    if (p) acc[1] += a; else acc[0] += a;
   }
-  const int64_t n = (int64_t)slab * kSlab + lane;
-  if (n < d_out) y[n] = fmaf(bf16_bits_to_f32(h[n]), acc[0], bf16_bits_to_f32(h[d_out + n]) * acc[1]);
+  part[wave][0][lane] = acc[0];
+  part[wave][1][lane] = acc[1];
+  __syncthreads();
+  if (wave == 0) {
+    float s0 = part[0][0][lane], s1 = part[0][1][lane];
+#pragma unroll
+    for (int w = 1; w < kLbWaves; ++w) {
+      s0 += part[w][0][lane];
+      s1 += part[w][1][lane];
+    }
+    const int64_t n = (int64_t)slab * kSlab + lane;
+    if (n < d_out) y[n] = fmaf(bf16_bits_to_f32(h[n]), s0, bf16_bits_to_f32(h[d_out + n]) * s1);
+  }
+  __syncthreads();  // part is rewritten by the next slab
+  }
 }
 
 // ---------------------------------------------------------------- packing
@@ -248,13 +272,14 @@ hipError_t launch_lb_gemv(const ql_littlebit& w, const uint16_t* x, float* y, vo
   float* partial = static_cast<float*>(ws);
   uint32_t* zs = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) +
                                              ((size_t)nslices * 2 * RP * 4 + 255) / 256 * 256);
-  const int64_t tasks = 2 * RP / 64 * nslices;
-  hipLaunchKernelGGL(lb_latent_kernel, dim3((unsigned)((tasks + kLbWaves - 1) / kLbWaves)), dim3(kLbWaves * 64), 0,
+  const int64_t tasks = 2 * RP / 64 * nslices, slots = 2 * (int64_t)device_cu_count();
+  const int64_t wg_lat = (tasks + kLbWaves - 1) / kLbWaves;
+  hipLaunchKernelGGL(lb_latent_kernel, dim3((unsigned)(wg_lat < slots ? wg_lat : slots)), dim3(kLbWaves * 64), 0,
                      stream, w.d_in, (int)RP, sc, nslices, static_cast<const uint8_t*>(w.v_bits), w.g, x, partial);
   hipLaunchKernelGGL(lb_reduce_kernel, dim3((unsigned)((2 * ZP + 255) / 256)), dim3(256), 0, stream, (int)r, (int)RP,
                      (int)ZP, nslices, partial, w.l, zs);
   const int64_t slabs = (w.d_out + 63) / 64;
-  hipLaunchKernelGGL(lb_output_kernel, dim3((unsigned)((slabs + kLbWaves - 1) / kLbWaves)), dim3(kLbWaves * 64), 0,
+  hipLaunchKernelGGL(lb_output_kernel, dim3((unsigned)(slabs < slots ? slabs : slots)), dim3(kLbWaves * 64), 0,
                      stream, w.d_out, (int)lb_u_row_bytes(r), (int)ZP, static_cast<const uint8_t*>(w.u_bits), zs, w.h,
                      y);
   return hipGetLastError();
