@@ -89,6 +89,18 @@ __device__ __forceinline__ u32x4g_t row_chunk(const uint8_t* slab, int r, int64_
   return v;
 }
 
+// byte offset b (4-aligned) of group bytes of a row -> the dword, zero for a missing slab
+__device__ __forceinline__ uint32_t row_dword(const uint8_t* slab, int r, int64_t byte) {
+  uint32_t v = 0u;
+  if (slab) v = *(const __attribute__((address_space(1))) uint32_t*)(slab + (byte >> 4) * kSlabChunkBytes + r * kChunkBytes + (byte & 15));
+  return v;
+}
+__device__ __forceinline__ u32x2g_t row_dword2(const uint8_t* slab, int r, int64_t byte) {
+  u32x2g_t v = {0u, 0u};
+  if (slab) v = *(const __attribute__((address_space(1))) u32x2g_t*)(slab + (byte >> 4) * kSlabChunkBytes + r * kChunkBytes + (byte & 15));
+  return v;
+}
+
 __device__ __forceinline__ uint32_t dword_of(const u32x4g_t& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
@@ -126,27 +138,25 @@ __device__ __forceinline__ void decode_t32(const u32x4g_t (&ch)[2], const uint8_
   put32(dst, o);
 }
 
-// 2-bit: codes [128g + 32q, +32) of one row = bytes 8(q&1).. of chunk 2g + q/2 (ch[0]).
-template <int Q>
+// 2-bit: codes [128g + 32q, +32) of one row = group bytes 8q..8q+7, staged as
+// ch[0].x, ch[0].y.
 __device__ __forceinline__ void decode_i2_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+  const uint32_t wd[2] = {ch[0].x, ch[0].y};
   uint32_t o[16];
   gfor<8>([&](auto bi) __attribute__((always_inline)) {
-    constexpr int j = 8 * (Q & 1) + decltype(bi)::value;  // byte within the chunk
-    const uint32_t b = (dword_of(ch[0], j >> 2) >> (8 * (j & 3))) & 0xFFu;
-    const u32x2g_t q = *(lq2p)(lut + kLutI2 + b * 8);
-    o[2 * decltype(bi)::value] = q.x;
-    o[2 * decltype(bi)::value + 1] = q.y;
+    constexpr int j = decltype(bi)::value;  // byte of the quarter
+    const uint32_t b = (wd[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    const u32x2g_t e = *(lq2p)(lut + kLutI2 + b * 8);
+    o[2 * j] = e.x;
+    o[2 * j + 1] = e.y;
   });
   put32(dst, o);
 }
 
-// 3-bit: codes [128g + 32q, +32) of one row = the 96-bit triple at group bytes 12q..12q+11,
-// inside chunks 3g + (12q)/16 (ch[0]) and the next one (ch[1]).
-template <int Q>
+// 3-bit: codes [128g + 32q, +32) of one row = the 96-bit triple at group bytes
+// 12q..12q+11, staged as ch[0].x, ch[0].y, ch[0].z (low word first).
 __device__ __forceinline__ void decode_i3_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
-  constexpr int B0 = 12 * Q - 16 * ((12 * Q) / 16);  // first byte of the triple within ch[0]
-  const uint32_t cw[8] = {ch[0].x, ch[0].y, ch[0].z, ch[0].w, ch[1].x, ch[1].y, ch[1].z, ch[1].w};
-  const uint32_t w0 = cw[B0 / 4], w1 = cw[B0 / 4 + 1], w2 = cw[B0 / 4 + 2];
+  const uint32_t w0 = ch[0].x, w1 = ch[0].y, w2 = ch[0].z;
   uint32_t o[16];
   gfor<16>([&](auto pi) __attribute__((always_inline)) {
     constexpr int P = decltype(pi)::value;
@@ -191,9 +201,9 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
   constexpr int RB = 8 / WR;         // 16-row blocks per wave (128 / WR rows)
   constexpr int MB = 2;              // 16-token blocks per wave
   constexpr int MT = 16 * MB * WM;   // tokens per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t wt[kTileN * kPad];
-  __shared__ __attribute__((aligned(16))) uint16_t xt[MT * kPad];
-  __shared__ __attribute__((aligned(16))) float sct[kTileN];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][kTileN * kPad];
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][MT * kPad];
+  __shared__ __attribute__((aligned(16))) float sct[2][kTileN];
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
   gemm_build_luts(lut);
 
@@ -213,7 +223,7 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
   const int dr = tid & 127, dq = __builtin_amdgcn_readfirstlane(tid >> 7);
   const uint8_t* dslab = dr < kSlab ? slab0 : slab1;
   const int dslab_r = dr & (kSlab - 1);
-  uint16_t* drow = wt + dr * kPad + 32 * dq;
+  const int drow_off = dr * kPad + 32 * dq;
   // x mapping: token xt_t, quarter xt_q
   const int xt_t = tid >> 2, xt_q = tid & 3;
   const bool x_ok = xt_t < MT && m0 + xt_t < M;
@@ -234,26 +244,30 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
       st.ch[0] = row_chunk(dslab, dslab_r, 8 * p + c0);
       st.ch[1] = row_chunk(dslab, dslab_r, 8 * p + c1);
     } else if (gr == QL_GRID_I2) {
-      // every branch writes both slots: stores to one slot or the other would be
-      // merged into one store with a computed address, which keeps st in memory
-      st.ch[0] = row_chunk(dslab, dslab_r, 2 * (int64_t)g + (dq >> 1));
+      // only the quarter's 8 bytes; every branch writes both slots: stores to one
+      // slot or the other would be merged into one store with a computed address,
+      // which keeps st in memory
+      const u32x2g_t v = row_dword2(dslab, dslab_r, 32 * (int64_t)g + 8 * dq);
+      st.ch[0] = u32x4g_t{v.x, v.y, 0u, 0u};
       st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
     } else {
-      const int c0 = (12 * dq) / 16;
-      st.ch[0] = row_chunk(dslab, dslab_r, 3 * (int64_t)g + c0);
-      st.ch[1] = row_chunk(dslab, dslab_r, 3 * (int64_t)g + (c0 < 2 ? c0 + 1 : c0));
+      // only the quarter's 12 bytes, as three aligned dwords (none straddles a chunk)
+      const int64_t b0 = 48 * (int64_t)g + 12 * dq;
+      st.ch[0] = u32x4g_t{row_dword(dslab, dslab_r, b0), row_dword(dslab, dslab_r, b0 + 4),
+                          row_dword(dslab, dslab_r, b0 + 8), 0u};
+      st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
     }
     st.sc = 0;
     if (tid < kTileN && sc_n < a.N) st.sc = a.pscales[pscale_index(sc_n, g, G8)];
   };
-  // x tile and scales of the staged group into LDS
-  auto put_x = [&]() __attribute__((always_inline)) {
+  // x tile and scales of the staged group into LDS buffer b
+  auto put_x = [&](int b) __attribute__((always_inline)) {
     if (xt_t < MT) {
-      uint16_t* dst = xt + xt_t * kPad + 32 * xt_q;
+      uint16_t* dst = xt[b] + xt_t * kPad + 32 * xt_q;
 #pragma unroll
       for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4g_t*>(dst + 8 * q) = st.xv[q];
     }
-    if (tid < kTileN) sct[tid] = bf16_bits_to_f32(st.sc);
+    if (tid < kTileN) sct[b][tid] = bf16_bits_to_f32(st.sc);
   };
 
   // MFMA mapping: wave (wr, wm) computes rows (128/WR)wr.. x tokens 32wm..
@@ -264,10 +278,10 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4_t{0, 0, 0, 0};
 
-  // after the staged group is in LDS: prefetch the next one, then multiply this one
-  auto mma = [&](int g) __attribute__((always_inline)) {
-    lds_barrier();
-    if (g + 1 < g_hi) load(g + 1);
+  // the MFMAs and scale epilogue of the group in LDS buffer b
+  auto mma = [&](int b) __attribute__((always_inline)) {
+    const uint16_t* wtb = wt[b];
+    const uint16_t* xtb = xt[b];
     f32x4_t pr[RB][MB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -279,10 +293,10 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
       bf16x8_t av[RB], bv[MB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        av[rb] = *reinterpret_cast<const bf16x8_t*>(wt + ((128 / WR) * wr + 16 * rb + (lane & 15)) * kPad + kk);
+        av[rb] = *reinterpret_cast<const bf16x8_t*>(wtb + ((128 / WR) * wr + 16 * rb + (lane & 15)) * kPad + kk);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        bv[mb] = *reinterpret_cast<const bf16x8_t*>(xt + (32 * wm + 16 * mb + (lane & 15)) * kPad + kk);
+        bv[mb] = *reinterpret_cast<const bf16x8_t*>(xtb + (32 * wm + 16 * mb + (lane & 15)) * kPad + kk);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -292,56 +306,54 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
     // D lane l: rows 4*(l/16)+i of the 16-row block, token l%16 of the 16-token block
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(sct + (128 / WR) * wr + 16 * rb + 4 * (lane >> 4));
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(sct[b] + (128 / WR) * wr + 16 * rb + 4 * (lane >> 4));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[rb][mb][i] = fmaf(s4[i], pr[rb][mb][i], acc[rb][mb][i]);
     }
-    lds_barrier();
   };
 
   // decode of the staged group (dq is wave-uniform: one branch per wave)
-  auto decode_t = [&](auto ii) __attribute__((always_inline)) {
+  auto decode_t = [&](auto ii, int b) __attribute__((always_inline)) {
     constexpr int i = decltype(ii)::value;
+    uint16_t* drow = wt[b] + drow_off;
     if (dq == 0) decode_t32<128 * i>(st.ch, lut, drow);
     else if (dq == 1) decode_t32<128 * i + 32>(st.ch, lut, drow);
     else if (dq == 2) decode_t32<128 * i + 64>(st.ch, lut, drow);
     else decode_t32<128 * i + 96>(st.ch, lut, drow);
   };
+  auto decode_i2 = [&](int b) __attribute__((always_inline)) { decode_i2_32(st.ch, lut, wt[b] + drow_off); };
+  auto decode_i3 = [&](int b) __attribute__((always_inline)) { decode_i3_32(st.ch, lut, wt[b] + drow_off); };
 
+  // Two LDS buffers, one barrier per step: step d decodes group d (its codes
+  // were loaded into registers one step earlier) into buffer (d - g_lo) & 1,
+  // issues the loads of group d + 1, and runs the MFMAs of group d - 1 from the
+  // other buffer.  Each grid keeps a single decode call site.
   __syncthreads();  // tables ready
   if (g_lo < g_hi) load(g_lo);
+  auto step = [&](int d, auto&& decode) __attribute__((always_inline)) {
+    const int b = (d - g_lo) & 1;
+    if (d < g_hi) {
+      decode(b);
+      put_x(b);
+      if (d + 1 < g_hi) load(d + 1);
+    }
+    if (d > g_lo) mma(b ^ 1);
+    lds_barrier();
+  };
   if (gr == QL_GRID_T) {
     // periods of 640 inputs: the byte positions of every group are compile-time
-    for (int64_t p = g_lo / 5; 5 * p < g_hi; ++p) {
+    for (int64_t p = g_lo / 5; 5 * p <= g_hi; ++p) {
       gfor<5>([&](auto ii) __attribute__((always_inline)) {
-        const int g = (int)(5 * p) + decltype(ii)::value;
-        if (g >= g_lo && g < g_hi) {
-          decode_t(ii);
-          put_x();
-          mma(g);
-        }
+        const int d = (int)(5 * p) + decltype(ii)::value;
+        if (d >= g_lo && d <= g_hi) step(d, [&](int b) __attribute__((always_inline)) { decode_t(ii, b); });
       });
     }
   } else if (gr == QL_GRID_I2) {
-    for (int g = g_lo; g < g_hi; ++g) {
-      if (dq == 0) decode_i2_32<0>(st.ch, lut, drow);
-      else if (dq == 1) decode_i2_32<1>(st.ch, lut, drow);
-      else if (dq == 2) decode_i2_32<2>(st.ch, lut, drow);
-      else decode_i2_32<3>(st.ch, lut, drow);
-      put_x();
-      mma(g);
-    }
+    for (int d = g_lo; d <= g_hi; ++d) step(d, decode_i2);
   } else {
-    for (int g = g_lo; g < g_hi; ++g) {
-      if (dq == 0) decode_i3_32<0>(st.ch, lut, drow);
-      else if (dq == 1) decode_i3_32<1>(st.ch, lut, drow);
-      else if (dq == 2) decode_i3_32<2>(st.ch, lut, drow);
-      else decode_i3_32<3>(st.ch, lut, drow);
-      put_x();
-      mma(g);
-    }
+    for (int d = g_lo; d <= g_hi; ++d) step(d, decode_i3);
   }
 
   // store: y directly, or this split's partial sums
