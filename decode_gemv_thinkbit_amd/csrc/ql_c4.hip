@@ -153,8 +153,8 @@ __global__ void __launch_bounds__(kC4Waves * 64, 4) c4_gemv_kernel(ql_gemv_desc 
 }
 
 // Persistent launch over many containers, scheduled exactly as the native
-// grouped GEMV: first task by wave index, then tickets from sched[0] drawn at
-// the end of each task; the last wave to check out on sched[1] zeroes both.
+// grouped GEMV: first task by wave index, then draws from the task queues at
+// the end of each task.
 __global__ void __launch_bounds__(kC4Waves * 64, 4) c4_gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
                                                                           int count, int64_t total,
                                                                           uint32_t* __restrict__ sched) {
@@ -163,21 +163,14 @@ __global__ void __launch_bounds__(kC4Waves * 64, 4) c4_gemv_grouped_kernel(const
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const uint32_t nwaves = gridDim.x * kC4Waves;
+  TaskQueues tq(sched, total, (int64_t)gridDim.x * kC4Waves);
   int64_t t = (int64_t)blockIdx.x * kC4Waves + wave;
-  while (t < total) {
+  if (t >= total) t = tq.next(lane);
+  while (t >= 0) {
     c4_task(descs, count, t, lut, lane);
-    uint32_t ticket = 0;
-    if (lane == 0) ticket = __hip_atomic_fetch_add(sched, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    t = (int64_t)nwaves + __builtin_amdgcn_readfirstlane(ticket);
+    t = tq.next(lane);
   }
-  if (lane == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(sched + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == nwaves - 1) {
-      __hip_atomic_store(sched, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sched + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  tq.checkout(lane);
 }
 
 int c4_grid_size(int64_t tasks) {

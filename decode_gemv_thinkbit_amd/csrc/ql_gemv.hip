@@ -571,13 +571,11 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_kernel(ql_g
 }
 
 // Many independent matrices in one persistent launch.  Slab costs differ
-// (row length, grid), so after its first task a wave takes the next one from
-// an atomic ticket counter (sched[0]) when it finishes a task: greedy list
-// scheduling over tasks that the host numbered longest-first.  (A ticket drawn
-// when a task starts would hide the fetch latency but fixes the assignment of
-// the next round at launch time, which balances far worse.)  Every wave then
-// checks out on sched[1]; the last one resets both words, leaving the state
-// zero for the next launch.
+// (row length, grid), so after its first task a wave draws the next one from
+// the task queues when it finishes a task: greedy list scheduling over tasks
+// that the host numbered longest-first.  (A task drawn when the previous one
+// starts would hide the draw latency but fixes the next round's assignment at
+// launch time, which balances far worse.)
 template <int M>
 __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
                                                                       int count, int64_t total, int Mact,
@@ -587,21 +585,14 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_ker
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const uint32_t nwaves = gridDim.x * kWaves;
+  TaskQueues tq(sched, total, (int64_t)gridDim.x * kWaves);
   int64_t t = (int64_t)blockIdx.x * kWaves + wave;
-  while (t < total) {
+  if (t >= total) t = tq.next(lane);
+  while (t >= 0) {
     gemv_task<M>(descs, count, t, Mact, lut, lane);
-    uint32_t ticket = 0;
-    if (lane == 0) ticket = __hip_atomic_fetch_add(sched, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    t = (int64_t)nwaves + __builtin_amdgcn_readfirstlane(ticket);
+    t = tq.next(lane);
   }
-  if (lane == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(sched + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == nwaves - 1) {  // every other wave has drawn its last ticket
-      __hip_atomic_store(sched, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sched + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  tq.checkout(lane);
 }
 
 // ---------------------------------------------------------------- launchers

@@ -150,4 +150,62 @@ __device__ __forceinline__ int find_desc(const ql_gemv_desc* __restrict__ descs,
   return lo;
 }
 
+// ---------------------------------------------------------------- task queues
+// Persistent grouped launches run tasks 0..total-1, numbered by the host
+// longest first.  Wave w of the launch takes task w; the rest, r = t - nwaves,
+// are dealt round-robin to kQueues queues (queue q holds r = q, q + kQueues,
+// ..., so each queue is longest-first too), each a counter in its own 128-byte
+// line of the caller's state buffer.  A wave draws from its home queue (its
+// workgroup index mod kQueues) until the queue runs dry; then one 64-lane load
+// reads every queue's counter and the wave moves to the first live queue after
+// its home.  One shared counter would serialize every draw of the launch on a
+// single address, which caps the whole launch at one task per atomic round
+// trip.  Counters only grow, so a stale read can only show a dry queue as live;
+// the draw that follows then fails and the wave reads again.
+constexpr int kQueues = 64;         // one per lane of the scan
+constexpr int kQueueStride = 32;    // words between counters (128 bytes)
+constexpr int kSchedDone = kQueues * kQueueStride;  // check-out word
+static_assert(kSchedDone + 1 <= QL_SCHED_WORDS, "scheduler state larger than QL_SCHED_WORDS");
+
+struct TaskQueues {
+  uint32_t* sched;
+  int64_t nwaves;  // tasks of the first round
+  int64_t rest;    // tasks dealt to the queues (total - nwaves, may be <= 0)
+  int home;
+
+  __device__ TaskQueues(uint32_t* s, int64_t total, int64_t nw)
+      : sched(s), nwaves(nw), rest(total - nw), home((int)(blockIdx.x % kQueues)) {}
+
+  __device__ uint32_t qcount(int q) const {
+    return rest > q ? (uint32_t)((rest - q + kQueues - 1) / kQueues) : 0u;
+  }
+  // the next task of this wave, or -1 once every queue is dry (wave-uniform)
+  __device__ int64_t next(int lane) {
+    for (;;) {
+      const uint32_t cnt = qcount(home);
+      if (cnt > 0) {
+        uint32_t t = 0;
+        if (lane == 0) t = __hip_atomic_fetch_add(sched + home * kQueueStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t = __builtin_amdgcn_readfirstlane(t);
+        if (t < cnt) return nwaves + home + (int64_t)t * kQueues;
+      }
+      const int q = (home + lane) % kQueues;
+      const uint32_t c = __hip_atomic_load(sched + q * kQueueStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t live = __ballot(c < qcount(q));
+      if (!live) return -1;
+      home = (home + (int)__builtin_ctzll(live)) % kQueues;
+    }
+  }
+  // every wave checks out once; the last one zeroes the state for the next launch
+  __device__ void checkout(int lane) {
+    uint32_t done = 0;
+    if (lane == 0) done = __hip_atomic_fetch_add(sched + kSchedDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __builtin_amdgcn_readfirstlane(done);
+    if (done == (uint32_t)(nwaves - 1)) {
+      __hip_atomic_store(sched + lane * kQueueStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(sched + kSchedDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+};
+
 }  // namespace ql

@@ -18,7 +18,7 @@ import torch
 GRID_T, GRID_I2, GRID_I3, GRID_MIXED = 0, 1, 2, 3
 GRID_C4 = 4  # 4-bit container baseline (not a ThinkBit grid)
 GROUP, SLAB, BLOCK = 128, 64, 128
-QL_SCHED_WORDS = 4  # uint32 words of grouped-launch scheduler state
+QL_SCHED_WORDS = 2080  # uint32 words of grouped-launch scheduler state
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "libqlinear.so")

@@ -165,12 +165,14 @@ typedef struct {
  * K = 4096 rows). */
 int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
 
-/* Words of the task-scheduler state of a grouped launch. */
-#define QL_SCHED_WORDS 4
+/* Words of the task-scheduler state of a grouped launch: 64 task-queue counters, each in its
+ * own 128-byte line, and a check-out word.  Draws spread over many counters because atomics
+ * on one shared address serialize across the whole device. */
+#define QL_SCHED_WORDS 2080
 
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
  * descs (dev), count entries) at batch M = 1 in one persistent launch; other M return
- * QL_EUNSUPPORTED.  Waves take 64-row slab tasks from an atomic counter in `sched`
+ * QL_EUNSUPPORTED.  Waves take 64-row slab tasks from atomic queue counters in `sched`
  * (dev, QL_SCHED_WORDS uint32, 16-byte aligned, owned by the caller): it must be all
  * zero when a launch starts, and every launch that runs to completion leaves it zero
  * again, so one zeroing at allocation serves any number of launches.  Launches that
