@@ -153,8 +153,8 @@ __global__ void __launch_bounds__(kC4Waves * 64, 4) c4_gemv_kernel(ql_gemv_desc 
 }
 
 // Persistent launch over many containers, scheduled exactly as the native
-// grouped GEMV: first task by wave index, then draws from the task queues at
-// the end of each task.
+// grouped GEMV: first task by wave index, then draws from the task queues, each
+// made when the previous task starts.
 __global__ void __launch_bounds__(kC4Waves * 64, 4) c4_gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
                                                                           int count, int64_t total,
                                                                           uint32_t* __restrict__ sched) {
@@ -167,8 +167,9 @@ __global__ void __launch_bounds__(kC4Waves * 64, 4) c4_gemv_grouped_kernel(const
   int64_t t = (int64_t)blockIdx.x * kC4Waves + wave;
   if (t >= total) t = tq.next(lane);
   while (t >= 0) {
+    const uint32_t claim = tq.claim(lane);
     c4_task(descs, count, t, lut, lane);
-    t = tq.next(lane);
+    t = tq.resolve(claim, lane);
   }
   tq.checkout(lane);
 }

@@ -571,11 +571,12 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_kernel(ql_g
 }
 
 // Many independent matrices in one persistent launch.  Slab costs differ
-// (row length, grid), so after its first task a wave draws the next one from
-// the task queues when it finishes a task: greedy list scheduling over tasks
-// that the host numbered longest-first.  (A task drawn when the previous one
-// starts would hide the draw latency but fixes the next round's assignment at
-// launch time, which balances far worse.)
+// (row length, grid), so after its first task a wave keeps drawing tasks from
+// the task queues: list scheduling over tasks that the host numbered
+// longest-first.  The next task is drawn when the current one starts and read
+// when it ends, so the atomic's round trip is hidden behind the task instead
+// of stalling the wave between tasks; a wave then holds at most one task
+// ahead, which costs little balance because the last tasks are the shortest.
 template <int M>
 __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
                                                                       int count, int64_t total, int Mact,
@@ -589,8 +590,9 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_ker
   int64_t t = (int64_t)blockIdx.x * kWaves + wave;
   if (t >= total) t = tq.next(lane);
   while (t >= 0) {
+    const uint32_t claim = tq.claim(lane);
     gemv_task<M>(descs, count, t, Mact, lut, lane);
-    t = tq.next(lane);
+    t = tq.resolve(claim, lane);
   }
   tq.checkout(lane);
 }

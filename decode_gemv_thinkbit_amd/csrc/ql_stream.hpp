@@ -196,6 +196,19 @@ struct TaskQueues {
       home = (home + (int)__builtin_ctzll(live)) % kQueues;
     }
   }
+  // draw from the home queue now; lane 0 holds the result until resolve reads it
+  __device__ uint32_t claim(int lane) {
+    uint32_t t = 0xFFFFFFFFu;
+    if (qcount(home) > 0 && lane == 0)
+      t = __hip_atomic_fetch_add(sched + home * kQueueStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return t;
+  }
+  // the task a claim drew, or the next one found by next() if it drew nothing
+  __device__ int64_t resolve(uint32_t claimed, int lane) {
+    const uint32_t t = __builtin_amdgcn_readfirstlane(claimed);
+    if (t < qcount(home)) return nwaves + home + (int64_t)t * kQueues;
+    return next(lane);
+  }
   // every wave checks out once; the last one zeroes the state for the next launch
   __device__ void checkout(int lane) {
     uint32_t done = 0;
