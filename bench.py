@@ -35,7 +35,8 @@ HBM_PEAK_GBS = 8000.0
 # Sources whose code decides the GEMV kernel's memory traffic; a traffic figure
 # measured with rocprofv3 counters is reported only while their hash matches.
 KERNEL_SOURCES = ["decode_gemv_thinkbit_amd/csrc/ql_gemv.hip", "decode_gemv_thinkbit_amd/csrc/ql_stream.hpp",
-                  "decode_gemv_thinkbit_amd/csrc/ql_device.hpp", "decode_gemv_thinkbit_amd/csrc/ql_internal.hpp"]
+                  "decode_gemv_thinkbit_amd/csrc/ql_luts.hpp", "decode_gemv_thinkbit_amd/csrc/ql_device.hpp",
+                  "decode_gemv_thinkbit_amd/csrc/ql_internal.hpp"]
 TRAFFIC_SUMMARY = "profiles/gemv_grouped_qwen3_8b_pass.md"
 METRIC = "packed-weight GB/s & % HBM peak, batch-1 GEMV; µs per 8B-shape decode weight pass"
 

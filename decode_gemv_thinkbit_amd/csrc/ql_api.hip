@@ -195,12 +195,14 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
 
 ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int32_t M,
                                uint32_t* sched, hipStream_t stream) {
-  if (M < 1 || M > 8) return fail(QL_EINVAL, "grouped gemv needs 1 <= M <= 8 (M=%d)", M);
-  if (M != 1) return fail(QL_EUNSUPPORTED, "grouped gemv runs batch 1 only (M=%d); use qlinear_gemm per matrix", M);
+  if (M < 1 || M > 16) return fail(QL_EINVAL, "grouped gemv needs 1 <= M <= 16 (M=%d)", M);
   if (count <= 0 || total_slabs <= 0 || total_slabs >= ((int64_t)1 << 31))
     return fail(QL_EINVAL, "bad count (%d) or slab total (%lld)", count, (long long)total_slabs);
   QL_TRY(check_ptrs({descs, sched}));
-  return hip_status(ql::launch_gemv_grouped(descs, count, total_slabs, M, sched, stream), "grouped gemv launch");
+  if (M == 1)
+    return hip_status(ql::launch_gemv_grouped(descs, count, total_slabs, M, sched, stream), "grouped gemv launch");
+  return hip_status(ql::launch_gemv_mm_grouped(descs, count, total_slabs, M, sched, stream),
+                    "grouped batched gemv launch");
 }
 
 size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return ql::gemm_workspace_bytes(M, N, K); }

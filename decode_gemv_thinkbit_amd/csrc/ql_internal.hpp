@@ -33,6 +33,9 @@ struct MatArgs {
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M, uint32_t* sched,
                                hipStream_t stream);
+// 2 <= M <= 16: the batched-decode kernel (MFMA), same descriptors and scheduler state
+hipError_t launch_gemv_mm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M,
+                                  uint32_t* sched, hipStream_t stream);
 hipError_t launch_c4_gemv(const MatArgs& a, hipStream_t stream);
 hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, uint32_t* sched,
                                   hipStream_t stream);

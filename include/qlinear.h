@@ -171,8 +171,12 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
 #define QL_SCHED_WORDS 2080
 
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
- * descs (dev), count entries) at batch M = 1 in one persistent launch; other M return
- * QL_EUNSUPPORTED.  Waves take 64-row slab tasks from atomic queue counters in `sched`
+ * descs (dev), count entries) in one persistent launch, at one batch size M for all entries
+ * (1 <= M <= 16; each x is M x K, each y M x N).  M = 1 runs the batch-1 kernel (v_dot2);
+ * 2 <= M <= 16 the batched-decode kernel, which decodes each packed byte once and runs the
+ * M-token products on MFMA (products exact, fp32 sums; summary page, section "What it is":
+ * a decode step at a small batch still streams every weight once).  M outside 1..16 returns
+ * QL_EINVAL.  Waves take 64-row slab tasks from atomic queue counters in `sched`
  * (dev, QL_SCHED_WORDS uint32, 16-byte aligned, owned by the caller): it must be all
  * zero when a launch starts, and every launch that runs to completion leaves it zero
  * again, so one zeroing at allocation serves any number of launches.  Launches that

@@ -84,7 +84,8 @@ def test_other_argument_errors():
     assert L.qlinear_unpack(4, 128, 9, None, None, FAKE, FAKE, None) == 1
     assert L.qlinear_dequant(4, 128, 0, None, None, None, FAKE, 0, FAKE, None) == 1
     assert L.qlinear_gemv_grouped(FAKE, 0, 10, 1, FAKE, None) == 1
-    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 9, FAKE, None) == 1
+    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 17, FAKE, None) == 1  # batch above 16
+    assert L.qlinear_gemv_grouped(FAKE, 2, 10, 0, FAKE, None) == 1
     assert L.qlinear_gemv_grouped(FAKE, 2, 10, 1, None, None) == 1  # no scheduler state
     assert L.qlinear_gemv_grouped(FAKE, 2, 10, 1, MISALIGNED, None) == 1
     bad = np.array([0, 7], np.int8)
