@@ -43,8 +43,14 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-constexpr int kMmWaves = 8;   // waves per workgroup
-constexpr int kMmWgPerCu = 2;  // resident workgroups per CU (LDS tables: 69 KB each)
+#ifndef QL_MM_WAVES
+#define QL_MM_WAVES 6
+#endif
+#ifndef QL_MM_WAVES_PER_EU
+#define QL_MM_WAVES_PER_EU 3
+#endif
+constexpr int kMmWaves = QL_MM_WAVES;  // waves per workgroup
+constexpr int kMmWgPerCu = 2;  // resident workgroups per CU (LDS tables: 69 KB each; 168 VGPRs: 3 waves per SIMD)
 constexpr int kRB = kSlab / 16;  // 16-row blocks per slab
 
 __device__ __forceinline__ f32x4_t mma(const u32x4_t& xa, const u32x4_t& cb, const f32x4_t& c) {
@@ -98,15 +104,47 @@ __device__ __forceinline__ void zero(Acc& a) {
   for (int rb = 0; rb < kRB; ++rb) a.v[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// y += s(row, g) * D for the slab's rows; lane l holds weight row 16 rb + (l & 15)
-__device__ __forceinline__ void flush(Acc& y, const Acc& d, const uint16_t* scales, int g, int G, int lane) {
-  if (g >= G) return;
+// Group scales of the slab's four row blocks (row 16 rb + (lane & 15)), read as
+// aligned dwords that hold groups 2k and 2k+1, one pair of groups ahead of use
+// (a scale read right before its multiply would stall the wave on memory at
+// every group).
+struct Scales {
+  uint32_t cur[kRB], nxt[kRB];  // pairs k and k + 1
+  const uint16_t* ss;
+  int G, lane;
+  __device__ __forceinline__ void load(uint32_t (&v)[kRB], int k) const {
+    int g = 2 * k;
+    g = g < G ? g : G - 1;  // past the row: any in-range pair (never used)
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const float s = ld_scale(scales, g, 16 * rb + (lane & 15));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y.v[rb][i] = fmaf(s, d.v[rb][i], y.v[rb][i]);
+    for (int rb = 0; rb < kRB; ++rb) v[rb] = ld_scale_pair(ss, g, 16 * rb + (lane & 15));
   }
+  __device__ __forceinline__ Scales(const uint16_t* s, int g_count, int l) : ss(s), G(g_count), lane(l) {
+    load(cur, 0);
+    load(nxt, 1);
+  }
+  // after the last group of pair k: move to pair k + 1 and start reading pair k + 2
+  __device__ __forceinline__ void advance(int k) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) cur[rb] = nxt[rb];
+    load(nxt, k + 2);
+  }
+  __device__ __forceinline__ float get(int rb, int g) const {
+    return __uint_as_float((g & 1) ? (cur[rb] & 0xFFFF0000u) : (cur[rb] << 16));
+  }
+};
+
+// y += s(row, g) * D; lane l holds weight row 16 rb + (l & 15).  Moves the
+// scale window on after the second group of a pair.
+__device__ __forceinline__ void flush(Acc& y, const Acc& d, Scales& sc, int g) {
+  if (g < sc.G) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const float s = sc.get(rb, g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y.v[rb][i] = fmaf(s, d.v[rb][i], y.v[rb][i]);
+    }
+  }
+  if (g & 1) sc.advance(g >> 1);
 }
 
 // ---------------------------------------------------------------- ternary
@@ -116,32 +154,11 @@ constexpr int t_edge(int c) { return c == 1 ? 48 : c == 3 ? 16 : c == 4 ? 64 : c
 // chunk phases after which a group ends (its accumulator is scaled and cleared)
 constexpr bool t_flush_after(int c) { return c == 1 || c == 3 || c == 4 || c == 6 || c == 7; }
 
-// the 4-dword x operand of window w (byte 4q + w of the lane's chunk dword)
-template <int W>
-__device__ __forceinline__ u32x4_t t_xop(const uint32_t (&X)[10]) {
-  constexpr int u = W >> 1;
-  if constexpr ((W & 1) == 0)
-    return u32x4_t{X[5 * u], X[5 * u + 1], X[5 * u + 2], 0u};
-  else
-    return u32x4_t{X[5 * u + 3], X[5 * u + 4], 0u, X[5 * u + 2]};
-}
-
-// the same with the dwords at or past the edge (index >= nlo) zeroed
-template <int W>
-__device__ __forceinline__ u32x4_t t_xop_lo(const uint32_t (&X)[10], int nlo) {
-  constexpr int u = W >> 1;
-  auto lo = [&](int i) __attribute__((always_inline)) { return i < nlo ? X[i] : 0u; };
-  if constexpr ((W & 1) == 0)
-    return u32x4_t{lo(5 * u), lo(5 * u + 1), lo(5 * u + 2), 0u};
-  else
-    return u32x4_t{lo(5 * u + 3), lo(5 * u + 4), 0u, lo(5 * u + 2)};
-}
-
 struct TWinE {
   u32x4_t e[kRB];
 };
 
-// table entries of window W from the chunk's code dwords (one per row block)
+// table entries of window W (byte W of each code dword; one per row block)
 template <int W>
 __device__ __forceinline__ void t_read(TWinE& b, const uint32_t (&cd)[kRB], uint32_t lane_off, const uint8_t* lut) {
 #pragma unroll
@@ -151,8 +168,20 @@ __device__ __forceinline__ void t_read(TWinE& b, const uint32_t (&cd)[kRB], uint
   }
 }
 
+// x of byte pair u (0, 1) of the lane's chunk dword: five dwords, inputs 10u .. 10u+9
+// of the lane's 20 (byte offset 160 ch + 40 q + 20 u of the token row)
+struct X5 {
+  uint32_t d[5];
+};
+__device__ __forceinline__ void load_x5(X5& x, const XSrc& xs, uint32_t off) {
+  const u32x4_t a = xs.b128(off);
+  x.d[0] = a.x; x.d[1] = a.y; x.d[2] = a.z; x.d[3] = a.w;
+  x.d[4] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xs.rsrc, xs.base + off + 16, 0, 0);
+}
+
 __device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int K, int G, int lane,
                       const uint8_t* lut, Acc& y) {
+  Scales sc(scales, G, lane);
   const int nchunks = (K + 79) / 80;
   const int nper = (nchunks + 7) / 8;
   const CodeDw src(codes, nchunks, lane);
@@ -161,52 +190,71 @@ __device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& 
   Acc cur, nxt;
   zero(cur);
   zero(nxt);
-  // ring of code dwords: chunk ch lives in slot ch % 4 (a period is 8 chunks), two ahead
+  // code dwords: chunk ch in slot ch % 4, loaded two chunks ahead; x by byte
+  // pair, one pair ahead (pair P of a period in buffer P % 2).  Every load is
+  // unconditional (past the slab or x it reads zero), which keeps the
+  // compiler's wait counts exact.
   uint32_t cd[4][kRB];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) cd[s][rb] = src.load(s, rb);
+  // x pair P (global: 2 ch + U) in slot P % 4, three pairs ahead
+  X5 xw[4];
+  auto xoff = [&](int P) __attribute__((always_inline)) { return (uint32_t)(160 * (P >> 1) + 40 * q + 20 * (P & 1)); };
+#pragma unroll
+  for (int i = 0; i < 3; ++i) load_x5(xw[i], xs, xoff(i));
+  // table entries, one window ahead (window w of a chunk in buffer w % 2)
+  TWinE ent[2];
+  t_read<0>(ent[0], cd[0], lane_off, lut);
+  // The last period skips its second half when the row ends in the first:
+  // no group still inside K ends after chunk 4 of such a period (K is a
+  // multiple of 128).
+  const bool short_last = nchunks - 8 * (nper - 1) <= 4;
   for (int p = 0; p < nper; ++p) {
     const bool tail = p == nper - 1;
-    sfor<8>([&](auto c_) __attribute__((always_inline)) {
+    auto chunk = [&](auto c_) __attribute__((always_inline)) {
       constexpr int C = decltype(c_)::value;
+      constexpr int E = t_edge(C);
       const int ch = 8 * p + C;
       sched_fence();
-      if (ch < nchunks) {
-        // prefetch chunk ch + 2 (slot (ch + 2) % 4; chunk ch - 2 is done with it)
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) cd[(C + 2) & 3][rb] = src.load(ch + 2, rb);
-        // x dwords of this chunk: inputs 80 ch + 20 q .. + 19
-        uint32_t X[10];
-        {
-          const uint32_t off = (uint32_t)(160 * ch + 40 * q);
-          const u32x4_t a = xs.b128(off), b = xs.b128(off + 16);
-          const u32x2_t c2 = xs.b64(off + 32);
-          X[0] = a.x; X[1] = a.y; X[2] = a.z; X[3] = a.w;
-          X[4] = b.x; X[5] = b.y; X[6] = b.z; X[7] = b.w;
-          X[8] = c2.x; X[9] = c2.y;
-        }
-        if (tail) {  // inputs past K meet zero codes; keep them zero on this side too
-          const int left = K - (80 * ch + 20 * q);
+      for (int rb = 0; rb < kRB; ++rb) cd[(C + 2) & 3][rb] = src.load(ch + 2, rb);
+      sfor<2>([&](auto u_) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_)::value;
+        constexpr int P = 2 * C + U;  // pair within the period (the period holds 16)
+        load_x5(xw[(P + 3) & 3], xs, xoff(2 * ch + U + 3));
+        X5 x = xw[P & 3];
+        if (tail) {  // inputs past K meet padding codes; keep them zero on this side too
+          const int left = K - (80 * ch + 20 * q + 10 * U);
 #pragma unroll
-          for (int i = 0; i < 10; ++i) X[i] = 2 * i < left ? X[i] : 0u;
+          for (int i = 0; i < 5; ++i) x.d[i] = 2 * i < left ? x.d[i] : 0u;
         }
-        constexpr int E = t_edge(C);
-        // edge chunk: how many of the lane's 10 x dwords lie before the edge
-        const int nlo = E == 0 ? 10 : ((E - 20 * q) / 2 < 0 ? 0 : (E - 20 * q) / 2);
-        sfor<4>([&](auto w_) __attribute__((always_inline)) {
-          constexpr int W = decltype(w_)::value;
-          TWinE cur_e;
-          sched_fence();
-          t_read<W>(cur_e, cd[C & 3], lane_off, lut);
-          lgkm_wait0();
-          const u32x4_t xo = t_xop<W>(X);
+        // edge chunk: how many of this pair's five dwords lie before the edge
+        int nlo = 5;
+        if constexpr (E != 0) {
+          const int v = (E - 20 * q - 10 * U) / 2;
+          nlo = v < 0 ? 0 : (v > 5 ? 5 : v);
+        }
+        sfor<2>([&](auto h_) __attribute__((always_inline)) {
+          constexpr int H = decltype(h_)::value;  // even / odd byte of the pair
+          constexpr int W = 2 * U + H;
+          // this window's entries were read one window earlier; read the next
+          // window's now (the last window of a chunk reads window 0 of the next
+          // chunk, whose code dwords are already in the ring)
+          if constexpr (W < 3)
+            t_read<W + 1>(ent[(W + 1) & 1], cd[C & 3], lane_off, lut);
+          else
+            t_read<0>(ent[0], cd[(C + 1) & 3], lane_off, lut);
+          const TWinE& cur_e = ent[W & 1];
+          // even byte: (x0,x1) (x2,x3) (x4,x5) 0; odd byte: (x6,x7) (x8,x9) 0 (x4,x5)
+          const u32x4_t xo = H == 0 ? u32x4_t{x.d[0], x.d[1], x.d[2], 0u} : u32x4_t{x.d[3], x.d[4], 0u, x.d[2]};
           if constexpr (E == 0) {
 #pragma unroll
             for (int rb = 0; rb < kRB; ++rb) cur.v[rb] = mma(xo, cur_e.e[rb], cur.v[rb]);
           } else {
-            const u32x4_t xl = t_xop_lo<W>(X, nlo);
+            auto lo = [&](int i) __attribute__((always_inline)) { return i < nlo ? x.d[i] : 0u; };
+            const u32x4_t xl = H == 0 ? u32x4_t{lo(0), lo(1), lo(2), 0u} : u32x4_t{lo(3), lo(4), 0u, lo(2)};
             const u32x4_t xh = xo ^ xl;
 #pragma unroll
             for (int rb = 0; rb < kRB; ++rb) {
@@ -215,68 +263,99 @@ __device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& 
             }
           }
         });
-      }
+      });
       if constexpr (t_flush_after(C)) {
         constexpr int gl = C == 1 ? 0 : C == 3 ? 1 : C == 4 ? 2 : C == 6 ? 3 : 4;
-        flush(y, cur, scales, 5 * p + gl, G, lane);
+        flush(y, cur, sc, 5 * p + gl);
         cur = nxt;
         zero(nxt);
       }
-    });
+    };
+    sfor<4>(chunk);
+    if (!(tail && short_last)) sfor_from<4, 4>(chunk);
   }
 }
 
 // ---------------------------------------------------------------- 2-bit
 // A group is 32 bytes = 2 chunks of 64 inputs.  Lane q's chunk dword holds
 // bytes 4q..4q+3 (inputs 16q .. 16q+15 of the chunk); window w takes bytes
-// 4q + 2w, 4q + 2w + 1, whose x dwords are 8q + 4w .. + 3 of the chunk.
+// 4q + 2w, 4q + 2w + 1, whose x dwords are 8q + 4w .. + 3 of the chunk
+// (byte offset 128 ch + 32 q + 16 w of the token row).
 __device__ void run_i2(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int K, int G, int lane,
                        const uint8_t* lut, Acc& y) {
+  Scales sc(scales, G, lane);
   const int nchunks = 2 * G;
   const CodeDw src(codes, nchunks, lane);
   const int q = lane >> 4;
   const uint32_t lane_off = (uint32_t)(lane & 3) << 3;
-  uint32_t cd[2][kRB];
+  // table entries of window W (bytes 2W, 2W+1) of a chunk's code dwords
+  struct E2 {
+    u32x2_t e[kRB][2];
+  };
+  auto read = [&](E2& b, const uint32_t (&c)[kRB], int W) __attribute__((always_inline)) {
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) cd[0][rb] = src.load(0, rb);
-  for (int g = 0; g < G; ++g) {
-    Acc d;
-    zero(d);
-    sfor<2>([&](auto h_) __attribute__((always_inline)) {
-      constexpr int H = decltype(h_)::value;
-      const int ch = 2 * g + H;
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) cd[H ^ 1][rb] = src.load(ch + 1, rb);
-      const uint32_t off = (uint32_t)(128 * ch + 32 * q);
-      const u32x4_t x0 = xs.b128(off), x1 = xs.b128(off + 16);
-      u32x2_t e[2][kRB][2];
-      sfor<2>([&](auto w_) __attribute__((always_inline)) {
-        constexpr int W = decltype(w_)::value;
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint32_t bv = (cd[H][rb] >> (8 * (2 * W + j))) & 0xFFu;
-            e[W][rb][j] = lds_b64(lut + kI2Lut + ((bv << 5) | lane_off));
-          }
-      });
-      lgkm_wait0();
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        d.v[rb] = mma(x0, u32x4_t{e[0][rb][0].x, e[0][rb][0].y, e[0][rb][1].x, e[0][rb][1].y}, d.v[rb]);
-        d.v[rb] = mma(x1, u32x4_t{e[1][rb][0].x, e[1][rb][0].y, e[1][rb][1].x, e[1][rb][1].y}, d.v[rb]);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t bv = (c[rb] >> (8 * (2 * W + j))) & 0xFFu;
+        b.e[rb][j] = lds_b64(lut + kI2Lut + ((bv << 5) | lane_off));
       }
+  };
+  // code dwords of chunk ch in slot ch % 4, two chunks ahead; x and table
+  // entries one window ahead
+  uint32_t cd[4][kRB];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) cd[s][rb] = src.load(s, rb);
+  // x of window wi (global: 2 ch + W) in slot wi % 4, three windows ahead
+  u32x4_t xw[4];
+  auto xoff2 = [&](int wi) __attribute__((always_inline)) { return (uint32_t)(128 * (wi >> 1) + 32 * q + 16 * (wi & 1)); };
+#pragma unroll
+  for (int i = 0; i < 3; ++i) xw[i] = xs.b128(xoff2(i));
+  E2 ent[2];
+  read(ent[0], cd[0], 0);
+  for (int gp = 0; gp < G; gp += 2) {  // two groups (4 chunks) per pass; an odd last one is dropped by flush
+    sfor<2>([&](auto s_) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_)::value;
+      const int g = gp + S;
+      Acc d;
+      zero(d);
+      sfor<2>([&](auto h_) __attribute__((always_inline)) {
+        constexpr int H = decltype(h_)::value;
+        constexpr int CS = 2 * S + H;  // chunk slot
+        const int ch = 2 * g + H;
+        sched_fence();
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) cd[(CS + 2) & 3][rb] = src.load(ch + 2, rb);
+        sfor<2>([&](auto w_) __attribute__((always_inline)) {
+          constexpr int W = decltype(w_)::value;
+          constexpr int WI = 2 * CS + W;  // window index within the pass
+          xw[(WI + 3) & 3] = xs.b128(xoff2(2 * ch + W + 3));
+          if constexpr (W == 0)
+            read(ent[(WI + 1) & 1], cd[CS], 1);
+          else
+            read(ent[(WI + 1) & 1], cd[(CS + 1) & 3], 0);
+          const u32x4_t xo = xw[WI & 3];
+          const E2& e = ent[WI & 1];
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+            d.v[rb] = mma(xo, u32x4_t{e.e[rb][0].x, e.e[rb][0].y, e.e[rb][1].x, e.e[rb][1].y}, d.v[rb]);
+        });
+      });
+      flush(y, d, sc, g);
     });
-    flush(y, d, scales, g, G, lane);
   }
 }
 
 // ---------------------------------------------------------------- 3-bit
 // A group is 48 bytes = four 96-bit triples of 32 codes.  Lane q decodes triple
 // q of its row (three aligned dwords, each inside one chunk); window w takes
-// fields 4w .. 4w+3 (codes 32q + 8w ..), whose x dwords are 16q + 4w .. + 3.
+// fields 4w .. 4w+3 (codes 32q + 8w ..), whose x dwords are 16q + 4w .. + 3
+// (byte offset 256 g + 64 q + 16 w of the token row).
 __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int K, int G, int lane,
                        const uint8_t* lut, Acc& y) {
+  Scales sc(scales, G, lane);
   const int nchunks = 3 * G;
   const CodeDw src(codes, nchunks, lane);
   const int q = lane >> 4;
@@ -295,39 +374,54 @@ __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc&
         t[rb][j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
             src.rsrc, src.lane_off + toff[j] + (uint32_t)(3 * g) * kSlabChunkBytes + rb * 256u, 0, 2);
   };
+  // triples of group g in slot g % 2, one group ahead; x and table entries one
+  // window ahead
+  struct E3 {
+    uint32_t e[kRB][4];
+  };
+  auto read = [&](E3& b, const uint32_t (&t)[kRB][3], auto w_) __attribute__((always_inline)) {
+    constexpr int W = decltype(w_)::value;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const uint32_t w0 = t[rb][0], w1 = t[rb][1], w2 = t[rb][2];
+      b.e[rb][0] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 0>(w0, w1, w2));
+      b.e[rb][1] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 1>(w0, w1, w2));
+      b.e[rb][2] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 2>(w0, w1, w2));
+      b.e[rb][3] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 3>(w0, w1, w2));
+    }
+  };
   uint32_t tw[2][kRB][3];
   load_tr(0, tw[0]);
-  for (int gb = 0; gb < G; gb += 2) {
+  // x of window wi (global: 4 g + W) in slot wi % 4, three windows ahead
+  u32x4_t xw[4];
+  auto xoff3 = [&](int wi) __attribute__((always_inline)) { return (uint32_t)(256 * (wi >> 2) + 64 * q + 16 * (wi & 3)); };
+#pragma unroll
+  for (int i = 0; i < 3; ++i) xw[i] = xs.b128(xoff3(i));
+  E3 ent[2];
+  read(ent[0], tw[0], std::integral_constant<int, 0>{});
+  for (int gp = 0; gp < G; gp += 2) {  // an odd last group runs past the row and is dropped by flush
     sfor<2>([&](auto s_) __attribute__((always_inline)) {
       constexpr int S = decltype(s_)::value;
-      const int g = gb + S;
-      if (g < G) {
-        load_tr(g + 1, tw[S ^ 1]);  // past the last group: reads zero, no memory access
-        const uint32_t off = (uint32_t)(256 * g + 64 * q);
-        u32x4_t xo[4];
+      const int g = gp + S;
+      sched_fence();
+      load_tr(g + 1, tw[S ^ 1]);
+      Acc d;
+      zero(d);
+      sfor<4>([&](auto w_) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_)::value;
+        constexpr int WI = 4 * S + W;
+        xw[(W + 3) & 3] = xs.b128(xoff3(4 * g + W + 3));
+        if constexpr (W < 3)
+          read(ent[(WI + 1) & 1], tw[S], std::integral_constant<int, W + 1>{});
+        else
+          read(ent[(WI + 1) & 1], tw[S ^ 1], std::integral_constant<int, 0>{});
+        const u32x4_t xo = xw[W];
+        const E3& e = ent[WI & 1];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) xo[w] = xs.b128(off + 16 * w);
-        Acc d;
-        zero(d);
-        sfor<4>([&](auto w_) __attribute__((always_inline)) {
-          constexpr int W = decltype(w_)::value;
-          sched_fence();
-          uint32_t e[kRB][4];
-#pragma unroll
-          for (int rb = 0; rb < kRB; ++rb) {
-            const uint32_t w0 = tw[S][rb][0], w1 = tw[S][rb][1], w2 = tw[S][rb][2];
-            e[rb][0] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 0>(w0, w1, w2));
-            e[rb][1] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 1>(w0, w1, w2));
-            e[rb][2] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 2>(w0, w1, w2));
-            e[rb][3] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 3>(w0, w1, w2));
-          }
-          lgkm_wait0();
-#pragma unroll
-          for (int rb = 0; rb < kRB; ++rb)
-            d.v[rb] = mma(xo[W], u32x4_t{e[rb][0], e[rb][1], e[rb][2], e[rb][3]}, d.v[rb]);
-        });
-        flush(y, d, scales, g, G, lane);
-      }
+        for (int rb = 0; rb < kRB; ++rb)
+          d.v[rb] = mma(xo, u32x4_t{e.e[rb][0], e.e[rb][1], e.e[rb][2], e.e[rb][3]}, d.v[rb]);
+      });
+      flush(y, d, sc, g);
     });
   }
 }
@@ -363,7 +457,7 @@ __device__ __forceinline__ void mm_task(const ql_gemv_desc* __restrict__ descs, 
   }
 }
 
-__global__ void __launch_bounds__(kMmWaves * 64, 4) gemv_mm_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
+__global__ void __launch_bounds__(kMmWaves * 64, QL_MM_WAVES_PER_EU) gemv_mm_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
                                                                          int count, int64_t total, int M,
                                                                          uint32_t* __restrict__ sched) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
