@@ -11,7 +11,9 @@ bytes / time per pass), microseconds per pass, the roofline of the GEMV
 kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed on a bounded
 sample of the same workload.  A "gemm" object adds the batched path on one
 Qwen3-8B-shaped layer (mixed grids, M = 64 / 256 / 512): microseconds per layer
-and MFMA utilisation against the dense bf16 peak; "container_ab" times the
+and MFMA utilisation against the dense bf16 peak; "batched" runs the Qwen3-14B
+stack and the 8B pass at decode batches M = 4 and 16 (grouped launch, batched-decode
+kernel); "container_ab" times the
 Qwen3-8B pass and the Qwen3-14B stack (M = 1) once more with the same codes stored
 in 4-bit containers, the format published checkpoints use; "allocator" allocates the
 8B pass's grids by the Lagrangian knapsack and runs the pass with them; "littlebit"
@@ -114,6 +116,46 @@ def time_grouped(grp, warmup, steps):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     return wall, sum(s.elapsed_time(e) for s, e in evs) / steps
+
+
+def batched_leg(dev, warmup, steps, workloads=("qwen3_14b_stack", "qwen3_8b_pass"), Ms=(4, 16)):
+    """Decode at a small batch: the same grouped weight pass at M = 4 and 16 tokens (the
+    batched-decode kernel: each packed byte decoded once, the M-token products on MFMA).
+    Reported as stored-weight GB/s, the same numerator as the M = 1 headline, with the
+    oracle on sampled rows."""
+    import torch
+    from decode_gemv_thinkbit_amd import configs
+    from decode_gemv_thinkbit_amd import qlinear as ql
+    from decode_gemv_thinkbit_amd import synth
+
+    out = []
+    for wl_name in workloads:
+        wl = configs.WORKLOADS[wl_name]
+        wi = list(configs.WORKLOADS).index(wl_name)
+        items, meta, stored, _ = build_pass(wl, wi, max(Ms), dev)
+        for M in Ms:
+            if M == max(Ms):
+                its = items
+            else:
+                xs = {}
+                its = []
+                for (pw, x, _), (layer, mi, lin, _s, _g) in zip(items, meta):
+                    key = (layer, lin.x_slot)
+                    if key not in xs:
+                        xs[key] = synth.activations(M, lin.K, synth.x_seed(wi, layer, lin.x_slot, M), device=dev)
+                    its.append((pw, xs[key], torch.empty((M, lin.N), dtype=torch.float32, device=dev)))
+            wall_ms, kern_ms = time_grouped(ql.GroupedGemv(its), warmup, steps)
+            err, nw, nmat = parity_sample(its, meta, M, dev, rows_per=16)
+            gbs = stored / (kern_ms * 1e-3) / 1e9
+            out.append({"workload": wl_name, "M": M, "us_per_pass": round(kern_ms * 1e3, 2),
+                        "us_per_step_wall": round(wall_ms * 1e3, 2), "stored_bytes": stored,
+                        "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                        "parity_max_err_over_row_norm": err, "parity_ok": err <= 2e-3})
+            log(f"batched {wl_name} M={M}: {kern_ms * 1e3:.1f} us per pass, {gbs:.0f} GB/s, parity {err:.3g}")
+            del its
+        del items
+        torch.cuda.empty_cache()
+    return {"kernel": "gemv_mm_grouped_kernel (grouped launch, 2 <= M <= 16)", "points": out}
 
 
 def container_ab(wl_name, dev, warmup, steps, native=None):
@@ -429,6 +471,7 @@ def main():
     ap.add_argument("--no-ab", action="store_true", help="skip the 4-bit container A/B leg")
     ap.add_argument("--no-alloc", action="store_true", help="skip the grid allocation leg")
     ap.add_argument("--no-littlebit", action="store_true", help="skip the LittleBit leg")
+    ap.add_argument("--no-batched", action="store_true", help="skip the small-batch (M = 4, 16) decode leg")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -504,6 +547,8 @@ def main():
         result["container_ab"] = [container_ab(args.workload, dev, args.warmup, args.steps,
                                                native=(ms_step, stored)),
                                   container_ab("qwen3_14b_stack", dev, args.warmup, args.steps)]
+    if not args.no_batched:
+        result["batched"] = batched_leg(dev, args.warmup, args.steps)
     if not args.no_alloc:
         result["allocator"] = allocator_leg(dev, args.warmup, args.steps)
     if not args.no_gemm:
