@@ -88,11 +88,6 @@ struct XSrc {
     const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, base + off, 0, 0);
     return u32x4_t{(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
   }
-  __device__ __forceinline__ u32x2_t b64(uint32_t off) const {
-    typedef int i32x2_t __attribute__((ext_vector_type(2)));
-    const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, base + off, 0, 0);
-    return u32x2_t{(uint32_t)v.x, (uint32_t)v.y};
-  }
 };
 
 struct Acc {
@@ -190,9 +185,8 @@ __device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& 
   Acc cur, nxt;
   zero(cur);
   zero(nxt);
-  // code dwords: chunk ch in slot ch % 4, loaded two chunks ahead; x by byte
-  // pair, one pair ahead (pair P of a period in buffer P % 2).  Every load is
-  // unconditional (past the slab or x it reads zero), which keeps the
+  // code dwords: chunk ch in slot ch % 4, loaded two chunks ahead.  Every load
+  // is unconditional (past the slab or x it reads zero), which keeps the
   // compiler's wait counts exact.
   uint32_t cd[4][kRB];
 #pragma unroll
@@ -301,8 +295,8 @@ __device__ void run_i2(const uint8_t* codes, const uint16_t* scales, const XSrc&
         b.e[rb][j] = lds_b64(lut + kI2Lut + ((bv << 5) | lane_off));
       }
   };
-  // code dwords of chunk ch in slot ch % 4, two chunks ahead; x and table
-  // entries one window ahead
+  // code dwords of chunk ch in slot ch % 4, two chunks ahead; table entries one
+  // window ahead
   uint32_t cd[4][kRB];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -374,8 +368,8 @@ __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc&
         t[rb][j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
             src.rsrc, src.lane_off + toff[j] + (uint32_t)(3 * g) * kSlabChunkBytes + rb * 256u, 0, 2);
   };
-  // triples of group g in slot g % 2, one group ahead; x and table entries one
-  // window ahead
+  // triples of group g in slot g % 2, one group ahead; table entries one window
+  // ahead
   struct E3 {
     uint32_t e[kRB][4];
   };
