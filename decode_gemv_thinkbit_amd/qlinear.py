@@ -451,7 +451,10 @@ class GroupedGemv:
         self.M = items[0][1].shape[0] if items[0][1].dim() == 2 else 1
         self.containers = isinstance(items[0][0], C4Weight)
         arr = (ql_gemv_desc * len(items))()
-        for i, (pw, x, y) in enumerate(items):
+        # heaviest slabs first (qlinear_grouped_prepare then orders by row length, stably):
+        # the launch ends on the cheapest tasks, which shortens its tail
+        order = sorted(range(len(items)), key=lambda j: -items[j][0].nbytes / ((items[j][0].N + 63) // 64))
+        for i, (pw, x, y) in enumerate(items[j] for j in order):
             if isinstance(pw, C4Weight) != self.containers:
                 raise ValueError("a grouped launch takes either containers or packed weights, not both")
             _dev(x, torch.bfloat16, "x")

@@ -162,7 +162,9 @@ typedef struct {
  * is free), fill slab_begin and return the total number of 64-row slabs (the task count),
  * or -1 on a bad descriptor.  Longest-first task order plus dynamic task fetching keeps
  * the persistent launch balanced when row lengths differ (a K = 12288 row costs three
- * K = 4096 rows). */
+ * K = 4096 rows).  Entries of equal K keep the caller's order: listing them by stored
+ * bytes per row, largest first (3-bit before 2-bit before ternary), ends the launch on
+ * its cheapest tasks. */
 int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
 
 /* Words of the task-scheduler state of a grouped launch: 64 task-queue counters, each in its
