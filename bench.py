@@ -13,7 +13,8 @@ sample of the same workload.  A "gemm" object adds the batched path on one
 Qwen3-8B-shaped layer (mixed grids, M = 64 / 256 / 512): microseconds per layer
 and MFMA utilisation against the dense bf16 peak; "batched" runs the Qwen3-14B
 stack and the 8B pass at decode batches M = 4 and 16 (grouped launch, batched-decode
-kernel); "container_ab" times the
+kernel); "layered" runs the 8B pass as the model orders it, four grouped launches per
+layer (qkv, o, gate_up, down) in one HIP graph, with and without split-K; "container_ab" times the
 Qwen3-8B pass and the Qwen3-14B stack (M = 1) once more with the same codes stored
 in 4-bit containers, the format published checkpoints use; "allocator" allocates the
 8B pass's grids by the Lagrangian knapsack and runs the pass with them; "littlebit"
@@ -156,6 +157,75 @@ def batched_leg(dev, warmup, steps, workloads=("qwen3_14b_stack", "qwen3_8b_pass
         del items
         torch.cuda.empty_cache()
     return {"kernel": "gemv_mm_grouped_kernel (grouped launch, 2 <= M <= 16)", "points": out}
+
+
+def layered_leg(dev, warmup, steps, wl_name="qwen3_8b_pass", Ms=(1, 4)):
+    """The dependency-respecting decode pass: per layer, four grouped launches in model order
+    (q, k, v on the attention input; o; gate, up on the MLP input; down), 144 launches for the
+    36-layer pass, captured in one HIP graph and replayed.  A launch of one layer holds far
+    fewer 64-row slabs than the device has wave slots, so it runs once with split-K (each
+    slab's input cut into parts of 640-input periods until the launch has twice as many
+    tasks as wave slots) and once without.  Same stored bytes, weights and grids as the
+    single grouped launch."""
+    import torch
+    from decode_gemv_thinkbit_amd import configs
+    from decode_gemv_thinkbit_amd import qlinear as ql
+    from decode_gemv_thinkbit_amd import synth
+
+    wl = configs.WORKLOADS[wl_name]
+    wi = list(configs.WORKLOADS).index(wl_name)
+    items1, meta, stored, _ = build_pass(wl, wi, 1, dev)
+    out = []
+    for M in Ms:
+        if M == 1:
+            items = items1
+        else:
+            xs, items = {}, []
+            for (pw, _x, _y), (layer, mi, lin, _s, _g) in zip(items1, meta):
+                key = (layer, lin.x_slot)
+                if key not in xs:
+                    xs[key] = synth.activations(M, lin.K, synth.x_seed(wi, layer, lin.x_slot, M), device=dev)
+                items.append((pw, xs[key], torch.empty((M, lin.N), dtype=torch.float32, device=dev)))
+        launches = []
+        for layer in range(wl.layers):
+            for slot in ("attn", "o", "mlp", "down"):
+                launches.append([i for i, m in enumerate(meta) if m[0] == layer and m[2].x_slot == slot])
+        for split in ("auto", None):
+            grps = [ql.GroupedGemv([items[i] for i in idx], split=split) for idx in launches]
+            for g in grps:
+                g.run()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for g in grps:
+                    g.run()
+            for _ in range(warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for a, b in evs:
+                a.record(st)
+                graph.replay()
+                b.record(st)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+            err, _nw, _nmat = parity_sample(items, meta, M, dev, rows_per=16)
+            gbs = stored / (ms * 1e-3) / 1e9
+            tasks = [g.total for g in grps[:4]]
+            out.append({"workload": wl_name, "M": M, "split_k": split or "none", "launches": len(grps),
+                        "tasks_per_launch_layer0": tasks, "us_per_pass": round(ms * 1e3, 2),
+                        "us_per_launch": round(ms * 1e3 / len(grps), 2), "gbs": round(gbs, 1),
+                        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                        "parity_max_err_over_row_norm": err, "parity_ok": err <= 2e-3})
+            log(f"layered {wl_name} M={M} split={split}: {ms * 1e3:.1f} us per pass ({len(grps)} launches), "
+                f"{gbs:.0f} GB/s, parity {err:.3g}")
+            del graph, grps
+            torch.cuda.empty_cache()
+    del items1
+    torch.cuda.empty_cache()
+    return {"variant": "dependency-respecting: 4 grouped launches per layer in one HIP graph",
+            "kernels": "gemv_grouped_kernel<1> (M = 1), gemv_mm_grouped_kernel (M > 1)", "points": out}
 
 
 def container_ab(wl_name, dev, warmup, steps, native=None):
@@ -472,6 +542,8 @@ def main():
     ap.add_argument("--no-alloc", action="store_true", help="skip the grid allocation leg")
     ap.add_argument("--no-littlebit", action="store_true", help="skip the LittleBit leg")
     ap.add_argument("--no-batched", action="store_true", help="skip the small-batch (M = 4, 16) decode leg")
+    ap.add_argument("--no-layered", action="store_true",
+                    help="skip the dependency-respecting pass (4 launches per layer, HIP graph)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -549,6 +621,8 @@ def main():
                                   container_ab("qwen3_14b_stack", dev, args.warmup, args.steps)]
     if not args.no_batched:
         result["batched"] = batched_leg(dev, args.warmup, args.steps)
+    if not args.no_layered:
+        result["layered"] = layered_leg(dev, args.warmup, args.steps)
     if not args.no_alloc:
         result["allocator"] = allocator_leg(dev, args.warmup, args.steps)
     if not args.no_gemm:

@@ -170,9 +170,10 @@ ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t* 
   return hip_status(ql::launch_gemm(a, (int)M, nullptr, 0, stream), "gemv (MFMA) launch");
 }
 
-int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
+int64_t qlinear_grouped_prepare_split(ql_gemv_desc* descs, int32_t count, int64_t min_tasks, int64_t* state_words) {
   if (!descs || count <= 0) return fail(QL_EINVAL, "empty descriptor list"), -1;
   const bool containers = descs[0].grid == QL_GRID_C4;
+  int64_t slabs = 0;
   for (int32_t i = 0; i < count; ++i) {
     const ql_gemv_desc& d = descs[i];
     if (check_shape(d.N, d.K) != QL_OK) return -1;
@@ -180,28 +181,63 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
       return fail(QL_EINVAL, "descriptor %d: a list must not mix 4-bit containers and native grids", i), -1;
     if (!containers && check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
     if (check_ptrs({d.packed, d.pscales, d.x, d.y}) != QL_OK) return -1;
+    if (d.kparts < 0) return fail(QL_EINVAL, "descriptor %d: kparts must be >= 0", i), -1;
+    if (containers && d.kparts > 1) return fail(QL_EINVAL, "descriptor %d: containers are not split", i), -1;
+    slabs += (d.N + QL_SLAB - 1) / QL_SLAB;
   }
-  // longest rows first: the tail of the launch is then made of short tasks
-  std::stable_sort(descs, descs + count, [](const ql_gemv_desc& a, const ql_gemv_desc& b) { return a.K > b.K; });
-  int64_t total = 0;
+  // parts per slab: forced, or enough for min_tasks where the rows have periods for it
+  const int64_t need = (!containers && min_tasks > slabs) ? (min_tasks + slabs - 1) / slabs : 1;
   for (int32_t i = 0; i < count; ++i) {
     ql_gemv_desc& d = descs[i];
-    if (total >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "too many slabs"), -1;
-    d.slab_begin = (int32_t)total;
-    total += (d.N + QL_SLAB - 1) / QL_SLAB;
+    const int64_t periods = (d.K + ql::kPeriodK - 1) / ql::kPeriodK;
+    const int64_t want = std::min<int64_t>(d.kparts > 0 ? d.kparts : need, QL_MAX_KPARTS);
+    d.kparts = (int32_t)std::min(want, periods);
+    d.reserved = 0;
   }
+  // longest tasks first: the tail of the launch is then made of short tasks
+  std::stable_sort(descs, descs + count, [](const ql_gemv_desc& a, const ql_gemv_desc& b) {
+    return (int64_t)a.K * b.kparts > (int64_t)b.K * a.kparts;
+  });
+  int64_t total = 0, words = QL_SCHED_WORDS;
+  words = (words + 63) / 64 * 64;
+  bool split = false;
+  for (int32_t i = 0; i < count; ++i) {
+    ql_gemv_desc& d = descs[i];
+    const int64_t ns = (d.N + QL_SLAB - 1) / QL_SLAB;
+    if (total + ns * d.kparts >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "too many tasks"), -1;
+    d.slab_begin = (int32_t)total;
+    total += ns * d.kparts;
+    d.ws_begin = 0;
+    if (d.kparts > 1) {
+      d.ws_begin = words;
+      words += ns * ql::kCounterWords + ns * d.kparts * ql::kPartWords;
+      split = true;
+    }
+  }
+  if (state_words) *state_words = split ? words : QL_SCHED_WORDS;
   return total;
 }
 
-ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int32_t M,
+int64_t qlinear_grouped_prepare(ql_gemv_desc* descs, int32_t count) {
+  if (!descs || count <= 0) return fail(QL_EINVAL, "empty descriptor list"), -1;
+  for (int32_t i = 0; i < count; ++i) descs[i].kparts = 1;
+  return qlinear_grouped_prepare_split(descs, count, 0, nullptr);
+}
+
+int64_t qlinear_grouped_wave_slots(int32_t M) {
+  if (M < 1 || M > 16) return fail(QL_EINVAL, "wave slots: M=%d outside 1..16", M), -1;
+  return ql::grouped_wave_slots(M);
+}
+
+ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int32_t M,
                                uint32_t* sched, hipStream_t stream) {
   if (M < 1 || M > 16) return fail(QL_EINVAL, "grouped gemv needs 1 <= M <= 16 (M=%d)", M);
-  if (count <= 0 || total_slabs <= 0 || total_slabs >= ((int64_t)1 << 31))
-    return fail(QL_EINVAL, "bad count (%d) or slab total (%lld)", count, (long long)total_slabs);
+  if (count <= 0 || total_tasks <= 0 || total_tasks >= ((int64_t)1 << 31))
+    return fail(QL_EINVAL, "bad count (%d) or task total (%lld)", count, (long long)total_tasks);
   QL_TRY(check_ptrs({descs, sched}));
   if (M == 1)
-    return hip_status(ql::launch_gemv_grouped(descs, count, total_slabs, M, sched, stream), "grouped gemv launch");
-  return hip_status(ql::launch_gemv_mm_grouped(descs, count, total_slabs, M, sched, stream),
+    return hip_status(ql::launch_gemv_grouped(descs, count, total_tasks, M, sched, stream), "grouped gemv launch");
+  return hip_status(ql::launch_gemv_mm_grouped(descs, count, total_tasks, M, sched, stream),
                     "grouped batched gemv launch");
 }
 

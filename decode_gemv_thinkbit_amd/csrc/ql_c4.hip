@@ -184,7 +184,7 @@ int c4_grid_size(int64_t tasks) {
 
 hipError_t launch_c4_gemv(const MatArgs& a, hipStream_t stream) {
   const int64_t nslabs = ((int64_t)a.N + kSlab - 1) / kSlab;
-  const ql_gemv_desc d{a.packed, a.pscales, nullptr, nullptr, a.x, a.y, a.N, a.K, QL_GRID_C4, 0};
+  const ql_gemv_desc d{a.packed, a.pscales, nullptr, nullptr, a.x, a.y, a.N, a.K, QL_GRID_C4, 0, 1, 0, 0};
   hipLaunchKernelGGL(c4_gemv_kernel, dim3(c4_grid_size(nslabs)), dim3(kC4Waves * 64), 0, stream, d, 1, nslabs);
   return hipGetLastError();
 }

@@ -15,6 +15,8 @@ constexpr int kChunkBytes = 16;   // bytes per row per slab step
 constexpr int kSlabChunkBytes = kChunkBytes * kSlab;  // 1024
 constexpr int kTritsPerChunk = 80;  // 16 bytes x 5 trits
 constexpr int kPeriodK = 640;       // lcm(80, 128): 8 ternary chunks = 5 groups
+constexpr int kCounterWords = 32;   // split-K state: words per slab counter (one 128-byte line)
+constexpr int kPartWords = 1024;    // split-K state: partial sums per (slab, part), 16 per lane
 
 // Ternary digit order, layout version 2.  A stored byte j holds inputs
 // 5j..5j+4 as base-3 digits.  Even bytes keep input order (digit i = input

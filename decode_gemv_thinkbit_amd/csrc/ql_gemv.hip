@@ -177,8 +177,9 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
   // the row's chunks end in the first half of its last period (p1 - 1)
   const bool last_half = nchunks - 8 * (p1 - 1) <= 4;
   uint32_t lane_off = (uint32_t)(c.lane & 15) << 4;
-  // chunks of the slab; later ones (and the ring's look-ahead past the end) read as zero
-  const ChunkSrc src(c.codes, nchunks, c.lane);
+  // chunks of the slab up to period p1; later ones (the ring's look-ahead past
+  // the end of the row or of a split part) read as zero without memory traffic
+  const ChunkSrc src(c.codes, nchunks < 8 * p1 ? nchunks : 8 * p1, c.lane);
   const i32x4_t xrs = scalar_rsrc(c.x, (uint32_t)c.K * 2u);
   // ring of R: chunk ch of a period lives in slot ch % R; once a chunk's last
   // byte is addressed its slot takes the chunk R positions later
@@ -455,10 +456,11 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
   }
 }
 
-// A slab's share of the input: periods [p0, p1) (groups 5*p0 .. 5*p1).
+// A slab's share of the input: periods [p0, p1) on ternary slabs, group
+// pairs [k0, k1) (groups 2 k0 .. min(2 k1, G) - 1) on 2- and 3-bit slabs.
 template <int M>
-__device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
-  const int g0 = 5 * p0, g1 = (5 * p1 < c.G) ? 5 * p1 : c.G;
+__device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, int p1, int k0, int k1, float (&y)[M]) {
+  const int g0 = 2 * k0, g1 = (2 * k1 < c.G) ? 2 * k1 : c.G;
   if (gr == QL_GRID_T)
     run_t<M>(c, p0, p1, y);
   else if (gr == QL_GRID_I2)
@@ -480,26 +482,33 @@ __device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, in
 constexpr int kWaves = QL_WAVES;          // waves per workgroup
 constexpr int kWgPerCu = QL_WG_PER_CU;    // resident workgroups per CU (LDS tables: 69 KB each)
 
-// One wave task: one 64-row slab of one descriptor.  Descriptor fields are
-// re-read per task, which keeps their live ranges short (the kernels stay free
-// of register spills).
+// One wave task: one 64-row slab of one descriptor, or one part of its input
+// when the entry is split (partial sums then meet in the state buffer).
+// Descriptor fields are re-read per task, which keeps their live ranges short
+// (the kernels stay free of register spills).
 template <int M>
 __device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t, int Mact,
-                                          const uint8_t* lut, int lane) {
+                                          const uint8_t* lut, int lane, uint32_t* state) {
+  static_assert(M == 1, "split partial sums hold one value per lane");
   const ql_gemv_desc& d = descs[find_desc(descs, count, t)];
-  const int64_t slab = t - d.slab_begin;
+  const SplitTask st(d, t);
   const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
   int gr;
-  const int64_t off = slab_offset(slab, K, d.grid, d.blk_grid, d.blk_off, &gr);
+  const int64_t off = slab_offset(st.slab, K, d.grid, d.blk_grid, d.blk_off, &gr);
   float y[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) y[m] = 0.0f;
-  SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off, d.pscales + slab * (int64_t)G8 * kSlab * 8, d.x, K, G,
+  SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off, d.pscales + st.slab * (int64_t)G8 * kSlab * 8, d.x, K, G,
                Mact, lane, lut};
-  run_slab<M>(gr, c, 0, (K + kPeriodK - 1) / kPeriodK, y);
-  const int64_t row = slab * kSlab + lane;
-  if (row < d.N)
-    for (int m = 0; m < Mact; ++m) d.y[(int64_t)m * d.N + row] = y[m];
+  run_slab<M>(gr, c, st.p0(K), st.p1(K), st.k0(K), st.k1(K), y);
+  if (st.split()) {
+    float* sl = st.slots(d, state);
+    st.put(sl, lane, y[0]);
+    if (!st.arrive(st.counter(d, state), lane)) return;
+    st.totals<1, 8>(sl, y, lane);
+  }
+  const int64_t row = (int64_t)st.slab * kSlab + lane;
+  if (row < d.N) d.y[row] = y[0];
 }
 
 // A single matrix: all slabs cost the same, so waves stride over them.  The
@@ -514,7 +523,7 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_kernel(ql_g
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t < total; t += (int64_t)gridDim.x * kWaves)
-    gemv_task<M>(&desc, count, t, Mact, lut, lane);
+    gemv_task<M>(&desc, count, t, Mact, lut, lane, nullptr);
 }
 
 // Many independent matrices in one persistent launch.  Slab costs differ
@@ -538,7 +547,7 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_ker
   if (t >= total) t = tq.next(lane);
   while (t >= 0) {
     const uint32_t claim = tq.claim(lane);
-    gemv_task<M>(descs, count, t, Mact, lut, lane);
+    gemv_task<M>(descs, count, t, Mact, lut, lane, sched);
     t = tq.resolve(claim, lane);
   }
   tq.checkout(lane);
@@ -565,7 +574,7 @@ int device_cu_count() {
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream) {
   if (M != 1) return hipErrorInvalidValue;
   const int64_t nslabs = ((int64_t)a.N + kSlab - 1) / kSlab;
-  const ql_gemv_desc d{a.packed, a.pscales, a.blk_grid, a.blk_off, a.x, a.y, a.N, a.K, a.grid, 0};
+  const ql_gemv_desc d{a.packed, a.pscales, a.blk_grid, a.blk_off, a.x, a.y, a.N, a.K, a.grid, 0, 1, 0, 0};
   const int slots = device_cu_count() * kWgPerCu;
   const int64_t wg_needed = (nslabs + kWaves - 1) / kWaves;
   const int grid = (int)(wg_needed < slots ? wg_needed : slots);
@@ -573,13 +582,18 @@ hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M, uint32_t* sched,
+int64_t grouped_wave_slots(int M) {
+  if (M == 1) return (int64_t)device_cu_count() * kWgPerCu * kWaves;
+  return mm_wave_slots();
+}
+
+hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
                                hipStream_t stream) {
   if (M != 1) return hipErrorInvalidValue;
   const int slots = device_cu_count() * kWgPerCu;
-  const int64_t wg_needed = (total_slabs + kWaves - 1) / kWaves;
+  const int64_t wg_needed = (total_tasks + kWaves - 1) / kWaves;
   const int grid = (int)(wg_needed < slots ? wg_needed : slots);
-  hipLaunchKernelGGL(gemv_grouped_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, descs, count, total_slabs, 1,
+  hipLaunchKernelGGL(gemv_grouped_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, descs, count, total_tasks, 1,
                      sched);
   return hipGetLastError();
 }

@@ -52,6 +52,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 constexpr int kMmWaves = QL_MM_WAVES;  // waves per workgroup
 constexpr int kMmWgPerCu = 2;  // resident workgroups per CU (LDS tables: 69 KB each; 168 VGPRs: 3 waves per SIMD)
 constexpr int kRB = kSlab / 16;  // 16-row blocks per slab
+static_assert(kRB * 4 * 64 <= kPartWords, "a split part stores 4 tokens x kRB rows per lane");
 
 __device__ __forceinline__ f32x4_t mma(const u32x4_t& xa, const u32x4_t& cb, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, cb), c,
@@ -106,16 +107,17 @@ __device__ __forceinline__ void zero(Acc& a) {
 struct Scales {
   uint32_t cur[kRB], nxt[kRB];  // pairs k and k + 1
   const uint16_t* ss;
-  int G, lane;
+  int G, lane;  // G: end of the groups this task sums (groups from G on are dropped)
   __device__ __forceinline__ void load(uint32_t (&v)[kRB], int k) const {
     int g = 2 * k;
     g = g < G ? g : G - 1;  // past the row: any in-range pair (never used)
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) v[rb] = ld_scale_pair(ss, g, 16 * rb + (lane & 15));
   }
-  __device__ __forceinline__ Scales(const uint16_t* s, int g_count, int l) : ss(s), G(g_count), lane(l) {
-    load(cur, 0);
-    load(nxt, 1);
+  // groups g0 .. g_end - 1 (pairs are aligned: g0 may be odd)
+  __device__ __forceinline__ Scales(const uint16_t* s, int g0, int g_end, int l) : ss(s), G(g_end), lane(l) {
+    load(cur, g0 >> 1);
+    load(nxt, (g0 >> 1) + 1);
   }
   // after the last group of pair k: move to pair k + 1 and start reading pair k + 2
   __device__ __forceinline__ void advance(int k) {
@@ -174,12 +176,14 @@ __device__ __forceinline__ void load_x5(X5& x, const XSrc& xs, uint32_t off) {
   x.d[4] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xs.rsrc, xs.base + off + 16, 0, 0);
 }
 
-__device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int K, int G, int lane,
-                      const uint8_t* lut, Acc& y) {
-  Scales sc(scales, G, lane);
+// Periods [p0, p1) of the slab's rows (the whole row, or one split part).
+__device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int K, int G, int p0, int p1,
+                      int lane, const uint8_t* lut, Acc& y) {
+  Scales sc(scales, 5 * p0, 5 * p1 < G ? 5 * p1 : G, lane);
   const int nchunks = (K + 79) / 80;
   const int nper = (nchunks + 7) / 8;
-  const CodeDw src(codes, nchunks, lane);
+  // chunks past the part (or the row) read as zero without memory traffic
+  const CodeDw src(codes, nchunks < 8 * p1 ? nchunks : 8 * p1, lane);
   const int q = lane >> 4;
   const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
   Acc cur, nxt;
@@ -192,12 +196,12 @@ __device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& 
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) cd[s][rb] = src.load(s, rb);
+    for (int rb = 0; rb < kRB; ++rb) cd[s][rb] = src.load(8 * p0 + s, rb);
   // x pair P (global: 2 ch + U) in slot P % 4, three pairs ahead
   X5 xw[4];
   auto xoff = [&](int P) __attribute__((always_inline)) { return (uint32_t)(160 * (P >> 1) + 40 * q + 20 * (P & 1)); };
 #pragma unroll
-  for (int i = 0; i < 3; ++i) load_x5(xw[i], xs, xoff(i));
+  for (int i = 0; i < 3; ++i) load_x5(xw[i], xs, xoff(16 * p0 + i));
   // table entries, one window ahead (window w of a chunk in buffer w % 2)
   TWinE ent[2];
   t_read<0>(ent[0], cd[0], lane_off, lut);
@@ -205,7 +209,7 @@ __device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& 
   // no group still inside K ends after chunk 4 of such a period (K is a
   // multiple of 128).
   const bool short_last = nchunks - 8 * (nper - 1) <= 4;
-  for (int p = 0; p < nper; ++p) {
+  for (int p = p0; p < p1; ++p) {
     const bool tail = p == nper - 1;
     auto chunk = [&](auto c_) __attribute__((always_inline)) {
       constexpr int C = decltype(c_)::value;
@@ -275,10 +279,12 @@ __device__ void run_t(const uint8_t* codes, const uint16_t* scales, const XSrc& 
 // bytes 4q..4q+3 (inputs 16q .. 16q+15 of the chunk); window w takes bytes
 // 4q + 2w, 4q + 2w + 1, whose x dwords are 8q + 4w .. + 3 of the chunk
 // (byte offset 128 ch + 32 q + 16 w of the token row).
-__device__ void run_i2(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int K, int G, int lane,
+// Group pairs [k0, k1) of the slab's rows (groups 2 k0 .. min(2 k1, G) - 1).
+__device__ void run_i2(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int k0, int k1, int G, int lane,
                        const uint8_t* lut, Acc& y) {
-  Scales sc(scales, G, lane);
-  const int nchunks = 2 * G;
+  const int g0 = 2 * k0, g1 = 2 * k1 < G ? 2 * k1 : G;
+  Scales sc(scales, g0, g1, lane);
+  const int nchunks = 2 * g1;
   const CodeDw src(codes, nchunks, lane);
   const int q = lane >> 4;
   const uint32_t lane_off = (uint32_t)(lane & 3) << 3;
@@ -301,18 +307,18 @@ __device__ void run_i2(const uint8_t* codes, const uint16_t* scales, const XSrc&
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) cd[s][rb] = src.load(s, rb);
+    for (int rb = 0; rb < kRB; ++rb) cd[s][rb] = src.load(2 * g0 + s, rb);
   // x of window wi (global: 2 ch + W) in slot wi % 4, three windows ahead
   u32x4_t xw[4];
   auto xoff2 = [&](int wi) __attribute__((always_inline)) { return (uint32_t)(128 * (wi >> 1) + 32 * q + 16 * (wi & 1)); };
 #pragma unroll
-  for (int i = 0; i < 3; ++i) xw[i] = xs.b128(xoff2(i));
+  for (int i = 0; i < 3; ++i) xw[i] = xs.b128(xoff2(4 * g0 + i));
   E2 ent[2];
   read(ent[0], cd[0], 0);
-  for (int gp = 0; gp < G; gp += 2) {  // two groups (4 chunks) per pass; an odd last one is dropped by flush
+  for (int k = k0; k < k1; ++k) {  // two groups (4 chunks) per pass; an odd last one is dropped by flush
     sfor<2>([&](auto s_) __attribute__((always_inline)) {
       constexpr int S = decltype(s_)::value;
-      const int g = gp + S;
+      const int g = 2 * k + S;
       Acc d;
       zero(d);
       sfor<2>([&](auto h_) __attribute__((always_inline)) {
@@ -347,10 +353,12 @@ __device__ void run_i2(const uint8_t* codes, const uint16_t* scales, const XSrc&
 // q of its row (three aligned dwords, each inside one chunk); window w takes
 // fields 4w .. 4w+3 (codes 32q + 8w ..), whose x dwords are 16q + 4w .. + 3
 // (byte offset 256 g + 64 q + 16 w of the token row).
-__device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int K, int G, int lane,
+// Group pairs [k0, k1) of the slab's rows (groups 2 k0 .. min(2 k1, G) - 1).
+__device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc& xs, int k0, int k1, int G, int lane,
                        const uint8_t* lut, Acc& y) {
-  Scales sc(scales, G, lane);
-  const int nchunks = 3 * G;
+  const int g0 = 2 * k0, g1 = 2 * k1 < G ? 2 * k1 : G;
+  Scales sc(scales, g0, g1, lane);
+  const int nchunks = 3 * g1;
   const CodeDw src(codes, nchunks, lane);
   const int q = lane >> 4;
   // the triple's three dwords: group-relative bytes 12 q + 4 j (each inside one chunk)
@@ -385,18 +393,18 @@ __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc&
     }
   };
   uint32_t tw[2][kRB][3];
-  load_tr(0, tw[0]);
+  load_tr(g0, tw[0]);
   // x of window wi (global: 4 g + W) in slot wi % 4, three windows ahead
   u32x4_t xw[4];
   auto xoff3 = [&](int wi) __attribute__((always_inline)) { return (uint32_t)(256 * (wi >> 2) + 64 * q + 16 * (wi & 3)); };
 #pragma unroll
-  for (int i = 0; i < 3; ++i) xw[i] = xs.b128(xoff3(i));
+  for (int i = 0; i < 3; ++i) xw[i] = xs.b128(xoff3(4 * g0 + i));
   E3 ent[2];
   read(ent[0], tw[0], std::integral_constant<int, 0>{});
-  for (int gp = 0; gp < G; gp += 2) {  // an odd last group runs past the row and is dropped by flush
+  for (int k = k0; k < k1; ++k) {  // an odd last group runs past the row and is dropped by flush
     sfor<2>([&](auto s_) __attribute__((always_inline)) {
       constexpr int S = decltype(s_)::value;
-      const int g = gp + S;
+      const int g = 2 * k + S;
       sched_fence();
       load_tr(g + 1, tw[S ^ 1]);
       Acc d;
@@ -420,30 +428,50 @@ __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc&
   }
 }
 
-// One task: one 64-row slab of one descriptor, all M tokens.
+// One task: one 64-row slab of one descriptor (or one part of its input when
+// the entry is split), all M tokens.
 __device__ __forceinline__ void mm_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t, int M,
-                                        const uint8_t* lut, int lane) {
+                                        const uint8_t* lut, int lane, uint32_t* state) {
   const ql_gemv_desc& d = descs[find_desc(descs, count, t)];
-  const int64_t slab = t - d.slab_begin;
+  const SplitTask st(d, t);
   const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
   int gr;
-  const int64_t off = slab_offset(slab, K, d.grid, d.blk_grid, d.blk_off, &gr);
+  const int64_t off = slab_offset(st.slab, K, d.grid, d.blk_grid, d.blk_off, &gr);
   const uint8_t* codes = static_cast<const uint8_t*>(d.packed) + off;
-  const uint16_t* scales = d.pscales + slab * (int64_t)G8 * kSlab * 8;
+  const uint16_t* scales = d.pscales + (int64_t)st.slab * G8 * kSlab * 8;
   const XSrc xs(d.x, M, K, lane);
   Acc y;
   zero(y);
   if (gr == QL_GRID_T)
-    run_t(codes, scales, xs, K, G, lane, lut, y);
+    run_t(codes, scales, xs, K, G, st.p0(K), st.p1(K), lane, lut, y);
   else if (gr == QL_GRID_I2)
-    run_i2(codes, scales, xs, K, G, lane, lut, y);
+    run_i2(codes, scales, xs, st.k0(K), st.k1(K), G, lane, lut, y);
   else
-    run_i3(codes, scales, xs, K, G, lane, lut, y);
-  // lane l: tokens 4q .. 4q+3 of weight row 16 rb + (l & 15)
+    run_i3(codes, scales, xs, st.k0(K), st.k1(K), G, lane, lut, y);
   const int q = lane >> 4;
+  if (st.split()) {
+    float* sl = st.slots(d, state);
+    // partial sum (rb, i) of lane l at word (4 rb + i) * 64 + l of the part's
+    // slot; lanes whose tokens are all past M hold nothing and skip the exchange
+    float v[4 * kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * rb + i] = y.v[rb][i];
+    if (4 * q < M)
+#pragma unroll
+      for (int j = 0; j < 4 * kRB; ++j) st.put(sl, 64 * j + lane, v[j]);
+    if (!st.arrive(st.counter(d, state), lane)) return;
+    if (4 * q < M) st.totals<4 * kRB, 4>(sl, v, lane);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y.v[rb][i] = v[4 * rb + i];
+  }
+  // lane l: tokens 4q .. 4q+3 of weight row 16 rb + (l & 15)
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const int64_t row = slab * kSlab + 16 * rb + (lane & 15);
+    const int64_t row = (int64_t)st.slab * kSlab + 16 * rb + (lane & 15);
     if (row < d.N)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -464,7 +492,7 @@ __global__ void __launch_bounds__(kMmWaves * 64, QL_MM_WAVES_PER_EU) gemv_mm_gro
   if (t >= total) t = tq.next(lane);
   while (t >= 0) {
     const uint32_t claim = tq.claim(lane);
-    mm_task(descs, count, t, M, lut, lane);
+    mm_task(descs, count, t, M, lut, lane, sched);
     t = tq.resolve(claim, lane);
   }
   tq.checkout(lane);
@@ -472,13 +500,15 @@ __global__ void __launch_bounds__(kMmWaves * 64, QL_MM_WAVES_PER_EU) gemv_mm_gro
 
 }  // namespace
 
-hipError_t launch_gemv_mm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M,
+int64_t mm_wave_slots() { return (int64_t)device_cu_count() * kMmWgPerCu * kMmWaves; }
+
+hipError_t launch_gemv_mm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
                                   uint32_t* sched, hipStream_t stream) {
   if (M < 2 || M > 16) return hipErrorInvalidValue;
   const int slots = device_cu_count() * kMmWgPerCu;
-  const int64_t wg_needed = (total_slabs + kMmWaves - 1) / kMmWaves;
+  const int64_t wg_needed = (total_tasks + kMmWaves - 1) / kMmWaves;
   const int grid = (int)(wg_needed < slots ? wg_needed : slots);
-  hipLaunchKernelGGL(gemv_mm_grouped_kernel, dim3(grid), dim3(kMmWaves * 64), 0, stream, descs, count, total_slabs, M,
+  hipLaunchKernelGGL(gemv_mm_grouped_kernel, dim3(grid), dim3(kMmWaves * 64), 0, stream, descs, count, total_tasks, M,
                      sched);
   return hipGetLastError();
 }

@@ -31,10 +31,10 @@ struct MatArgs {
 };
 
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
-hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M, uint32_t* sched,
+hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
                                hipStream_t stream);
 // 2 <= M <= 16: the batched-decode kernel (MFMA), same descriptors and scheduler state
-hipError_t launch_gemv_mm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, int M,
+hipError_t launch_gemv_mm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
                                   uint32_t* sched, hipStream_t stream);
 hipError_t launch_c4_gemv(const MatArgs& a, hipStream_t stream);
 hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, uint32_t* sched,
@@ -55,5 +55,8 @@ hipError_t launch_lb_pack(int64_t d_out, int64_t d_in, int64_t r, const int8_t* 
 hipError_t launch_lb_gemv(const ql_littlebit& w, const uint16_t* x, float* y, void* ws, hipStream_t stream);
 
 int device_cu_count();
+// waves of a persistent grouped launch at batch size M (1: batch-1 kernel, else batched)
+int64_t grouped_wave_slots(int M);
+int64_t mm_wave_slots();
 
 }  // namespace ql

@@ -150,6 +150,98 @@ __device__ __forceinline__ int find_desc(const ql_gemv_desc* __restrict__ descs,
   return lo;
 }
 
+// ---------------------------------------------------------------- split-K
+// qlinear_grouped_prepare_split may cut the input of every slab of an entry
+// into kparts parts, each a task of its own: whole 640-input periods on
+// ternary slabs, whole pairs of 128-input groups on 2- and 3-bit slabs
+// (kparts never exceeds the periods, so no part is empty).  The
+// entry's split state starts at word ws_begin of the launch's state buffer:
+// one counter per slab (each in its own 128-byte line), then kPartWords
+// partial sums per (slab, part).  A part stores its partial sums and counts
+// itself in; the wave that counts last sums the parts in part order, so the
+// result is the same bits whichever wave finishes last, and resets the counter
+// for the next launch.
+//
+// Partial sums travel as device-scope atomic stores and loads, which the
+// hardware keeps coherent across the XCDs' separate L2 caches by themselves
+// (they write through to, and read from, the device's coherence point).  The
+// counter increment is issued only once those stores are complete, and the
+// last wave's loads only once its increment has returned, so no device-scope
+// fence is needed: such a fence writes back (release) or invalidates (acquire)
+// a whole L2, and with one per task those cache operations serialized the
+// launch (measured: a 2688-task launch took 2.6x as long as its unsplit form).
+struct SplitTask {
+  uint32_t slab, part, parts;  // task indices stay below 2^31
+
+  __device__ __forceinline__ SplitTask(const ql_gemv_desc& d, int64_t t) {
+    parts = d.kparts > 1 ? (uint32_t)d.kparts : 1u;
+    const uint32_t local = (uint32_t)(t - d.slab_begin);
+    slab = local / parts;
+    part = local - slab * parts;
+  }
+  // ternary: periods [p0, p1) of the row
+  __device__ __forceinline__ int p0(int K) const { return (int)(part * (uint32_t)((K + kPeriodK - 1) / kPeriodK) / parts); }
+  __device__ __forceinline__ int p1(int K) const {
+    return (int)((part + 1) * (uint32_t)((K + kPeriodK - 1) / kPeriodK) / parts);
+  }
+  // 2- and 3-bit: group pairs [k0, k1) (groups 2 k0 .. min(2 k1, G) - 1), so
+  // that each part starts on an even group: the scale pairs and ring slots of
+  // the 2- and 3-bit drivers then have compile-time parity
+  __device__ __forceinline__ int k0(int K) const { return (int)(part * (uint32_t)((K / kGroup + 1) / 2) / parts); }
+  __device__ __forceinline__ int k1(int K) const {
+    return (int)((part + 1) * (uint32_t)((K / kGroup + 1) / 2) / parts);
+  }
+  __device__ __forceinline__ bool split() const { return __builtin_expect(parts > 1u, 0); }
+  // the slab's counter and partial sums (part q at q * kPartWords)
+  __device__ __forceinline__ uint32_t* counter(const ql_gemv_desc& d, uint32_t* state) const {
+    return state + d.ws_begin + (int64_t)slab * kCounterWords;
+  }
+  __device__ __forceinline__ float* slots(const ql_gemv_desc& d, uint32_t* state) const {
+    const int64_t nslabs = ((int64_t)d.N + kSlab - 1) / kSlab;
+    return reinterpret_cast<float*>(state + d.ws_begin + nslabs * kCounterWords) + (int64_t)slab * parts * kPartWords;
+  }
+  // partial-sum word w of this part
+  __device__ __forceinline__ void put(float* sl, int w, float v) const {
+    __hip_atomic_store(sl + part * kPartWords + w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // After this part's put()s: count the part in.  True (wave-uniform) in the
+  // wave whose part completes the slab.
+  __device__ __forceinline__ bool arrive(uint32_t* cnt, int lane) const {
+    // this wave's stores complete before the increment is issued (the memory
+    // clobber also keeps the compiler from moving them past it)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != parts - 1u) return false;
+    asm volatile("" ::: "memory");  // the loads of totals() stay below the increment
+    if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  // Last wave only: acc[j] = sum over the parts, in part order, of partial-sum
+  // word 64 j + lane.  The loads of B parts are issued together, so the sum
+  // costs about parts / B memory round trips.
+  template <int NW, int B>
+  __device__ __forceinline__ void totals(const float* sl, float (&acc)[NW], int lane) const {
+    for (int q0 = 0; q0 < (int)parts; q0 += B) {
+      float v[B][NW];
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+          v[b][j] = q0 + b < (int)parts
+                        ? __hip_atomic_load(sl + (q0 + b) * kPartWords + 64 * j + lane, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : 0.0f;
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+          if (q0 + b < (int)parts) acc[j] = q0 + b == 0 ? v[b][j] : acc[j] + v[b][j];
+    }
+  }
+};
+
 // ---------------------------------------------------------------- task queues
 // Persistent grouped launches run tasks 0..total-1, numbered by the host
 // longest first.  Wave w of the launch takes task w; the rest, r = t - nwaves,
@@ -164,7 +256,8 @@ __device__ __forceinline__ int find_desc(const ql_gemv_desc* __restrict__ descs,
 // the draw that follows then fails and the wave reads again.
 constexpr int kQueues = 64;         // one per lane of the scan
 constexpr int kQueueStride = 32;    // words between counters (128 bytes)
-constexpr int kSchedDone = kQueues * kQueueStride;  // check-out word
+constexpr int kLineBase = kQueues * kQueueStride;      // check-out counter of home h at kLineBase + h * kQueueStride
+constexpr int kSchedDone = 2 * kQueues * kQueueStride;  // check-out word
 static_assert(kSchedDone + 1 <= QL_SCHED_WORDS, "scheduler state larger than QL_SCHED_WORDS");
 
 struct TaskQueues {
@@ -209,13 +302,28 @@ struct TaskQueues {
     if (t < qcount(home)) return nwaves + home + (int64_t)t * kQueues;
     return next(lane);
   }
-  // every wave checks out once; the last one zeroes the state for the next launch
+  // Every wave checks out once, after its last draw; the last one zeroes the
+  // state for the next launch.  Check-out is two-level so that no address takes
+  // one atomic per wave (thousands of them, serialized at the end of the
+  // launch): a wave counts itself in on the check-out line of its workgroup's
+  // first home queue (one 128-byte line per home, apart from the queue lines);
+  // the wave completing a line counts the line in on the check-out word, and
+  // the wave completing that resets every counter.
   __device__ void checkout(int lane) {
+    const int h = (int)(blockIdx.x % kQueues);
+    const int wgs = (int)gridDim.x;
+    const uint32_t line_waves = (uint32_t)(((wgs - 1 - h) / kQueues + 1) * (nwaves / wgs));
+    const uint32_t lines = (uint32_t)(wgs < kQueues ? wgs : kQueues);
+    uint32_t c = 0;
+    if (lane == 0) c = __hip_atomic_fetch_add(sched + kLineBase + h * kQueueStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    c = __builtin_amdgcn_readfirstlane(c);
+    if (c != line_waves - 1) return;
     uint32_t done = 0;
     if (lane == 0) done = __hip_atomic_fetch_add(sched + kSchedDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     done = __builtin_amdgcn_readfirstlane(done);
-    if (done == (uint32_t)(nwaves - 1)) {
+    if (done == lines - 1) {
       __hip_atomic_store(sched + lane * kQueueStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sched + kLineBase + lane * kQueueStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (lane == 0) __hip_atomic_store(sched + kSchedDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

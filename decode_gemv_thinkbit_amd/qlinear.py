@@ -18,7 +18,8 @@ import torch
 GRID_T, GRID_I2, GRID_I3, GRID_MIXED = 0, 1, 2, 3
 GRID_C4 = 4  # 4-bit container baseline (not a ThinkBit grid)
 GROUP, SLAB, BLOCK = 128, 64, 128
-QL_SCHED_WORDS = 2080  # uint32 words of grouped-launch scheduler state
+QL_SCHED_WORDS = 4128  # uint32 words of grouped-launch scheduler state
+QL_MAX_KPARTS = 16  # split-K parts per slab at most
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "libqlinear.so")
@@ -34,7 +35,8 @@ class ql_gemv_desc(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("pscales", ctypes.c_void_p), ("blk_grid", ctypes.c_void_p),
                 ("blk_off", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("slab_begin", ctypes.c_int32)]
+                ("slab_begin", ctypes.c_int32), ("kparts", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ws_begin", ctypes.c_int64)]
 
 
 class ql_alloc_unit(ctypes.Structure):
@@ -74,6 +76,10 @@ def lib():
         L.qlinear_gemv.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
         L.qlinear_grouped_prepare.argtypes = [vp, ctypes.c_int32]
         L.qlinear_grouped_prepare.restype = i64
+        L.qlinear_grouped_prepare_split.argtypes = [vp, ctypes.c_int32, i64, ctypes.POINTER(i64)]
+        L.qlinear_grouped_prepare_split.restype = i64
+        L.qlinear_grouped_wave_slots.argtypes = [ctypes.c_int32]
+        L.qlinear_grouped_wave_slots.restype = i64
         L.qlinear_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp, vp]
         L.qlinear_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.qlinear_gemm_workspace_bytes.restype = sz
@@ -440,21 +446,44 @@ def gemm(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor] = None,
     return out
 
 
+def wave_slots(M=1):
+    """Waves of a persistent grouped launch at batch size M on the current device."""
+    n = lib().qlinear_grouped_wave_slots(M)
+    if n < 0:
+        _check(1, "grouped_wave_slots")
+    return int(n)
+
+
 class GroupedGemv:
     """One persistent launch over many independent (x, W, y) products with the same M."""
 
-    def __init__(self, items):
-        """items: list of (PackedWeight or C4Weight, x [M,K] bf16, y [M,N] fp32); all of one kind."""
+    def __init__(self, items, split=None):
+        """items: list of (PackedWeight or C4Weight, x [M,K] bf16, y [M,N] fp32); all of one kind.
+
+        split: None (one task per 64-row slab), "auto" (cut the slabs' input into parts until
+        the launch has twice as many tasks as the device has wave slots, where rows allow),
+        an int (that many parts for every item) or a list of ints (parts per item; 0 = auto)."""
         if not items:
             raise ValueError("no items")
         self.items = items
         self.M = items[0][1].shape[0] if items[0][1].dim() == 2 else 1
         self.containers = isinstance(items[0][0], C4Weight)
+        if isinstance(split, (list, tuple)):
+            if len(split) != len(items):
+                raise ValueError("split: one entry per item")
+            parts = [int(v) for v in split]
+        elif isinstance(split, int) and not isinstance(split, bool):
+            parts = [split] * len(items)
+        elif split in (None, "auto"):
+            parts = [0] * len(items)
+        else:
+            raise ValueError(f"split: {split!r}")
         arr = (ql_gemv_desc * len(items))()
-        # heaviest slabs first (qlinear_grouped_prepare then orders by row length, stably):
+        # heaviest slabs first (prepare then orders by task length, stably):
         # the launch ends on the cheapest tasks, which shortens its tail
         order = sorted(range(len(items)), key=lambda j: -items[j][0].nbytes / ((items[j][0].N + 63) // 64))
-        for i, (pw, x, y) in enumerate(items[j] for j in order):
+        for i, j in enumerate(order):
+            pw, x, y = items[j]
             if isinstance(pw, C4Weight) != self.containers:
                 raise ValueError("a grouped launch takes either containers or packed weights, not both")
             _dev(x, torch.bfloat16, "x")
@@ -464,21 +493,32 @@ class GroupedGemv:
                 raise ValueError(f"item {i}: shapes do not match")
             if self.containers:
                 arr[i] = ql_gemv_desc(pw.c4.data_ptr(), pw.pscales.data_ptr(), None, None, x.data_ptr(),
-                                      y.data_ptr(), pw.N, pw.K, GRID_C4, 0)
+                                      y.data_ptr(), pw.N, pw.K, GRID_C4, 0, parts[j], 0, 0)
             else:
                 arr[i] = ql_gemv_desc(pw.packed.data_ptr(), pw.pscales.data_ptr(),
                                       pw.blk_grid.data_ptr() if pw.blk_grid is not None else None,
                                       pw.blk_off.data_ptr() if pw.blk_off is not None else None,
-                                      x.data_ptr(), y.data_ptr(), pw.N, pw.K, pw.grid, 0)
-        total = lib().qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(items))
+                                      x.data_ptr(), y.data_ptr(), pw.N, pw.K, pw.grid, 0, parts[j], 0, 0)
+        if split is None:
+            total = lib().qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(items))
+            words = QL_SCHED_WORDS
+        else:
+            min_tasks = 2 * wave_slots(self.M) if any(v == 0 for v in parts) else 0
+            w = ctypes.c_int64(0)
+            total = lib().qlinear_grouped_prepare_split(ctypes.cast(arr, ctypes.c_void_p), len(items), min_tasks,
+                                                        ctypes.byref(w))
+            words = int(w.value)
         if total < 0:
             _check(1, "grouped_prepare")
         self.total = int(total)
+        self.kparts = [int(arr[i].kparts) for i in range(len(items))]  # in launch order
+        self.plan = [{"N": int(d.N), "K": int(d.K), "kparts": int(d.kparts), "ws_begin": int(d.ws_begin),
+                      "slab_begin": int(d.slab_begin)} for d in arr]
         raw = bytes(memoryview(arr))
         self.count = len(items)
         self.descs = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(items[0][1].device)
-        # task-counter state: zero once here, left zero by every completed launch
-        self.sched = torch.zeros(QL_SCHED_WORDS, dtype=torch.int32, device=items[0][1].device)
+        # task counters and split state: zero once here, counters left zero by every completed launch
+        self.sched = torch.zeros(words, dtype=torch.int32, device=items[0][1].device)
 
     def run(self):
         fn = lib().qlinear_c4_gemv_grouped if self.containers else lib().qlinear_gemv_grouped

@@ -153,7 +153,12 @@ typedef struct {
   const uint16_t *x;        /* (dev) bf16 bits [M][K] */
   float *y;                 /* (dev) fp32 [M][N] */
   int32_t N, K, grid;       /* shape and grid (QL_GRID_*) */
-  int32_t slab_begin;       /* filled by qlinear_grouped_prepare */
+  int32_t slab_begin;       /* filled by prepare: the entry's first task */
+  int32_t kparts;           /* split-K parts per slab: in (prepare_split), 0 = choose, else forced;
+                               out, the parts used (1 = no split) */
+  int32_t reserved;         /* 0 */
+  int64_t ws_begin;         /* filled by prepare: first word of the entry's split-K state in the
+                               launch's state buffer (0 when kparts == 1) */
 } ql_gemv_desc;
 
 /* Prepare a descriptor list (host array) for qlinear_gemv_grouped (or, for a list of 4-bit
@@ -167,10 +172,33 @@ typedef struct {
  * its cheapest tasks. */
 int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
 
-/* Words of the task-scheduler state of a grouped launch: 64 task-queue counters, each in its
- * own 128-byte line, and a check-out word.  Draws spread over many counters because atomics
- * on one shared address serialize across the whole device. */
-#define QL_SCHED_WORDS 2080
+/* Largest number of split-K parts per slab (the last part's wave sums every part). */
+#define QL_MAX_KPARTS 16
+
+/* Split-K for launches with few slabs (one matrix, or the few of one layer: a 4096-row
+ * matrix has 64 slabs, one per wave, on a device with thousands of wave slots).  As
+ * qlinear_grouped_prepare, but the input of every slab may be cut into kparts parts of
+ * whole 640-input periods, each part a task of its own; the wave that finishes a slab's
+ * last part sums the parts' fp32 partial sums in part order, so results stay bitwise
+ * deterministic.  An entry with kparts > 0 keeps that many parts (at most its period
+ * count and QL_MAX_KPARTS); for kparts == 0 the parts are chosen so that the launch has
+ * at least min_tasks tasks where rows allow (e.g. twice qlinear_grouped_wave_slots(M);
+ * min_tasks <= 0 splits nothing).  Tasks are ordered by part length, longest first.  A list of 4-bit containers
+ * is never split.  *state_words (host) receives the size of the launch's state buffer in
+ * 32-bit words: QL_SCHED_WORDS, plus, per split entry, one 128-byte counter line per slab
+ * and 1024 words of partial sums per part of each slab.  Returns the task count, or -1. */
+int64_t qlinear_grouped_prepare_split(ql_gemv_desc *descs, int32_t count, int64_t min_tasks,
+                                      int64_t *state_words);
+
+/* Waves a grouped launch at batch size M (1..16) runs on the current device at most (the
+ * persistent grid), or -1 if M is out of range or the device cannot be queried. */
+int64_t qlinear_grouped_wave_slots(int32_t M);
+
+/* Words of the task-scheduler state of a grouped launch: 64 task-queue counters and 64
+ * check-out counters, each in its own 128-byte line, and a check-out word.  Draws and
+ * check-outs spread over many counters because atomics on one shared address serialize
+ * across the whole device. */
+#define QL_SCHED_WORDS 4128
 
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
  * descs (dev), count entries) in one persistent launch, at one batch size M for all entries
@@ -178,13 +206,15 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
  * 2 <= M <= 16 the batched-decode kernel, which decodes each packed byte once and runs the
  * M-token products on MFMA (products exact, fp32 sums; summary page, section "What it is":
  * a decode step at a small batch still streams every weight once).  M outside 1..16 returns
- * QL_EINVAL.  Waves take 64-row slab tasks from atomic queue counters in `sched`
- * (dev, QL_SCHED_WORDS uint32, 16-byte aligned, owned by the caller): it must be all
- * zero when a launch starts, and every launch that runs to completion leaves it zero
- * again, so one zeroing at allocation serves any number of launches.  Launches that
- * share one sched buffer must not overlap (enqueue them on one stream).  The products
- * are independent: no y may alias another entry's x or y. */
-ql_status qlinear_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_slabs, int32_t M,
+ * QL_EINVAL.  Waves take tasks (64-row slabs, or parts of them after prepare_split) from
+ * atomic queue counters in the state buffer `sched` (dev, 16-byte aligned, owned by the
+ * caller; QL_SCHED_WORDS uint32 after qlinear_grouped_prepare, the state_words reported by
+ * qlinear_grouped_prepare_split otherwise): its counters must be all zero when a launch
+ * starts, and every launch that runs to completion leaves them zero again, so one zeroing
+ * at allocation serves any number of launches.  Launches that share one state buffer must
+ * not overlap (enqueue them on one stream).  The products are independent: no y may alias
+ * another entry's x or y. */
+ql_status qlinear_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_tasks, int32_t M,
                                uint32_t *sched, hipStream_t stream);
 
 /* Batched GEMM for 1 <= M (tuned for 16..512): tiles of codes are decoded into LDS as bf16

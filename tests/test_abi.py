@@ -142,3 +142,96 @@ def test_grouped_prepare_rejects_mixed_container_lists():
     arr[1] = ql.ql_gemv_desc(16, 32, None, None, 48, 64, 64, 256, ql.GRID_C4, 0)
     assert L.qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), 2) == 2
     assert arr[0].K == 256 and arr[0].slab_begin == 0 and arr[1].slab_begin == 1
+
+
+def _descs(shapes, parts):
+    arr = (ql.ql_gemv_desc * len(shapes))()
+    for i, ((N, K, g), p) in enumerate(zip(shapes, parts)):
+        arr[i] = ql.ql_gemv_desc(FAKE, FAKE, None, None, FAKE, FAKE, N, K, g, -1, p, 7, 99)
+    return arr
+
+
+def test_grouped_prepare_split_plans_parts_and_state():
+    """Split plan: parts per slab (forced, clamped to the row's 640-input periods, or enough
+    for min_tasks), task order by part length, task numbering, and the state layout: the
+    queue words, then per split entry one 32-word counter line per slab and 1024 words of
+    partial sums per (slab, part)."""
+    L = ql.lib()
+    shapes = [(4096, 4096, 0), (1024, 4096, 2), (100, 128, 1), (4096, 12288, 0), (130, 5120, 1)]
+    arr = _descs(shapes, [0, 3, 0, 0, 50])
+    words = ctypes.c_int64(-1)
+    slabs = [(n + 63) // 64 for n, _, _ in shapes]
+    min_tasks = 4096
+    total = L.qlinear_grouped_prepare_split(ctypes.cast(arr, ctypes.c_void_p), len(shapes), min_tasks,
+                                            ctypes.byref(words))
+    need = -(-min_tasks // sum(slabs))
+    periods = {K: -(-K // 640) for _, K, _ in shapes}
+    cap = ql.QL_MAX_KPARTS
+    want = {(4096, 4096, 0): min(need, 7, cap), (1024, 4096, 2): 3, (100, 128, 1): 1,
+            (4096, 12288, 0): min(need, 20, cap), (130, 5120, 1): 8}
+    got = {(d.N, d.K, d.grid): d.kparts for d in arr}
+    assert got == want
+    assert all(1 <= d.kparts <= min(periods[d.K], cap) for d in arr)
+    # longest parts first (K / kparts), stable
+    keys = [d.K / d.kparts for d in arr]
+    assert keys == sorted(keys, reverse=True)
+    ntask = [((d.N + 63) // 64) * d.kparts for d in arr]
+    assert [d.slab_begin for d in arr] == list(np.cumsum([0] + ntask)[:-1])
+    assert total == sum(ntask)
+    w = (ql.QL_SCHED_WORDS + 63) // 64 * 64
+    for d in arr:
+        assert d.reserved == 0
+        if d.kparts == 1:
+            assert d.ws_begin == 0
+            continue
+        ns = (d.N + 63) // 64
+        assert d.ws_begin == w
+        w += ns * 32 + ns * d.kparts * 1024
+    assert words.value == w
+
+
+def test_grouped_prepare_split_without_split_matches_prepare():
+    L = ql.lib()
+    shapes = [(100, 4096, 0), (64, 12288, 1), (300, 4096, 2), (1, 128, 0)]
+    a, b = _descs(shapes, [0] * 4), _descs(shapes, [0] * 4)
+    words = ctypes.c_int64(-1)
+    ta = L.qlinear_grouped_prepare(ctypes.cast(a, ctypes.c_void_p), 4)
+    tb = L.qlinear_grouped_prepare_split(ctypes.cast(b, ctypes.c_void_p), 4, 0, ctypes.byref(words))
+    assert ta == tb == sum((n + 63) // 64 for n, _, _ in shapes)
+    assert words.value == ql.QL_SCHED_WORDS
+    assert bytes(memoryview(a)) == bytes(memoryview(b))
+    assert all(d.kparts == 1 and d.ws_begin == 0 for d in a)
+    # plain prepare ignores requested parts
+    c = _descs(shapes, [5] * 4)
+    assert L.qlinear_grouped_prepare(ctypes.cast(c, ctypes.c_void_p), 4) == ta
+    assert all(d.kparts == 1 for d in c)
+
+
+def test_grouped_prepare_split_rejects_bad_parts_and_split_containers():
+    L = ql.lib()
+    words = ctypes.c_int64(-1)
+    arr = _descs([(64, 256, 0)], [-1])
+    assert L.qlinear_grouped_prepare_split(ctypes.cast(arr, ctypes.c_void_p), 1, 0, ctypes.byref(words)) == -1
+    arr = _descs([(64, 1280, ql.GRID_C4), (64, 1280, ql.GRID_C4)], [2, 0])
+    assert L.qlinear_grouped_prepare_split(ctypes.cast(arr, ctypes.c_void_p), 2, 0, ctypes.byref(words)) == -1
+    assert b"not split" in L.qlinear_last_error()
+    arr = _descs([(64, 1280, ql.GRID_C4), (64, 1280, ql.GRID_C4)], [0, 0])
+    assert L.qlinear_grouped_prepare_split(ctypes.cast(arr, ctypes.c_void_p), 2, 10 ** 6, ctypes.byref(words)) == 2
+    assert all(d.kparts == 1 for d in arr) and words.value == ql.QL_SCHED_WORDS
+
+
+def test_split_periods_tile_every_row():
+    """The device's part ranges, p0 = part * P // parts .. (part + 1) * P // parts, tile
+    [0, P) with no empty part for every parts <= P."""
+    for P in range(1, 40):
+        for parts in range(1, P + 1):
+            r = [(q * P // parts, (q + 1) * P // parts) for q in range(parts)]
+            assert r[0][0] == 0 and r[-1][1] == P
+            assert all(a < b for a, b in r) and all(r[i][1] == r[i + 1][0] for i in range(parts - 1))
+
+
+def test_wave_slots_query():
+    L = ql.lib()
+    assert L.qlinear_grouped_wave_slots(0) == -1 and L.qlinear_grouped_wave_slots(17) == -1
+    n1, n4 = L.qlinear_grouped_wave_slots(1), L.qlinear_grouped_wave_slots(4)
+    assert n1 > 0 and n4 > 0 and n1 % 16 == 0 and n4 % 12 == 0
