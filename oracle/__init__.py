@@ -72,6 +72,8 @@ def lib():
         L.ora_dequant.restype = None
         L.ora_gemv.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
         L.ora_gemv.restype = None
+        L.ora_gemv_w16.argtypes = [i64, i64, i64, vp, vp, vp, vp, i32]
+        L.ora_gemv_w16.restype = None
         L.ora_c4_bytes.argtypes = [i64, i64]
         L.ora_c4_bytes.restype = i64
         L.ora_c4_pack.argtypes = [i64, i64, vp, vp]
@@ -258,6 +260,20 @@ def gemv(codes: np.ndarray, scales: np.ndarray, x_bf16: np.ndarray, threads: int
     assert x.shape[1] == K
     y = np.empty((M, N), dtype=np.float64)
     lib().ora_gemv(M, N, K, _p(codes), _p(scales), _p(x), _p(y), threads or (os.cpu_count() or 1))
+    return y
+
+
+def gemv_w16(codes: np.ndarray, scales: np.ndarray, x_bf16: np.ndarray, threads: int = 0) -> np.ndarray:
+    """y [M][N] = sum_k bf16_rne(c*s)[n,k] * x[m,k] in fp64 (ascending k): the product with
+    weights dequantized to bf16, equal to gemv wherever c*s is a bf16 value."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    x = np.ascontiguousarray(np.atleast_2d(x_bf16), dtype=np.uint16)
+    N, K = codes.shape
+    M = x.shape[0]
+    assert x.shape[1] == K
+    y = np.empty((M, N), dtype=np.float64)
+    lib().ora_gemv_w16(M, N, K, _p(codes), _p(scales), _p(x), _p(y), threads or (os.cpu_count() or 1))
     return y
 
 

@@ -395,6 +395,31 @@ void ora_gemv(int64_t M, int64_t N, int64_t K, const int8_t* codes, const uint16
   });
 }
 
+// The product with bf16-rounded weights: y[m][n] = sum_k w16[n][k] * x[m][k]
+// with w16 = bf16_rne(c*s), fp64 products and sum in ascending k.  This is
+// what a matrix-core path computes when it dequantizes to bf16 before the
+// contraction (k-quant calibration page, section "Not just any noise": that
+// reproduces the native low-bit result); it differs from ora_gemv only where
+// c*s is not a bf16 value (3-bit codes of magnitude 3).
+void ora_gemv_w16(int64_t M, int64_t N, int64_t K, const int8_t* codes, const uint16_t* scales, const uint16_t* x,
+                  double* y, int nthreads) {
+  const int64_t G = K / kGroup;
+  std::vector<double> xd(M * K);
+  for (int64_t i = 0; i < M * K; ++i) xd[i] = (double)bf16_to_f32(x[i]);
+  parallel_rows(N, nthreads, [&](int64_t lo, int64_t hi) {
+    std::vector<double> w(K);
+    for (int64_t n = lo; n < hi; ++n) {
+      for (int64_t k = 0; k < K; ++k)
+        w[k] = (double)bf16_to_f32(bf16_rne((float)codes[n * K + k] * bf16_to_f32(scales[n * G + k / kGroup])));
+      for (int64_t m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += w[k] * xd[m * K + k];
+        y[m * N + n] = acc;
+      }
+    }
+  });
+}
+
 // The same product read from packed buffers (decode each row with this
 // file's own unpacker, then as ora_gemv).  Returns -2 on a corrupt byte.
 int ora_gemv_packed(int64_t M, int64_t N, int64_t K, const int8_t* blk_grid, const uint8_t* packed,

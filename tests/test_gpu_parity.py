@@ -149,6 +149,24 @@ def test_gemm_parity(ora, dev, N, K, grid, M):
     assert normwise <= TRIP_GEMM, normwise
 
 
+BIG_GEMM_CASES = [(64, 128, 128), (129, 1280, 200), (1000, 4096, 128), (70, 384, 384), (256, 5120, 256),
+                  (520, 1920, 130), (300, 12288, 128)]
+
+
+@pytest.mark.parametrize("N,K,M", BIG_GEMM_CASES)
+@pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
+def test_gemm_large_batch_parity(ora, dev, N, K, M, grid):
+    """Batches of 128 tokens and more: ragged token tiles (M = 130, 200), rows past N,
+    mixed grid blocks, long rows and K splits; every product exact, fp32 sums."""
+    note(f"gemm large batch N={N} K={K} grid={grid} M={M}")
+    pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=N * 5 + K + M)
+    y = ql.gemm(x, pw)
+    torch.cuda.synchronize()
+    err, normwise = ora.rel_err(y.cpu().numpy(), y64)
+    assert err <= GEMM_TOL, (err, normwise)
+    assert normwise <= TRIP_GEMM, normwise
+
+
 def test_grouped_gemv_parity(ora, dev):
     note("grouped gemv")
     cases = [(256, 4096, "mixed"), (1024, 4096, I3), (128, 12288, T), (3, 640, I2), (1000, 2048, T)]

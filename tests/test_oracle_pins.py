@@ -414,6 +414,57 @@ def test_gemv_packed_equals_gemv_and_thread_count_free(ora):
     assert np.array_equal(y1, y8) and np.array_equal(y1, yp)
 
 
+def test_gemv_w16_exact_rational_sum(ora):
+    """The bf16-weight product is the fp64 sum of bf16_rne(c*s) * x (w16 itself is pinned
+    to torch's bf16 rounding by test_dequant_exact), within the fp64 summation bound."""
+    W = synth.weight(4, 256, seed=18).numpy()
+    for grid in (T, I2, I3):
+        c, s = ora.quantize(W, grid)
+        x = synth.bf16_bits(synth.activations(2, 256, seed=19))
+        y = ora.gemv_w16(c, s, x, threads=1)
+        _, w16 = ora.dequant(c, s)
+        wf = f32_of_bf16(w16)
+        xf = f32_of_bf16(x)
+        for m in range(2):
+            for n in range(4):
+                terms = [Fraction(float(wf[n, k])) * Fraction(float(xf[m, k])) for k in range(256)]
+                bound = 256 * 2.0 ** -53 * float(sum(abs(t) for t in terms)) * 1.01
+                assert abs(float(Fraction(y[m, n]) - sum(terms))) <= bound
+
+
+def test_gemv_w16_differs_only_at_codes_of_magnitude_three(ora):
+    """bf16_rne(c*s) == c*s unless |c| = 3 (c*s then needs up to two more significant bits), so
+    ternary and 2-bit rows agree bit for bit with gemv, and 3-bit rows do once the codes of
+    magnitude 3 are removed; with them the difference stays within 2^-9 of each such term."""
+    N, K = 64, 512
+    W = synth.weight(N, K, seed=20).numpy()
+    x = synth.bf16_bits(synth.activations(3, K, seed=21))
+    for grid in (T, I2):
+        c, s = ora.quantize(W, grid)
+        assert np.array_equal(ora.gemv_w16(c, s, x), ora.gemv(c, s, x))
+    c, s = ora.quantize(W, I3)
+    assert (np.abs(c) == 3).any()
+    c0 = np.where(np.abs(c) == 3, 0, c).astype(np.int8)
+    assert np.array_equal(ora.gemv_w16(c0, s, x), ora.gemv(c0, s, x))
+    w32, _ = ora.dequant(c, s)
+    xf = f32_of_bf16(x).astype(np.float64)
+    bound = (np.abs(c) == 3) * np.abs(w32.astype(np.float64)) * 2.0 ** -9
+    d = np.abs(ora.gemv_w16(c, s, x) - ora.gemv(c, s, x))
+    assert np.all(d <= np.abs(xf) @ bound.T * 1.0001 + 1e-300)
+    assert d.max() > 0  # the rounding is real
+
+
+def test_gemv_w16_one_hot_column(ora):
+    W = synth.weight(7, 384, seed=22).numpy()
+    c, s = ora.quantize(W, I3)
+    _, w16 = ora.dequant(c, s)
+    one = ora.f32_to_bf16(np.ones(1, np.float32))[0]
+    for k in (0, 5, 127, 128, 300, 383):
+        x = np.zeros((1, 384), np.uint16)
+        x[0, k] = one
+        assert np.array_equal(ora.gemv_w16(c, s, x)[0], f32_of_bf16(w16[:, k]).astype(np.float64))
+
+
 def test_rel_err_definition(ora):
     y64 = np.array([[3.0, 4.0], [0.0, 1.0]])
     yg = np.array([[3.0, 4.5], [0.0, 1.0]])
