@@ -164,8 +164,8 @@ def layered_leg(dev, warmup, steps, wl_name="qwen3_8b_pass", Ms=(1, 4)):
     (q, k, v on the attention input; o; gate, up on the MLP input; down), 144 launches for the
     36-layer pass, captured in one HIP graph and replayed.  A launch of one layer holds far
     fewer 64-row slabs than the device has wave slots, so it runs once with split-K (each
-    slab's input cut into parts of 640-input periods until the launch has twice as many
-    tasks as wave slots) and once without.  Same stored bytes, weights and grids as the
+    slab's input cut into parts until the launch has half as many tasks as wave slots) and
+    once without.  Same stored bytes, weights and grids as the
     single grouped launch."""
     import torch
     from decode_gemv_thinkbit_amd import configs

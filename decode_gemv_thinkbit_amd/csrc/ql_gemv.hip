@@ -518,7 +518,7 @@ __device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs
 template <int M>
 __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_kernel(ql_gemv_desc desc, int count, int64_t total, int Mact) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  build_luts(lut);
+  build_luts<kWaves * 64>(lut);
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -538,7 +538,7 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_ker
                                                                       int count, int64_t total, int Mact,
                                                                       uint32_t* __restrict__ sched) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  build_luts(lut);
+  build_luts<kWaves * 64>(lut);
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;

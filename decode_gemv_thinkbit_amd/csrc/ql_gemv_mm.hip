@@ -483,7 +483,7 @@ __global__ void __launch_bounds__(kMmWaves * 64, QL_MM_WAVES_PER_EU) gemv_mm_gro
                                                                          int count, int64_t total, int M,
                                                                          uint32_t* __restrict__ sched) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  build_luts(lut);
+  build_luts<kMmWaves * 64>(lut);
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;

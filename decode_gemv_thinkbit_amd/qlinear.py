@@ -461,7 +461,8 @@ class GroupedGemv:
         """items: list of (PackedWeight or C4Weight, x [M,K] bf16, y [M,N] fp32); all of one kind.
 
         split: None (one task per 64-row slab), "auto" (cut the slabs' input into parts until
-        the launch has twice as many tasks as the device has wave slots, where rows allow),
+        the launch has half as many tasks as the device has wave slots, where rows allow: the
+        best measured point for the per-layer launches of the 8B pass at M = 1 and 4),
         an int (that many parts for every item) or a list of ints (parts per item; 0 = auto)."""
         if not items:
             raise ValueError("no items")
@@ -503,7 +504,7 @@ class GroupedGemv:
             total = lib().qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(items))
             words = QL_SCHED_WORDS
         else:
-            min_tasks = 2 * wave_slots(self.M) if any(v == 0 for v in parts) else 0
+            min_tasks = wave_slots(self.M) // 2 if any(v == 0 for v in parts) else 0
             w = ctypes.c_int64(0)
             total = lib().qlinear_grouped_prepare_split(ctypes.cast(arr, ctypes.c_void_p), len(items), min_tasks,
                                                         ctypes.byref(w))

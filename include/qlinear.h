@@ -182,7 +182,7 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
  * last part sums the parts' fp32 partial sums in part order, so results stay bitwise
  * deterministic.  An entry with kparts > 0 keeps that many parts (at most its period
  * count and QL_MAX_KPARTS); for kparts == 0 the parts are chosen so that the launch has
- * at least min_tasks tasks where rows allow (e.g. twice qlinear_grouped_wave_slots(M);
+ * at least min_tasks tasks where rows allow (e.g. half of qlinear_grouped_wave_slots(M);
  * min_tasks <= 0 splits nothing).  Tasks are ordered by part length, longest first.  A list of 4-bit containers
  * is never split.  *state_words (host) receives the size of the launch's state buffer in
  * 32-bit words: QL_SCHED_WORDS, plus, per split entry, one 128-byte counter line per slab
