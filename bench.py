@@ -8,8 +8,9 @@ codes, scales, activations) are resident in HBM before the timed region.
 
 Prints one JSON line: packed-weight GB/s of the pass (stored code + scale
 bytes / time per pass), microseconds per pass, the roofline of the GEMV
-kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed on a bounded
-sample of the same workload.  A "gemm" object adds the batched path on one
+kernel against MI355X's 8 TB/s HBM peak, the measured read ceiling (the
+library's pure read probe over a buffer of the pass's size) and the GEMV's
+share of it, and the CPU oracle timed on a bounded sample of the same workload.  A "gemm" object adds the batched path on one
 Qwen3-8B-shaped layer (mixed grids, M = 64 / 256 / 512): microseconds per layer
 and MFMA utilisation against the dense bf16 peak; "batched" runs the Qwen3-14B
 stack and the 8B pass at decode batches M = 4 and 16 (grouped launch, batched-decode
@@ -226,6 +227,37 @@ def layered_leg(dev, warmup, steps, wl_name="qwen3_8b_pass", Ms=(1, 4)):
     torch.cuda.empty_cache()
     return {"variant": "dependency-respecting: 4 grouped launches per layer in one HIP graph",
             "kernels": "gemv_grouped_kernel<1> (M = 1), gemv_mm_grouped_kernel (M > 1)", "points": out}
+
+
+def read_ceiling(dev, nbytes, warmup, steps):
+    """The measured HBM read ceiling: the library's pure read probe over a buffer the size of the
+    pass (HIP events per launch, median), next to the nominal 8 TB/s."""
+    import torch
+    from decode_gemv_thinkbit_amd import qlinear as ql
+
+    nbytes = (nbytes + 1023) // 1024 * 1024
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.zeros(256, dtype=torch.int32, device=dev)
+    for _ in range(warmup):
+        ql.read_probe(buf, out)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ts = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        ql.read_probe(buf, out)
+        b.record(st)
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ts)
+    med = us[len(us) // 2]
+    gbs = nbytes / (med * 1e-6) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "read_probe_kernel (1 KB blocks interleaved over 8 waves per CU, 128-bit non-temporal loads)",
+            "bytes": nbytes, "median_us": round(med, 2), "gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 
 def container_ab(wl_name, dev, warmup, steps, native=None):
@@ -608,6 +640,11 @@ def main():
                           "traffic_source": traffic_src, "kernel_sources_sha256": kernel_source_hash(),
                           "kernel": "gemv_grouped_kernel<1>", "algorithmic_bytes": alg,
                           "avg_kernel_us": round(avg_kern_ms * 1e3, 2)}
+    rc = read_ceiling(dev, stored, args.warmup, args.steps)
+    rc["gemv_pct_of_ceiling"] = round(100 * ach / rc["gbs"], 2)
+    result["read_ceiling"] = rc
+    log(f"read probe: {rc['gbs']:.0f} GB/s ({rc['pct_hbm_peak']:.1f} % of 8 TB/s); "
+        f"GEMV at {rc['gemv_pct_of_ceiling']:.1f} % of it")
     if not args.no_parity:
         err, nw, nmat = parity_sample(items, meta, M, dev)
         result["parity"] = {"max_err_over_row_norm": err, "normwise_sampled": nw, "matrices": nmat,

@@ -389,4 +389,11 @@ ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t* 
   return hip_status(ql::launch_gemm(a, (int)M, workspace, workspace_bytes, stream), "gemm launch");
 }
 
+ql_status qlinear_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream) {
+  if (bytes <= 0 || bytes % 1024 || bytes >= ((int64_t)1 << 32))
+    return fail(QL_EINVAL, "read probe needs 0 < bytes < 2^32, a multiple of 1024 (bytes=%lld)", (long long)bytes);
+  QL_TRY(check_ptrs({buf, out}));
+  return hip_status(ql::launch_read_probe(buf, bytes, out, stream), "read probe launch");
+}
+
 }  // extern "C"

@@ -55,6 +55,8 @@ hipError_t launch_lb_pack(int64_t d_out, int64_t d_in, int64_t r, const int8_t* 
 hipError_t launch_lb_gemv(const ql_littlebit& w, const uint16_t* x, float* y, void* ws, hipStream_t stream);
 
 int device_cu_count();
+// read-bandwidth probe over `bytes` (a multiple of 1024) of device memory; out ^= XOR of the data
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
 // waves of a persistent grouped launch at batch size M (1: batch-1 kernel, else batched)
 int64_t grouped_wave_slots(int M);
 int64_t mm_wave_slots();

@@ -78,6 +78,8 @@ def lib():
         L.qlinear_grouped_prepare.restype = i64
         L.qlinear_grouped_prepare_split.argtypes = [vp, ctypes.c_int32, i64, ctypes.POINTER(i64)]
         L.qlinear_grouped_prepare_split.restype = i64
+        L.qlinear_read_probe.argtypes = [vp, i64, vp, vp]
+        L.qlinear_read_probe.restype = ctypes.c_int
         L.qlinear_grouped_wave_slots.argtypes = [ctypes.c_int32]
         L.qlinear_grouped_wave_slots.restype = i64
         L.qlinear_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp, vp]
@@ -444,6 +446,15 @@ def gemm(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor] = None,
     _check(lib().qlinear_gemm(M, pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
                               _ptr(pw.pscales), _ptr(x), _ptr(out), _ptr(workspace), need, _stream()), "gemm")
     return out
+
+
+def read_probe(buf, out):
+    """out (256 int32 words) ^= the per-lane-position XOR of buf's 1 KB blocks (uint8 device tensor)."""
+    _dev(buf, torch.uint8, "buf")
+    _dev(out, torch.int32, "out")
+    if out.numel() != 256:
+        raise ValueError("out needs 256 words")
+    _check(lib().qlinear_read_probe(_ptr(buf), buf.numel(), _ptr(out), _stream()), "read_probe")
 
 
 def wave_slots(M=1):

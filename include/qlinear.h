@@ -354,6 +354,17 @@ ql_status qlinear_c4_gemv(int64_t M, int64_t N, int64_t K, const void *c4, const
 ql_status qlinear_c4_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_slabs, int32_t M,
                                   uint32_t *sched, hipStream_t stream);
 
+/* ---------------------------------------------------------------- measurement */
+
+/* Pure HBM read probe, the measured bandwidth ceiling beside the nominal 8 TB/s: streams
+ * `bytes` (a positive multiple of 1024, below 2^32) of device memory at buf (dev, 16-byte
+ * aligned) with 128-bit non-temporal loads, 1 KB blocks interleaved across all waves, and
+ * folds it into out (dev, 256 uint32, 16-byte aligned): word 4 l + j is XORed with dword j of
+ * bytes 16 l .. 16 l + 15 of every block (so a zeroed out afterwards holds the XOR over the
+ * blocks).  The atomic fold makes out order-independent; calls that share out must not
+ * overlap unless their XORs may combine. */
+ql_status qlinear_read_probe(const void *buf, int64_t bytes, uint32_t *out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -235,3 +235,13 @@ def test_wave_slots_query():
     assert L.qlinear_grouped_wave_slots(0) == -1 and L.qlinear_grouped_wave_slots(17) == -1
     n1, n4 = L.qlinear_grouped_wave_slots(1), L.qlinear_grouped_wave_slots(4)
     assert n1 > 0 and n4 > 0 and n1 % 16 == 0 and n4 % 12 == 0
+
+
+def test_read_probe_argument_errors():
+    L = ql.lib()
+    p = ctypes.c_void_p(0x10000)
+    assert L.qlinear_read_probe(p, 0, p, None) == 1
+    assert L.qlinear_read_probe(p, 1000, p, None) == 1          # not a multiple of 1024
+    assert L.qlinear_read_probe(p, 1 << 32, p, None) == 1       # offsets are 32-bit
+    assert L.qlinear_read_probe(None, 1024, p, None) == 1
+    assert L.qlinear_read_probe(p, 1024, ctypes.c_void_p(0x10004), None) == 1  # misaligned out
