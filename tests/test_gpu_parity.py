@@ -150,13 +150,14 @@ def test_gemm_parity(ora, dev, N, K, grid, M):
 
 
 BIG_GEMM_CASES = [(64, 128, 128), (129, 1280, 200), (1000, 4096, 128), (70, 384, 384), (256, 5120, 256),
-                  (520, 1920, 130), (300, 12288, 128)]
+                  (520, 1920, 130), (300, 12288, 128), (300, 4096, 512), (64, 128, 256), (520, 1920, 300),
+                  (129, 1280, 257), (1000, 4096, 256)]
 
 
 @pytest.mark.parametrize("N,K,M", BIG_GEMM_CASES)
 @pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
 def test_gemm_large_batch_parity(ora, dev, N, K, M, grid):
-    """Batches of 128 tokens and more: ragged token tiles (M = 130, 200), rows past N,
+    """Batches of 128 tokens and more: ragged token tiles (M = 130, 200, 257, 300), rows past N,
     mixed grid blocks, long rows and K splits; every product exact, fp32 sums."""
     note(f"gemm large batch N={N} K={K} grid={grid} M={M}")
     pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=N * 5 + K + M)
