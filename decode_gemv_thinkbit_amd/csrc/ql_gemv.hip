@@ -1,4 +1,5 @@
-// Decode-time GEMV (1 <= M <= 8) over ThinkBit-packed weights on gfx950.
+// Decode-time batch-1 GEMV over ThinkBit-packed weights on gfx950 (the drivers
+// are templated on the token count; only M = 1 is instantiated).
 //
 // The per-token weight stream is the bandwidth-bound step of decoding
 // (ThinkBit summary page, onedev.kr/papers/1416, section "What it is"); the
@@ -69,8 +70,9 @@ __device__ __forceinline__ uint32_t xpair(cu32p xb, int kleft) {
 // step.  Scalar loads may return out of order, so a wait on a partial count is
 // impossible while they are in flight; ordering "issue next, compute current,
 // wait" overlaps both latencies with the current unit's arithmetic instead.
-// Code chunks stream through an 8-deep ring of 128-bit registers, each slot
-// reloaded as soon as its last byte has been turned into table addresses.
+// Code chunks stream through a ring of 128-bit registers (ternary: 4 chunks;
+// 2-bit: 2 groups = 4 chunks; 3-bit: 2 groups = 6 chunks), each slot reloaded
+// as soon as its last byte has been turned into table addresses.
 
 template <int M>
 struct SlabCtx {
