@@ -366,7 +366,7 @@ struct I3Buf {
 // triple T (0..3) of group slot S: words 3T..3T+2 of the slot's 3 chunks (12 words)
 template <int M, int S, int U>
 __device__ __forceinline__ void i3_issue(I3Buf<M>& b, const uint4 (&d)[6], const uint8_t* lut, const cu32p (&xb)[M],
-                                         uint32_t tok) {
+                                         uint32_t tok, uint32_t lane_off) {
   constexpr int NP = i3_np<M>();
   constexpr int T = (U * NP) / 16;   // triple within the group
   constexpr int P0 = (U * NP) % 16;  // first pair within the triple
@@ -377,7 +377,7 @@ __device__ __forceinline__ void i3_issue(I3Buf<M>& b, const uint4 (&d)[6], const
   asm volatile("" : "+v"(w0), "+v"(w1), "+v"(w2) : "v"(tok));  // table reads stay in this step
   sfor<NP>([&](auto pi) __attribute__((always_inline)) {
     constexpr int P = P0 + decltype(pi)::value;
-    b.e[decltype(pi)::value] = lds_b32(lut + kI3Lut + i3_field_x4<P>(w0, w1, w2));
+    b.e[decltype(pi)::value] = lds_b32(lut + kI3Lut + i3_addr<P>(w0, w1, w2, lane_off));
   });
 #pragma unroll
   for (int m = 0; m < M; ++m)
@@ -405,8 +405,9 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
   I3Buf<M> A, B;
   cu32p xb[M];
   set_xb(xb, c, kGroup * g0);
+  const uint32_t lane_off = i3_lane_off(c.lane);
   uint32_t tok = 0;  // step token: rewritten (as far as the compiler knows) after each step's arithmetic
-  i3_issue<M, 0, 0>(A, d, c.lut, xb, tok);
+  i3_issue<M, 0, 0>(A, d, c.lut, xb, tok, lane_off);
   lgkm_wait0();
   for (int gb = g0; gb < g1; gb += 2) {
     sfor<2>([&](auto s_) __attribute__((always_inline)) {
@@ -425,15 +426,15 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
           constexpr bool even = ((S * NU + U) & 1) == 0;
           if constexpr (U + 1 < NU) {
             if constexpr (even)
-              i3_issue<M, S, U + 1>(B, d, c.lut, xb, tok);
+              i3_issue<M, S, U + 1>(B, d, c.lut, xb, tok, lane_off);
             else
-              i3_issue<M, S, U + 1>(A, d, c.lut, xb, tok);
+              i3_issue<M, S, U + 1>(A, d, c.lut, xb, tok, lane_off);
           } else {
             if (more) {
               if constexpr (even)
-                i3_issue<M, S ^ 1, 0>(B, d, c.lut, xn, tok);
+                i3_issue<M, S ^ 1, 0>(B, d, c.lut, xn, tok, lane_off);
               else
-                i3_issue<M, S ^ 1, 0>(A, d, c.lut, xn, tok);
+                i3_issue<M, S ^ 1, 0>(A, d, c.lut, xn, tok, lane_off);
             }
 #pragma unroll
             for (int q = 0; q < 3; ++q) d[3 * S + q] = src.load(3 * (g + 2) + q);
@@ -482,7 +483,7 @@ __device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, in
 #define QL_WG_PER_CU 2
 #endif
 constexpr int kWaves = QL_WAVES;          // waves per workgroup
-constexpr int kWgPerCu = QL_WG_PER_CU;    // resident workgroups per CU (LDS tables: 69 KB each)
+constexpr int kWgPerCu = QL_WG_PER_CU;    // resident workgroups per CU (LDS tables: 77 KB each)
 
 // One wave task: one 64-row slab of one descriptor, or one part of its input
 // when the entry is split (partial sums then meet in the state buffer).

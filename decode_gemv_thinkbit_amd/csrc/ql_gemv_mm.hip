@@ -50,7 +50,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 #define QL_MM_WAVES_PER_EU 3
 #endif
 constexpr int kMmWaves = QL_MM_WAVES;  // waves per workgroup
-constexpr int kMmWgPerCu = 2;  // resident workgroups per CU (LDS tables: 69 KB each; 168 VGPRs: 3 waves per SIMD)
+constexpr int kMmWgPerCu = 2;  // resident workgroups per CU (LDS tables: 77 KB each; 168 VGPRs: 3 waves per SIMD)
 constexpr int kRB = kSlab / 16;  // 16-row blocks per slab
 static_assert(kRB * 4 * 64 <= kPartWords, "a split part stores 4 tokens x kRB rows per lane");
 
@@ -361,6 +361,7 @@ __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc&
   const int nchunks = 3 * g1;
   const CodeDw src(codes, nchunks, lane);
   const int q = lane >> 4;
+  const uint32_t i3_off = i3_lane_off(lane);
   // the triple's three dwords: group-relative bytes 12 q + 4 j (each inside one chunk)
   uint32_t toff[3];
 #pragma unroll
@@ -386,10 +387,10 @@ __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc&
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       const uint32_t w0 = t[rb][0], w1 = t[rb][1], w2 = t[rb][2];
-      b.e[rb][0] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 0>(w0, w1, w2));
-      b.e[rb][1] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 1>(w0, w1, w2));
-      b.e[rb][2] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 2>(w0, w1, w2));
-      b.e[rb][3] = lds_b32(lut + kI3Lut + i3_field_x4<4 * W + 3>(w0, w1, w2));
+      b.e[rb][0] = lds_b32(lut + kI3Lut + i3_addr<4 * W + 0>(w0, w1, w2, i3_off));
+      b.e[rb][1] = lds_b32(lut + kI3Lut + i3_addr<4 * W + 1>(w0, w1, w2, i3_off));
+      b.e[rb][2] = lds_b32(lut + kI3Lut + i3_addr<4 * W + 2>(w0, w1, w2, i3_off));
+      b.e[rb][3] = lds_b32(lut + kI3Lut + i3_addr<4 * W + 3>(w0, w1, w2, i3_off));
     }
   };
   uint32_t tw[2][kRB][3];

@@ -10,12 +10,16 @@
 namespace ql {
 
 // ---------------------------------------------------------------- LDS tables
-// The 3-bit table sits at offset 0, so its addresses need no base; the other
-// two bases fit the 16-bit immediate offset of the LDS read instructions.
-constexpr int kI3Lut = 0;                   // 64 entries x 4 B
-constexpr int kTLut = 64 * 4;               // 243 rows x 256 B (16 replicas x 16 B)
-constexpr int kI2Lut = kTLut + 243 * 256;   // 256 rows x 32 B (4 replicas x 8 B)
-constexpr int kLutBytes = kI2Lut + 256 * 32;  // 70656
+// Each lane reads its own replica of a table row, so a wave's 64 data-dependent
+// reads spread over the banks instead of piling onto the few that hold one
+// copy.  The 3-bit table sits at offset 0, so its addresses need no base; the
+// other two bases fit the 16-bit immediate offset of the LDS read instructions.
+// Two workgroups' tables (2 x 78592 B) fit the 160 KB of LDS of a CU.
+constexpr int kI3Lut = 0;                     // 64 rows x 128 B (32 replicas x 4 B)
+constexpr int kI2Lut = 64 * 128;              // 256 rows x 32 B (4 replicas x 8 B)
+constexpr int kTLut = kI2Lut + 256 * 32;      // 243 rows x 256 B (16 replicas x 16 B)
+constexpr int kLutBytes = kTLut + 243 * 256;  // 78592
+static_assert(kTLut < 65536 && kI2Lut < 65536, "table bases must fit the LDS immediate offset");
 
 typedef uint32_t lut_v4 __attribute__((ext_vector_type(4)));
 typedef uint32_t lut_v2 __attribute__((ext_vector_type(2)));
@@ -62,34 +66,42 @@ __device__ inline void build_luts(uint8_t* smem) {
       *reinterpret_cast<uint2*>(smem + kI2Lut + b * 32) = q;
     } else {
       const int e = r - 243 - 256;
-      *reinterpret_cast<uint32_t*>(smem + kI3Lut + e * 4) = code_bf16((e & 7) - 4) | (code_bf16((e >> 3) - 4) << 16);
+      *reinterpret_cast<uint32_t*>(smem + kI3Lut + e * 128) = code_bf16((e & 7) - 4) | (code_bf16((e >> 3) - 4) << 16);
     }
   }
   __syncthreads();
-  // ternary: 243 rows x 16 replicas x 16 B; 2-bit: 256 rows x 4 replicas x 8 B
-  constexpr int kT = (243 * 16 + NT - 1) / NT, kI2 = (256 * 4 + NT - 1) / NT;
+  // ternary: 243 rows x 16 replicas x 16 B; 2-bit: 256 rows x 4 replicas x 8 B;
+  // 3-bit: 64 rows x 32 replicas x 4 B
+  constexpr int kT = (243 * 16 + NT - 1) / NT, kI2 = (256 * 4 + NT - 1) / NT, kI3 = (64 * 32 + NT - 1) / NT;
   lut_copies<lut_v4, 16, 16, 243 * 16, NT>(smem + kTLut, t, std::make_integer_sequence<int, kT>{});
   lut_copies<lut_v2, 4, 8, 256 * 4, NT>(smem + kI2Lut, t, std::make_integer_sequence<int, kI2>{});
+  lut_copies<uint32_t, 32, 4, 64 * 32, NT>(smem + kI3Lut, t, std::make_integer_sequence<int, kI3>{});
 }
 
-// 3-bit table address of field P of a 96-bit triple
-// 4 * (6-bit field P of the 96-bit triple w0|w1<<32|w2<<64)
+// Replica offset of a lane in the 3-bit table.
+__device__ __forceinline__ uint32_t i3_lane_off(int lane) { return (uint32_t)(lane & 31) << 2; }
+
+// 3-bit table address of field P of the 96-bit triple w0|w1<<32|w2<<64: the
+// 6-bit field times the 128-byte row, plus the lane's replica offset (i3_lane_off).
+// One shift or funnel shift brings the field to bits 7..12, one and-or adds the offset.
 template <int P>
-__device__ __forceinline__ uint32_t i3_field_x4(uint32_t w0, uint32_t w1, uint32_t w2) {
+__device__ __forceinline__ uint32_t i3_addr(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t lane_off) {
   constexpr int bit = 6 * P;
-  if constexpr (bit == 0) {
-    return (w0 << 2) & 0xFCu;
-  } else if constexpr (bit + 6 <= 32) {
-    return (w0 >> (bit - 2)) & 0xFCu;
-  } else if constexpr (bit < 32) {
-    return __builtin_amdgcn_alignbit(w1, w0, bit - 2) & 0xFCu;
-  } else if constexpr (bit + 6 <= 64) {
-    return (w1 >> (bit - 34)) & 0xFCu;
-  } else if constexpr (bit < 64) {
-    return __builtin_amdgcn_alignbit(w2, w1, bit - 34) & 0xFCu;
+  constexpr int s = bit - 7;  // right shift of the 96-bit value that puts the field at bit 7
+  uint32_t v;
+  if constexpr (s < 0) {
+    v = w0 << -s;
   } else {
-    return (w2 >> (bit - 66)) & 0xFCu;
+    constexpr int wi = s / 32, sh = s % 32;
+    const uint32_t lo = wi == 0 ? w0 : wi == 1 ? w1 : w2;
+    if constexpr (bit + 6 <= 32 * (wi + 1)) {
+      v = lo >> sh;
+    } else {
+      static_assert(wi < 2, "a field past bit 96");
+      v = __builtin_amdgcn_alignbit(wi == 0 ? w1 : w2, lo, sh);
+    }
   }
+  return (v & 0x1F80u) | lane_off;
 }
 
 }  // namespace ql
