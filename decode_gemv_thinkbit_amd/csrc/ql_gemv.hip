@@ -166,6 +166,20 @@ __device__ __forceinline__ void t_compute(const TEnt& b, const TWin& w, float (&
   });
 }
 
+// y += scale(g) * acc[g - 5p] over the period's groups, in group order; the
+// period starts at position S0 of its first scale block (sa), later groups sit
+// in the next block (sb).  Groups at or past G contribute nothing.
+template <int S0>
+__device__ __forceinline__ void t_scale(const u32x4_t& sa, const u32x2_t& sb, int g_left, const float (&acc)[5],
+                                        float& y) {
+  sfor<5>([&](auto gl_) __attribute__((always_inline)) {
+    constexpr int gl = decltype(gl_)::value, q = S0 + gl;
+    const uint32_t w = q < 8 ? sa[q >> 1] : sb[(q - 8) >> 1];
+    const float v = scale_of_pair<q & 1>(w);
+    y = fmaf(gl < g_left ? v : 0.0f, acc[gl], y);
+  });
+}
+
 #ifndef QL_T_RING
 #define QL_T_RING 4  // 16-byte chunks in flight per lane (ternary)
 #endif
@@ -197,15 +211,23 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
   t_lds<0, R>(A, d, lane_off, c.lut);
   t_x<0>(W0, xrs, 2 * kPeriodK * p0);
   lgkm_wait0();
+  const int G8 = (c.G + 7) >> 3;
   for (int p = p0; p < p1; ++p) {
-    float sc[5];
+    // Scales of the period's groups 5p .. 5p+4: the lane's 8-group block holding
+    // group 5p and, when the period runs past it, the next block (if stored).
+    // Whole-block loads touch each cache line once; per-group loads touched a
+    // line per lane.
+    const int blk = (5 * p) >> 3, s0 = (5 * p) & 7;
+    // A period reaches at most 4 groups into the next block, so only that half
+    // is read.  Both loads are unconditional (the second clamped to the last
+    // stored block, whose values are then never used) and every loaded dword
+    // stays live to the period's end: the chunk waits in between then count
+    // these loads as in flight instead of waiting for them.
+    const u32x4_t sa = ld_scale_blk(c.scales, blk, c.lane);
+    const u32x2_t sb = ld_scale_blk_lo(c.scales, blk + 1 < G8 ? blk + 1 : blk, c.lane);
+    const int g_left = c.G - 5 * p;  // groups of the period below G (at least 1)
 #pragma unroll
-    for (int gl = 0; gl < 5; ++gl) {
-      const int g = 5 * p + gl;
-      const float v = ld_scale(c.scales, g < c.G ? g : c.G - 1, c.lane);
-      sc[gl] = g < c.G ? v : 0.0f;
-      acc[gl] = 0.0f;
-    }
+    for (int gl = 0; gl < 5; ++gl) acc[gl] = 0.0f;
     const bool more = p + 1 < p1;
     int x_off = 2 * kPeriodK * p;
     auto step = [&](auto u) __attribute__((always_inline)) {
@@ -241,8 +263,16 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
     sfor<kTUnits / 2>(step);
     if (more || !last_half)
       sfor_from<kTUnits / 2, kTUnits / 2>(step);
-#pragma unroll
-    for (int gl = 0; gl < 5; ++gl) y[0] = fmaf(sc[gl], acc[gl], y[0]);
+    switch (s0) {
+      case 0: t_scale<0>(sa, sb, g_left, acc, y[0]); break;
+      case 1: t_scale<1>(sa, sb, g_left, acc, y[0]); break;
+      case 2: t_scale<2>(sa, sb, g_left, acc, y[0]); break;
+      case 3: t_scale<3>(sa, sb, g_left, acc, y[0]); break;
+      case 4: t_scale<4>(sa, sb, g_left, acc, y[0]); break;
+      case 5: t_scale<5>(sa, sb, g_left, acc, y[0]); break;
+      case 6: t_scale<6>(sa, sb, g_left, acc, y[0]); break;
+      default: t_scale<7>(sa, sb, g_left, acc, y[0]); break;
+    }
   }
 }
 

@@ -117,6 +117,16 @@ template <int H>
 __device__ __forceinline__ float scale_of_pair(uint32_t p) {
   return __uint_as_float(H ? (p & 0xFFFF0000u) : (p << 16));
 }
+// The 16 bytes holding the scales of groups 8 blk .. 8 blk + 7 of slab row `lane`
+// (one coalesced kilobyte per wave); blk must be below ceil(G / 8).
+__device__ __forceinline__ u32x4_t ld_scale_blk(const uint16_t* __restrict__ ss, int blk, int lane) {
+  return ((gu32x4p)ss)[blk * kSlab + lane];
+}
+// The first half of that block (groups 8 blk .. 8 blk + 3).
+__device__ __forceinline__ u32x2_t ld_scale_blk_lo(const uint16_t* __restrict__ ss, int blk, int lane) {
+  typedef const __attribute__((address_space(1))) u32x2_t* gu32x2p;
+  return ((gu32x2p)ss)[(blk * kSlab + lane) * 2];
+}
 __device__ __forceinline__ float ld_scale(const uint16_t* __restrict__ ss, int g, int lane) {
   return bf16_bits_to_f32(((gu16p)ss)[((g >> 3) * kSlab + lane) * 8 + (g & 7)]);
 }
