@@ -237,6 +237,10 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
       auto& nxt = odd ? A : B;
       auto& wc = odd ? W1 : W0;
       auto& wn = odd ? W0 : W1;
+      // issue the next unit's reads at raised wave priority, so that a wave
+      // with its operands ready hands the table reads to LDS before the SIMD
+      // turns to other waves' arithmetic
+      __builtin_amdgcn_s_setprio(1);
       if constexpr (U + 1 < kTUnits) {
         t_lds<U + 1, R>(nxt, d, lane_off, c.lut);
         t_x<U + 1>(wn, xrs, x_off);
@@ -251,6 +255,7 @@ __device__ void run_t(const SlabCtx<M>& c, int p0, int p1, float (&y)[M]) {
           t_x<0>(wn, xrs, x_off + 2 * kPeriodK);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       sched_fence();
       t_compute<U>(cur, wc, acc);
       after(lane_off, acc);
