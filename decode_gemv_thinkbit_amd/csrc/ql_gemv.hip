@@ -459,6 +459,7 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
         sfor<NU>([&](auto u) __attribute__((always_inline)) {
           constexpr int U = decltype(u)::value;
           constexpr bool even = ((S * NU + U) & 1) == 0;
+          __builtin_amdgcn_s_setprio(1);  // the next unit's reads at raised priority, as in the ternary step
           if constexpr (U + 1 < NU) {
             if constexpr (even)
               i3_issue<M, S, U + 1>(B, d, c.lut, xb, tok, lane_off);
@@ -474,6 +475,7 @@ __device__ void run_i3(const SlabCtx<M>& c, int g0, int g1, float (&y)[M]) {
 #pragma unroll
             for (int q = 0; q < 3; ++q) d[3 * S + q] = src.load(3 * (g + 2) + q);
           }
+          __builtin_amdgcn_s_setprio(0);
           sched_fence();
           if constexpr (even)
             i3_compute<M>(A, acc);
