@@ -136,6 +136,8 @@ __device__ __forceinline__ uint32_t word_of(const uint4& d, int w) {
 }
 
 __device__ i32x4_t ql_sbuf_load_x4(i32x4_t rsrc, int offset, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v4i32");
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+__device__ i32x16_t ql_sbuf_load_x16(i32x4_t rsrc, int offset, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v16i32");
 
 // Buffer resource over n_bytes of uniform memory at p (raw, stride 0).
 __device__ __forceinline__ i32x4_t scalar_rsrc(const void* p, uint32_t n_bytes) {
