@@ -7,8 +7,9 @@ rounding noise of a grid it approximates the loss increase of that grid; one
 grid per unit is chosen under a bit budget for the whole decoder by
 Lagrangian relaxation, with query and key projections kept at >= 2 bits.
 
-The rounding noise runs on the GPU (``qlinear_rtn_noise``), the knapsack in
-the library's host code (``qlinear_allocate``); this module only gathers the
+The rounding noise and the sensitivities run on the GPU
+(``qlinear_rtn_noise``, ``qlinear_block_sensitivity``), the knapsack in the
+library's host code (``qlinear_allocate``); this module only gathers the
 units.  A unit is a 128-row grid block (the granularity the packed layout
 stores) or a whole linear.  The activations are the workload's own seeded
 x; the output gradients are seeded stand-ins (``synth.output_gradient``).
@@ -36,16 +37,6 @@ class Units:
     allowed: np.ndarray   # uint32 masks
 
 
-def block_sensitivity(x: torch.Tensor, grad: torch.Tensor) -> np.ndarray:
-    """S of every 128-row block: ||x||^2 * sum over the block's rows of grad^2 (fp64)."""
-    xs = float(x.double().square().sum())
-    g2 = grad.double().square()
-    nb = (g2.numel() + BLOCK_ROWS - 1) // BLOCK_ROWS
-    pad = torch.zeros(nb * BLOCK_ROWS, dtype=torch.float64, device=g2.device)
-    pad[: g2.numel()] = g2
-    return xs * pad.view(nb, BLOCK_ROWS).sum(dim=1).cpu().numpy()
-
-
 def workload_units(wl: Workload, wl_index: int, dev, layers=None, granularity: str = "block",
                    keep_2bit=("q", "k")) -> Units:
     """Units of the workload's decoder layers with their weights, sensitivity and noise."""
@@ -56,7 +47,7 @@ def workload_units(wl: Workload, wl_index: int, dev, layers=None, granularity: s
             noise = ql.rtn_noise(W).cpu().numpy()
             del W
             x = synth.activations(1, lin.K, synth.x_seed(wl_index, layer, lin.x_slot, 1), device=dev)
-            sb = block_sensitivity(x, synth.output_gradient(lin.N, wl_index, layer, mi, device=dev))
+            sb = ql.block_sensitivity(x, synth.output_gradient(lin.N, wl_index, layer, mi, device=dev)).cpu().numpy()
             rows = np.minimum(BLOCK_ROWS, lin.N - BLOCK_ROWS * np.arange(len(sb)))
             mask = ql.AT_LEAST_2BIT if lin.name in keep_2bit else ql.ALL_GRIDS
             if granularity == "block":

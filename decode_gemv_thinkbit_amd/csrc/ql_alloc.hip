@@ -61,6 +61,38 @@ hipError_t launch_rtn_noise(int64_t N, int64_t K, const float* W, double* noise,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- sensitivity
+// S of every 128-row block of a linear: ||x||^2 times the block's sum of
+// squared output gradients.  Each square is exact in fp64 (a bf16 or fp32
+// value squared), and both sums run in ascending index order in one lane, so
+// the result does not depend on the launch shape.  Offline work: one
+// workgroup per block, the x norm recomputed by each (K is a row length).
+__global__ void __launch_bounds__(64) block_sensitivity_kernel(int64_t N, int64_t K, const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ grad,
+                                                               double* __restrict__ S) {
+  if (threadIdx.x != 0) return;
+  const int64_t b = blockIdx.x;
+  double xs = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    const double v = (double)bf16_bits_to_f32(x[k]);
+    xs += v * v;
+  }
+  double gs = 0.0;
+  const int64_t n1 = (b + 1) * kBlock < N ? (b + 1) * kBlock : N;
+  for (int64_t n = b * kBlock; n < n1; ++n) {
+    const double g = (double)grad[n];
+    gs += g * g;
+  }
+  S[b] = xs * gs;
+}
+
+hipError_t launch_block_sensitivity(int64_t N, int64_t K, const uint16_t* x, const float* grad, double* S,
+                                    hipStream_t stream) {
+  const int64_t nb = (N + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(block_sensitivity_kernel, dim3((unsigned)nb), dim3(64), 0, stream, N, K, x, grad, S);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- knapsack (host)
 namespace {
 

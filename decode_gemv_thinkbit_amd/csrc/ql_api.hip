@@ -250,6 +250,14 @@ ql_status qlinear_rtn_noise(int64_t N, int64_t K, const float* W, double* noise,
   return hip_status(ql::launch_rtn_noise(N, K, W, noise, stream), "rtn_noise launch");
 }
 
+ql_status qlinear_block_sensitivity(int64_t N, int64_t K, const uint16_t* x, const float* grad, double* S,
+                                     hipStream_t stream) {
+  if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+    return fail(QL_EINVAL, "block sensitivity needs positive N and K (N=%lld, K=%lld)", (long long)N, (long long)K);
+  QL_TRY(check_ptrs({x, grad, S}));
+  return hip_status(ql::launch_block_sensitivity(N, K, x, grad, S, stream), "block_sensitivity launch");
+}
+
 ql_status qlinear_allocate(const ql_alloc_unit* units, int64_t count, double budget_bits, const double* grid_bits,
                            int8_t* grid_out, double* lambda_out) {
   if (!units || !grid_out || count <= 0) return fail(QL_EINVAL, "allocate needs units, an output and count > 0");

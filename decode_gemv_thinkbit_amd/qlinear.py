@@ -88,6 +88,7 @@ def lib():
         L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qlinear_rtn_noise.argtypes = [i64, i64, vp, vp, vp]
         L.qlinear_allocate.argtypes = [vp, i64, ctypes.c_double, vp, vp, vp]
+        L.qlinear_block_sensitivity.argtypes = [i64, i64, vp, vp, vp, vp]
         L.qlinear_lb_bpw.argtypes = [i64, i64, i64]
         L.qlinear_lb_bpw.restype = ctypes.c_double
         L.qlinear_lb_rank.argtypes = [i64, i64, ctypes.c_double]
@@ -111,7 +112,7 @@ def lib():
                      "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
                      "qlinear_gemv_grouped", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
                      "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped", "qlinear_rtn_noise",
-                     "qlinear_allocate", "qlinear_lb_pack", "qlinear_lb_gemv"):
+                     "qlinear_allocate", "qlinear_block_sensitivity", "qlinear_lb_pack", "qlinear_lb_gemv"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -257,6 +258,16 @@ def rtn_noise(W: torch.Tensor) -> torch.Tensor:
     N, K = W.shape
     out = torch.empty((n_blocks(N), 3), dtype=torch.float64, device=W.device)
     _check(lib().qlinear_rtn_noise(N, K, _ptr(W), _ptr(out), _stream()), "rtn_noise")
+    return out
+
+
+def block_sensitivity(x: torch.Tensor, grad: torch.Tensor) -> torch.Tensor:
+    """float64 [ceil(N/128)] on the device: ||x||^2 * (sum of grad^2 over each 128-row block)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(grad, torch.float32, "grad")
+    K, N = x.numel(), grad.numel()
+    out = torch.empty(n_blocks(N), dtype=torch.float64, device=x.device)
+    _check(lib().qlinear_block_sensitivity(N, K, _ptr(x), _ptr(grad), _ptr(out), _stream()), "block_sensitivity")
     return out
 
 

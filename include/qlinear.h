@@ -249,6 +249,14 @@ typedef struct {
  * W (dev) fp32 [N][K]; noise (dev) double [ceil(N/128)][3].  Deterministic. */
 ql_status qlinear_rtn_noise(int64_t N, int64_t K, const float *W, double *noise, hipStream_t stream);
 
+/* Sensitivity of every 128-row block of a linear (summary page, section "How it differs",
+ * stage 1: the product of the squared norms of the input activations and of the output
+ * gradients), restricted to the block's output rows: S[b] = (sum_k x[k]^2) *
+ * (sum_{n in block b} grad[n]^2), each sum in fp64 in ascending index order (deterministic).
+ *   x (dev) bf16 bits [K]; grad (dev) fp32 [N]; S (dev) double [ceil(N/128)]. */
+ql_status qlinear_block_sensitivity(int64_t N, int64_t K, const uint16_t *x, const float *grad, double *S,
+                                    hipStream_t stream);
+
 /* Lagrangian multiple-choice knapsack (host only, no GPU).  For a multiplier lam >= 0 every
  * unit takes the allowed grid minimising S*noise[g] + lam*weights*grid_bits[g] (ties to fewer
  * bits); the result is the assignment at the smallest lam whose total bits fit

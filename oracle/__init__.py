@@ -333,7 +333,8 @@ def block_sensitivity(x_bf16: np.ndarray, grad: np.ndarray) -> np.ndarray:
 
 
 def allocate(n, S, E, allowed, budget: float, bits=None) -> tuple[np.ndarray, float]:
-    """Lagrangian multiple-choice knapsack: grid per unit and the multiplier used."""
+    """Lagrangian multiple-choice knapsack by the convex-hull greedy: grid per unit and the
+    slope of the first group of hull edges left out (0 when every edge fits)."""
     n = np.ascontiguousarray(n, dtype=np.int64)
     S = np.ascontiguousarray(S, dtype=np.float64)
     E = np.ascontiguousarray(E, dtype=np.float64).reshape(len(n), 3)

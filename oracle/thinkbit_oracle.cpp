@@ -677,42 +677,35 @@ int ora_block_sensitivity(int64_t K, const uint16_t* x_bf16, int64_t N, const fl
   return 0;
 }
 
-// Multiple-choice knapsack by Lagrangian relaxation.  Unit i has n[i]
-// weights, sensitivity S[i], noise E[i*3 + g] and a mask of allowed grids.
-// For a multiplier lam >= 0 every unit independently takes the allowed grid
-// minimising S*E[g] + lam*(n*bits[g]), scanning grids in increasing bits and
-// keeping the first minimum (ties go to fewer bits).  The bits used fall as
-// lam grows, and a unit's choice changes only where two of its costs cross,
-// so the assignments are constant between consecutive crossings.  Each such
-// interval is tried at one interior point (0, the midpoints, twice the last
-// crossing; interior so that no cost comparison sits on a rounding tie), in
-// increasing order, and the first whose total bits fit budget * sum(n) is
-// returned with that multiplier.  Returns 0, -1 for bad input, -2 if even the
-// cheapest allowed grids exceed the budget.
-namespace {
-double unit_cost(double S, double E, double lam, int64_t n, double bits) { return S * E + lam * ((double)n * bits); }
-
-int pick(int64_t n, double S, const double* E, uint32_t allowed, const double* bits, const int* order, double lam) {
-  int best = -1;
-  double bc = 0.0;
-  for (int t = 0; t < 3; ++t) {
-    const int g = order[t];
-    if (!(allowed >> g & 1u)) continue;
-    const double c = unit_cost(S, E[g], lam, n, bits[g]);
-    if (best < 0 || c < bc) {
-      best = g;
-      bc = c;
-    }
-  }
-  return best;
-}
-}  // namespace
-
+// Multiple-choice knapsack by Lagrangian relaxation (summary page, section
+// "How it differs", stage 1), written as the greedy walk along each unit's
+// lower convex hull -- the textbook equivalent of sweeping the multiplier,
+// and a different computation from a sweep over multiplier values.
+//
+// Unit i has n[i] weights, sensitivity S[i], noise E[i*3 + g] and a mask of
+// allowed grids.  Its options are points (bits b_g = n*bits[g], cost
+// f_g = S*E[g]).  For a multiplier lam every unit takes the option minimising
+// f + lam*b (ties to fewer bits); as lam falls from +inf to 0 that choice
+// walks the lower convex hull of the points from the fewest-bits option,
+// one hull edge at a time, taking an edge when lam drops below its slope
+// (cost saved per extra bit).  So:
+//   1. start every unit at its fewest-bits option (lowest cost among equal
+//      bits); if that already exceeds budget * sum(n), the budget is infeasible;
+//   2. list every unit's hull edges with positive slope (points on one line
+//      collapse into the edge to the farthest point, which is what a
+//      multiplier strictly inside an interval picks);
+//   3. take the edges in decreasing slope, all edges of one slope together
+//      (no multiplier separates them), and stop at the first group that would
+//      exceed the budget: a smaller multiplier would take that group too.
+// The result is the Lagrangian assignment at the smallest multiplier whose
+// bits fit.  lam_out receives the slope of the first group left out (0 when
+// every edge fits): the assignment is the minimiser for every multiplier
+// strictly between that slope and the slope of the last group taken.
+// Returns 0, -1 for bad input, -2 if even the cheapest allowed options exceed
+// the budget.
 int ora_allocate(int64_t count, const int64_t* n, const double* S, const double* E, const uint32_t* allowed,
                  const double* bits, double budget, int8_t* out, double* lam_out) {
   if (count <= 0) return -1;
-  int order[3] = {0, 1, 2};
-  std::sort(order, order + 3, [&](int a, int b) { return bits[a] < bits[b] || (bits[a] == bits[b] && a < b); });
   double total_n = 0.0;
   for (int64_t i = 0; i < count; ++i) {
     if (n[i] <= 0 || !(S[i] >= 0.0) || !(allowed[i] & 7u)) return -1;
@@ -721,30 +714,68 @@ int ora_allocate(int64_t count, const int64_t* n, const double* S, const double*
     total_n += (double)n[i];
   }
   const double cap = budget * total_n;
-  std::vector<double> cand{0.0};
-  for (int64_t i = 0; i < count; ++i)
-    for (int a = 0; a < 3; ++a)
-      for (int b = 0; b < 3; ++b) {
-        if (!(allowed[i] >> a & 1u) || !(allowed[i] >> b & 1u) || !(bits[a] < bits[b])) continue;
-        const double lam = (S[i] * E[i * 3 + a] - S[i] * E[i * 3 + b]) / ((double)n[i] * (bits[b] - bits[a]));
-        if (lam > 0.0) cand.push_back(lam);
+  struct Edge {
+    double slope;
+    int64_t unit;
+    int to;  // grid at the edge's far end
+  };
+  std::vector<Edge> edges;
+  for (int64_t i = 0; i < count; ++i) {
+    // the unit's options, by bits, then cost, then grid index; equal bits keep the first
+    std::vector<int> opt;
+    for (int g = 0; g < 3; ++g)
+      if (allowed[i] >> g & 1u) opt.push_back(g);
+    std::sort(opt.begin(), opt.end(), [&](int a, int b) {
+      if (bits[a] != bits[b]) return bits[a] < bits[b];
+      const double fa = S[i] * E[i * 3 + a], fb = S[i] * E[i * 3 + b];
+      if (fa != fb) return fa < fb;
+      return a < b;
+    });
+    std::vector<int> pts;
+    for (int g : opt)
+      if (pts.empty() || bits[g] != bits[pts.back()]) pts.push_back(g);
+    out[i] = (int8_t)pts[0];
+    int v = pts[0];
+    for (;;) {
+      int best = -1;
+      double bs = 0.0;
+      for (int w : pts) {
+        if (!(bits[w] > bits[v])) continue;
+        const double s = (S[i] * E[i * 3 + v] - S[i] * E[i * 3 + w]) / ((double)n[i] * bits[w] - (double)n[i] * bits[v]);
+        if (best < 0 || s > bs || (s == bs && bits[w] > bits[best])) {
+          best = w;
+          bs = s;
+        }
       }
-  std::sort(cand.begin(), cand.end());
-  cand.erase(std::unique(cand.begin(), cand.end()), cand.end());
-  std::vector<double> pts{0.0};
-  for (size_t j = 1; j < cand.size(); ++j)
-    pts.push_back(j + 1 < cand.size() ? 0.5 * (cand[j] + cand[j + 1]) : 2.0 * cand[j]);
-  if (cand.size() > 1) pts.insert(pts.begin() + 1, 0.5 * cand[1]);
-  for (double lam : pts) {
-    double used = 0.0;
-    for (int64_t i = 0; i < count; ++i) used += (double)n[i] * bits[pick(n[i], S[i], E + 3 * i, allowed[i], bits, order, lam)];
-    if (used <= cap) {
-      for (int64_t i = 0; i < count; ++i) out[i] = (int8_t)pick(n[i], S[i], E + 3 * i, allowed[i], bits, order, lam);
-      if (lam_out) *lam_out = lam;
-      return 0;
+      if (best < 0 || !(bs > 0.0)) break;
+      edges.push_back({bs, i, best});
+      v = best;
     }
   }
-  return -2;
+  auto used_bits = [&]() {
+    double u = 0.0;
+    for (int64_t i = 0; i < count; ++i) u += (double)n[i] * bits[out[i]];
+    return u;
+  };
+  if (used_bits() > cap) return -2;
+  // decreasing slope; within a unit the hull's slopes already decrease, and the
+  // stable order keeps a unit's edges in walk order when slopes tie
+  std::stable_sort(edges.begin(), edges.end(), [](const Edge& a, const Edge& b) { return a.slope > b.slope; });
+  double lam = 0.0;
+  for (size_t j = 0; j < edges.size();) {
+    size_t e = j;
+    while (e < edges.size() && edges[e].slope == edges[j].slope) ++e;
+    std::vector<int8_t> keep(out, out + count);
+    for (size_t q = j; q < e; ++q) out[edges[q].unit] = (int8_t)edges[q].to;
+    if (used_bits() > cap) {
+      std::copy(keep.begin(), keep.end(), out);
+      lam = edges[j].slope;
+      break;
+    }
+    j = e;
+  }
+  if (lam_out) *lam_out = lam;
+  return 0;
 }
 
 }  // extern "C"

@@ -8,7 +8,10 @@ The oracle's pieces are pinned against what the mathematics fixes:
   * rounding noise: the squared error of the (separately pinned) quantizer's
     codes and scales; zero for weights already on the grid;
   * sensitivity: closed forms.
-The library's host solver must then reproduce the oracle bit for bit.
+The oracle solves the knapsack as a greedy walk along each unit's lower convex
+hull; the library sweeps the multiplier over its crossing points.  The two are
+different computations of the same Lagrangian answer: the brute-force pins run
+against both solvers, and the library must pick the oracle's grids exactly.
 """
 import itertools
 
@@ -50,8 +53,19 @@ def test_page_shares_fit_the_two_bit_budget():
     assert 0.753 * (1.6 + 1 / 8) + 0.06 * BITS[1] + 0.187 * BITS[2] > 2.0
 
 
+def solve(which, ora, n, S, E, allowed, budget, bits=None):
+    """(grids, multiplier) from the oracle or the library; ValueError when infeasible."""
+    if which == "oracle":
+        return ora.allocate(n, S, E, allowed, budget, bits)
+    try:
+        return ql.allocate(n, S, E, allowed, budget, bits)
+    except ql.QLinearError as e:
+        raise ValueError(str(e)) from e
+
+
+@pytest.mark.parametrize("which", ["oracle", "library"])
 @pytest.mark.parametrize("seed", range(40))
-def test_oracle_knapsack_against_brute_force(ora, seed):
+def test_knapsack_against_brute_force(ora, seed, which):
     rng = np.random.default_rng(seed)
     m = int(rng.integers(1, 8))
     n, S, E, allowed = random_instance(rng, m)
@@ -60,9 +74,9 @@ def test_oracle_knapsack_against_brute_force(ora, seed):
     cheapest = sum(n[i] * min(BITS[g] for g in range(3) if allowed[i] >> g & 1) for i in range(m))
     if cheapest > cap:
         with pytest.raises(ValueError):
-            ora.allocate(n, S, E, allowed, budget)
+            solve(which, ora, n, S, E, allowed, budget)
         return
-    g, lam = ora.allocate(n, S, E, allowed, budget)
+    g, lam = solve(which, ora, n, S, E, allowed, budget)
     assert all(allowed[i] >> g[i] & 1 for i in range(m))
     used = float((n * BITS[g]).sum())
     cost = float((S * E[np.arange(m), g]).sum())
@@ -76,6 +90,21 @@ def test_oracle_knapsack_against_brute_force(ora, seed):
                for i in range(m)) - lam * cap
     assert dual <= opt_full * (1 + 1e-12) + 1e-12
     assert opt_full <= cost * (1 + 1e-12) + 1e-12
+
+
+def test_knapsack_duality_gap_example(ora):
+    """Three equal units at a budget where two of them could take 2-bit: the exact optimum
+    upgrades two, but the three T -> I2 hull edges have one slope, so no multiplier takes
+    only two of them and the relaxation leaves all three ternary (the method's known gap)."""
+    n = np.array([128, 128, 128])
+    S = np.ones(3)
+    E = np.array([[10.0, 2.0, 0.0]] * 3) * 128
+    budget = (2 * BITS[1] + BITS[0]) / 3 * (1 + 1e-12)
+    for which in ("oracle", "library"):
+        g, _ = solve(which, ora, n, S, E, np.full(3, 7, np.uint32), budget)
+        assert list(g) == [0, 0, 0], (which, g)
+    opt, _ = brute(n, S, E, np.full(3, 7), budget * n.sum())
+    assert opt == pytest.approx((2.0 + 2.0 + 10.0) * 128)
 
 
 def test_oracle_knapsack_closed_forms(ora):
@@ -121,30 +150,38 @@ def test_oracle_block_sensitivity(ora):
     assert S[1] == 2048.0 * sum(i * i for i in range(129, 201))
 
 
+def lagrangian_minimiser(n, S, E, allowed, lam, bits):
+    """Per unit, the allowed grid minimising S*E + lam*n*bits, ties to fewer bits."""
+    out = []
+    for i in range(len(n)):
+        opts = sorted((h for h in range(3) if allowed[i] >> h & 1), key=lambda h: (bits[h], h))
+        costs = [S[i] * E[i, h] + lam * (n[i] * bits[h]) for h in opts]
+        out.append(opts[int(np.argmin(costs))])
+    return np.array(out)
+
+
 @pytest.mark.parametrize("seed", range(20))
 def test_library_allocator_matches_oracle(ora, seed):
+    """Same grids as the oracle's hull walk; the library's multiplier lies at or above the
+    oracle's (the slope of the first group left out) and its Lagrangian minimiser is that
+    same assignment."""
     rng = np.random.default_rng(100 + seed)
     m = int(rng.integers(1, 400))
     n, S, E, allowed = random_instance(rng, m, masks=(7, 6, 3, 5, 1, 2, 4))
     if seed % 4 == 0:
         S[rng.integers(0, m, m // 3)] = 0.0
-    for budget in (1.75, 2.0, 2.4, 3.0):
+    cases = [(b, None) for b in (1.75, 2.0, 2.4, 3.0)] + [(2.5, np.array([1.6 + 1 / 8, 2.125, 3.125]))]
+    for budget, bits in cases:
         try:
-            g2, l2 = ora.allocate(n, S, E, allowed, budget)
+            g2, l2 = ora.allocate(n, S, E, allowed, budget, bits)
         except ValueError:
             with pytest.raises(ql.QLinearError):
-                ql.allocate(n, S, E, allowed, budget)
+                ql.allocate(n, S, E, allowed, budget, bits)
             continue
-        g1, l1 = ql.allocate(n, S, E, allowed, budget)
-        assert np.array_equal(g1, g2) and l1 == l2
-    # explicit bits per grid (1.6-bit ternary storage)
-    bits = np.array([1.6 + 1 / 8, 2.125, 3.125])
-    try:
-        g2, l2 = ora.allocate(n, S, E, allowed, 2.5, bits)
-        g1, l1 = ql.allocate(n, S, E, allowed, 2.5, bits)
-        assert np.array_equal(g1, g2) and l1 == l2
-    except ValueError:
-        pass
+        g1, l1 = ql.allocate(n, S, E, allowed, budget, bits)
+        assert np.array_equal(g1, g2), (budget, np.flatnonzero(g1 != g2)[:5])
+        assert l1 >= l2
+        assert np.array_equal(lagrangian_minimiser(n, S, E, allowed, l1, BITS if bits is None else bits), g1)
 
 
 def test_allocate_argument_errors():

@@ -39,6 +39,16 @@ def test_rtn_noise_matches_oracle(ora, dev, N, K):
     assert np.array_equal(ql.rtn_noise(W.to(dev)).cpu().numpy(), E)
 
 
+@pytest.mark.parametrize("N,K", [(1, 128), (130, 256), (200, 2048), (1024, 17408), (70, 384)])
+def test_block_sensitivity_matches_oracle(ora, dev, N, K):
+    """qlinear_block_sensitivity against the oracle: bit-exact (ascending fp64 sums on both sides)."""
+    x = synth.activations(1, K, seed=N + K).view(-1)
+    g = torch.randn(N, generator=torch.Generator().manual_seed(K)) * 3.0
+    S = ql.block_sensitivity(x.to(dev), g.to(dev)).cpu().numpy()
+    S_ref = ora.block_sensitivity(synth.bf16_bits(x), g.numpy())
+    assert np.array_equal(S, S_ref)
+
+
 def oracle_units(ora, wl, wi, layer, granularity, dev):
     """The oracle's units from the same seeded inputs (drawn on the device, as the
     library's pipeline draws them, and copied to the host)."""
@@ -75,10 +85,11 @@ def test_qwen3_1p7b_layer_allocation_matches_oracle(ora, dev, granularity):
     keys, n, S, E, allowed = oracle_units(ora, wl, wi, 0, granularity, dev)
     assert units.keys == keys and np.array_equal(units.weights, n)
     np.testing.assert_allclose(units.noise, E, rtol=1e-12)
-    np.testing.assert_allclose(units.sensitivity, S, rtol=1e-12)
+    assert np.array_equal(units.sensitivity, S)  # same sums, same order: bit-exact
     g_ref, lam_ref = ora.allocate(n, S, E, allowed, 2.0)
     assert np.array_equal(grids, g_ref)
-    assert lam == pytest.approx(lam_ref, rel=1e-9)
+    # the library's multiplier sits inside the interval the oracle's assignment holds on
+    assert lam >= lam_ref * (1 - 1e-9)
     sh = allocation.shares(units, grids)
     bits = sum(sh[g] * ora.GRID_BITS[g] for g in range(3))
     print(f"{granularity}: shares T {sh[0]:.3f} I2 {sh[1]:.3f} I3 {sh[2]:.3f}, {bits:.4f} bits/weight", flush=True)

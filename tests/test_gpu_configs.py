@@ -88,10 +88,12 @@ def test_config1_qwen3_1p7b_layer_every_row(ora, dev):
 
 
 @pytest.mark.parametrize("layer", [0, 39])
-@pytest.mark.parametrize("M", [1, 4, 16])
-def test_config3_qwen3_14b_layer_sampled(ora, dev, layer, M):
-    """A Qwen3-14B layer at full size, mixed grids; M=1 in the grouped launch, M=4 through
-    qlinear_gemv (MFMA path), M=16 through qlinear_gemm; 48 seeded rows per matrix."""
+@pytest.mark.parametrize("M,path", [(1, "grouped"), (4, "grouped"), (16, "grouped"), (4, "mfma"), (16, "mfma")])
+def test_config3_qwen3_14b_layer_sampled(ora, dev, layer, M, path):
+    """A Qwen3-14B layer at full size (down_proj K = 17408 included), mixed grids, 48 seeded rows
+    per matrix.  path "grouped": the grouped launch the benchmark times (batch-1 kernel at M = 1,
+    batched-decode kernel at M = 4 and 16; GEMV bar).  path "mfma": qlinear_gemv (M = 4) and
+    qlinear_gemm (M = 16) on the LDS-tile MFMA path (GEMM bar)."""
     wl = configs.WORKLOADS["qwen3_14b_stack"]
     wi = wl_index(wl.name)
     alloc = synth.allocation(wl, layer)
@@ -103,8 +105,9 @@ def test_config3_qwen3_14b_layer_sampled(ora, dev, layer, M):
         W = synth.weight(lin.N, lin.K, synth.weight_seed(wi, layer, mi), device=dev)
         pw = ql.quantize_pack(W, alloc[lin.name])
         mats.append((lin, W, pw))
-    if M == 1:
-        items = [(pw, xs[lin.x_slot], torch.empty((1, lin.N), device=dev)) for lin, _, pw in mats]
+    note(f"14B layer {layer} M={M} path={path}")
+    if path == "grouped":
+        items = [(pw, xs[lin.x_slot], torch.full((M, lin.N), float("nan"), device=dev)) for lin, _, pw in mats]
         ql.GroupedGemv(items).run()
         ys = [y for _, _, y in items]
     elif M <= 8:
@@ -112,9 +115,9 @@ def test_config3_qwen3_14b_layer_sampled(ora, dev, layer, M):
     else:
         ys = [ql.gemm(xs[lin.x_slot], pw) for lin, _, pw in mats]
     torch.cuda.synchronize()
-    tol, trip = (GEMV_TOL, TRIP_GEMV) if M == 1 else (GEMM_TOL, TRIP_GEMM)
+    tol, trip = (GEMV_TOL, TRIP_GEMV) if path == "grouped" else (GEMM_TOL, TRIP_GEMM)
     for (lin, W, pw), y in zip(mats, ys):
-        note(f"14B layer {layer} M={M}: {lin.name} {lin.N}x{lin.K}")
+        note(f"14B layer {layer} M={M} {path}: {lin.name} {lin.N}x{lin.K}")
         rows = np.sort(rng.choice(lin.N, size=48, replace=False))
         y64 = oracle_rows(ora, W, rows, alloc[lin.name], synth.bf16_bits(xs[lin.x_slot].cpu()))
         yg = y[:, torch.from_numpy(rows).to(dev)].cpu().numpy()
