@@ -134,6 +134,7 @@ __device__ __forceinline__ void c4_task(const ql_gemv_desc* __restrict__ descs, 
                                         const uint8_t* lut, int lane) {
   const ql_gemv_desc& d = descs[find_desc(descs, count, t)];
   if (d.grid != QL_GRID_C4) return;  // not a container: nothing of it is read
+  if (!task_in_entry(d, t)) return;
   const int64_t slab = t - d.slab_begin;
   const int K = d.K, G8 = (K / kGroup + 7) / 8;
   const uint8_t* codes = static_cast<const uint8_t*>(d.packed) + slab * (int64_t)kSlab * (K / 2);

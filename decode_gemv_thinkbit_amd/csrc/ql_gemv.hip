@@ -533,6 +533,7 @@ __device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs
                                           const uint8_t* lut, int lane, uint32_t* state) {
   static_assert(M == 1, "split partial sums hold one value per lane");
   const ql_gemv_desc& d = descs[find_desc(descs, count, t)];
+  if (!task_in_entry(d, t)) return;
   const SplitTask st(d, t);
   const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
   int gr;

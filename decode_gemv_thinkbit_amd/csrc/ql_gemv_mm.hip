@@ -434,6 +434,7 @@ __device__ void run_i3(const uint8_t* codes, const uint16_t* scales, const XSrc&
 __device__ __forceinline__ void mm_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t, int M,
                                         const uint8_t* lut, int lane, uint32_t* state) {
   const ql_gemv_desc& d = descs[find_desc(descs, count, t)];
+  if (!task_in_entry(d, t)) return;
   const SplitTask st(d, t);
   const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
   int gr;

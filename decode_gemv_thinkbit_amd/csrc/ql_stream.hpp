@@ -162,6 +162,16 @@ __device__ __forceinline__ int find_desc(const ql_gemv_desc* __restrict__ descs,
   return lo;
 }
 
+// True when task t lies inside descriptor d's own tasks.  A task total larger
+// than the one prepare returned would map its extra tasks onto the last entry
+// with slab indices past its rows; such tasks are dropped instead of reading
+// past the entry's packed and scale buffers.
+__device__ __forceinline__ bool task_in_entry(const ql_gemv_desc& d, int64_t t) {
+  const int64_t nslabs = ((int64_t)d.N + kSlab - 1) / kSlab;
+  const int64_t parts = d.kparts > 1 ? d.kparts : 1;
+  return t - (int64_t)d.slab_begin < nslabs * parts;
+}
+
 // ---------------------------------------------------------------- split-K
 // qlinear_grouped_prepare_split may cut the input of every slab of an entry
 // into kparts parts, each a task of its own: whole 640-input periods on

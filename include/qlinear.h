@@ -163,9 +163,9 @@ typedef struct {
 
 /* Prepare a descriptor list (host array) for qlinear_gemv_grouped (or, for a list of 4-bit
  * containers, qlinear_c4_gemv_grouped; a list must not mix the two): check every entry, sort
- * the entries by K, largest first (stable; the products are independent, so their order
- * is free), fill slab_begin and return the total number of 64-row slabs (the task count),
- * or -1 on a bad descriptor.  Longest-first task order plus dynamic task fetching keeps
+ * the entries by task length (K / kparts; here kparts = 1, so by K), largest first (stable;
+ * the products are independent, so their order is free), fill slab_begin and return the
+ * total number of 64-row slabs (the task count), or -1 on a bad descriptor.  Longest-first task order plus dynamic task fetching keeps
  * the persistent launch balanced when row lengths differ (a K = 12288 row costs three
  * K = 4096 rows).  Entries of equal K keep the caller's order: listing them by stored
  * bytes per row, largest first (3-bit before 2-bit before ternary), ends the launch on
@@ -183,7 +183,8 @@ int64_t qlinear_grouped_prepare(ql_gemv_desc *descs, int32_t count);
  * deterministic.  An entry with kparts > 0 keeps that many parts (at most its period
  * count and QL_MAX_KPARTS); for kparts == 0 the parts are chosen so that the launch has
  * at least min_tasks tasks where rows allow (e.g. half of qlinear_grouped_wave_slots(M);
- * min_tasks <= 0 splits nothing).  Tasks are ordered by part length, longest first.  A list of 4-bit containers
+ * min_tasks <= 0 splits nothing).  Entries are sorted by task length K / kparts, longest
+ * first (stable).  A list of 4-bit containers
  * is never split.  *state_words (host) receives the size of the launch's state buffer in
  * 32-bit words: QL_SCHED_WORDS, plus, per split entry, one 128-byte counter line per slab
  * and 1024 words of partial sums per part of each slab.  Returns the task count, or -1. */
@@ -212,7 +213,9 @@ int64_t qlinear_grouped_wave_slots(int32_t M);
  * qlinear_grouped_prepare_split otherwise): its counters must be all zero when a launch
  * starts, and every launch that runs to completion leaves them zero again, so one zeroing
  * at allocation serves any number of launches.  Launches that share one state buffer must
- * not overlap (enqueue them on one stream).  The products are independent: no y may alias
+ * not overlap (enqueue them on one stream).  total_tasks and the state buffer's size must be
+ * the ones prepare reported for this list: tasks past an entry's own range are dropped on the
+ * device, but a state buffer smaller than state_words is not detected.  The products are independent: no y may alias
  * another entry's x or y. */
 ql_status qlinear_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_tasks, int32_t M,
                                uint32_t *sched, hipStream_t stream);

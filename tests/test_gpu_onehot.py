@@ -96,10 +96,11 @@ def test_gemv_batch1_one_hot(ora, dev, N, K, grid):
     pw, w32 = weight_case(ora, dev, N, K, grid, seed=11 * N + K)
     ks = positions(K)
     X = one_hot(ks, K, dev)
-    Y = torch.full((len(ks), N), float("nan"), device=dev)
+    # one output tensor per launch: the library takes 16-byte aligned pointers only
+    Y = [torch.full((1, N), float("nan"), device=dev) for _ in ks]
     for i in range(len(ks)):
-        ql.gemv(X[i:i + 1], pw, out=Y[i:i + 1])
-    assert_columns(Y.cpu().numpy(), w32, ks, "gemv M=1")
+        ql.gemv(X[i:i + 1], pw, out=Y[i])
+    assert_columns(torch.cat(Y).cpu().numpy(), w32, ks, "gemv M=1")
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
@@ -112,15 +113,16 @@ def test_grouped_batch1_one_hot(ora, dev, N, K, grid, split):
     pw, w32 = weight_case(ora, dev, N, K, grid, seed=13 * N + K)
     ks = positions(K)
     X = one_hot(ks, K, dev)
-    Y = torch.full((len(ks), N), float("nan"), device=dev)
-    items = [(pw, X[i:i + 1], Y[i:i + 1]) for i in range(len(ks))]
+    Y = [torch.full((1, N), float("nan"), device=dev) for _ in ks]
+    items = [(pw, X[i:i + 1], Y[i]) for i in range(len(ks))]
     grp = ql.GroupedGemv(items, split=split)
     for rep in range(2):
         grp.run()
         torch.cuda.synchronize()
         assert int(grp.sched.abs().sum().item()) == 0 or split is not None
-        assert_columns(Y.cpu().numpy(), w32, ks, f"grouped M=1 split={split} rep {rep}")
-        Y.fill_(float("nan"))
+        assert_columns(torch.cat(Y).cpu().numpy(), w32, ks, f"grouped M=1 split={split} rep {rep}")
+        for y in Y:
+            y.fill_(float("nan"))
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
@@ -133,10 +135,11 @@ def test_grouped_batched_one_hot(ora, dev, N, K, grid, M):
     ks = positions(K)
     ks = ks + ks[: (-len(ks)) % M]  # whole items of M tokens
     X = one_hot(ks, K, dev)
-    Y = torch.full((len(ks), N), float("nan"), device=dev)
-    items = [(pw, X[i:i + M], Y[i:i + M]) for i in range(0, len(ks), M)]
+    Y = [torch.full((M, N), float("nan"), device=dev) for _ in range(0, len(ks), M)]
+    items = [(pw, X[i:i + M], Y[i // M]) for i in range(0, len(ks), M)]
     for split in (None, "auto"):
         ql.GroupedGemv(items, split=split).run()
         torch.cuda.synchronize()
-        assert_columns(Y.cpu().numpy(), w32, ks, f"batched M={M} split={split}")
-        Y.fill_(float("nan"))
+        assert_columns(torch.cat(Y).cpu().numpy(), w32, ks, f"batched M={M} split={split}")
+        for y in Y:
+            y.fill_(float("nan"))
