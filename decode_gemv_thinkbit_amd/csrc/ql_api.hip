@@ -57,6 +57,18 @@ ql_status check_ptrs(std::initializer_list<const void*> ps) {
   return QL_OK;
 }
 
+}  // namespace
+
+ql_status ql::set_error(ql_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+namespace {
+
 #define QL_TRY(x)                    \
   do {                               \
     ql_status _s = (x);              \

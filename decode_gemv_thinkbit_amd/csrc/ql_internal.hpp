@@ -5,6 +5,9 @@
 
 namespace ql {
 
+// Records the message qlinear_last_error() returns on this thread; returns st.
+ql_status set_error(ql_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 hipError_t launch_quantize(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const float* W, int8_t* codes,
                            uint16_t* scales, hipStream_t stream);
 hipError_t launch_pack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,

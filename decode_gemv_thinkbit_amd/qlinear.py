@@ -20,6 +20,7 @@ GRID_C4 = 4  # 4-bit container baseline (not a ThinkBit grid)
 GROUP, SLAB, BLOCK = 128, 64, 128
 QL_SCHED_WORDS = 4128  # uint32 words of grouped-launch scheduler state
 QL_MAX_KPARTS = 16  # split-K parts per slab at most
+QL_NOALLOC_STATE_WORDS = 4194304  # uint32 words of the library's static grouped-launch state
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "libqlinear.so")
@@ -83,6 +84,7 @@ def lib():
         L.qlinear_grouped_wave_slots.argtypes = [ctypes.c_int32]
         L.qlinear_grouped_wave_slots.restype = i64
         L.qlinear_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp, vp]
+        L.qlinear_gemv_grouped_noalloc.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, i64, vp]
         L.qlinear_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.qlinear_gemm_workspace_bytes.restype = sz
         L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -110,7 +112,7 @@ def lib():
         L.qlinear_c4_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp, vp]
         for name in ("qlinear_block_offsets", "qlinear_quantize", "qlinear_pack", "qlinear_pack_scales",
                      "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
-                     "qlinear_gemv_grouped", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
+                     "qlinear_gemv_grouped", "qlinear_gemv_grouped_noalloc", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
                      "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped", "qlinear_rtn_noise",
                      "qlinear_allocate", "qlinear_block_sensitivity", "qlinear_lb_pack", "qlinear_lb_gemv"):
             getattr(L, name).restype = i32
@@ -479,13 +481,16 @@ def wave_slots(M=1):
 class GroupedGemv:
     """One persistent launch over many independent (x, W, y) products with the same M."""
 
-    def __init__(self, items, split=None):
+    def __init__(self, items, split=None, noalloc=False):
         """items: list of (PackedWeight or C4Weight, x [M,K] bf16, y [M,N] fp32); all of one kind.
 
         split: None (one task per 64-row slab), "auto" (cut the slabs' input into parts until
         the launch has half as many tasks as the device has wave slots, where rows allow: the
         best measured point for the per-layer launches of the 8B pass at M = 1 and 4),
-        an int (that many parts for every item) or a list of ints (parts per item; 0 = auto)."""
+        an int (that many parts for every item) or a list of ints (parts per item; 0 = auto).
+
+        noalloc: run through qlinear_gemv_grouped_noalloc, whose scheduler and split-K state
+        live in the library's static device array (no state tensor is allocated here)."""
         if not items:
             raise ValueError("no items")
         self.items = items
@@ -540,9 +545,17 @@ class GroupedGemv:
         raw = bytes(memoryview(arr))
         self.count = len(items)
         self.descs = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(items[0][1].device)
+        self.state_words = words
+        self.noalloc = bool(noalloc)
+        if self.noalloc and (self.containers or words > QL_NOALLOC_STATE_WORDS):
+            raise ValueError("noalloc launches take native grids and at most QL_NOALLOC_STATE_WORDS of state")
         # task counters and split state: zero once here, counters left zero by every completed launch
-        self.sched = torch.zeros(words, dtype=torch.int32, device=items[0][1].device)
+        self.sched = None if self.noalloc else torch.zeros(words, dtype=torch.int32, device=items[0][1].device)
 
     def run(self):
+        if self.noalloc:
+            _check(lib().qlinear_gemv_grouped_noalloc(_ptr(self.descs), self.count, self.total, self.M,
+                                                      self.state_words, _stream()), "gemv_grouped_noalloc")
+            return
         fn = lib().qlinear_c4_gemv_grouped if self.containers else lib().qlinear_gemv_grouped
         _check(fn(_ptr(self.descs), self.count, self.total, self.M, _ptr(self.sched), _stream()), "gemv_grouped")

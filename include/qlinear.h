@@ -220,6 +220,21 @@ int64_t qlinear_grouped_wave_slots(int32_t M);
 ql_status qlinear_gemv_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_tasks, int32_t M,
                                uint32_t *sched, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): qlinear_gemv_grouped without the caller's state
+ * buffer.  The task counters and split-K partial sums live in a static device array of the
+ * library, QL_NOALLOC_STATE_WORDS uint32 (16 MiB) per GPU, held until the process ends.
+ * state_words is what qlinear_grouped_prepare (QL_SCHED_WORDS) or qlinear_grouped_prepare_split
+ * reported for the descriptor list; a launch that needs more than the array holds is rejected
+ * with QL_EINVAL before anything is enqueued.  The first call on a GPU clears the array with a
+ * fill kernel on `stream`; every completed launch leaves its counters zero again.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (different streams, or
+ * other threads) race and give wrong results: serialize them on one stream.  Same kernels and
+ * results as qlinear_gemv_grouped for the same list.  Allocates nothing. */
+#define QL_NOALLOC_STATE_WORDS 4194304
+ql_status qlinear_gemv_grouped_noalloc(const ql_gemv_desc *descs, int32_t count, int64_t total_tasks, int32_t M,
+                                       int64_t state_words, hipStream_t stream);
+
 /* Batched GEMM for 1 <= M (tuned for 16..512): tiles of codes are decoded into LDS as bf16
  * (codes are exact in bf16) and contracted on MFMA (bf16 x bf16 -> fp32); the group scale
  * is applied to each 128-deep partial product in fp32.  Dequantizing to bf16 and computing
