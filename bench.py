@@ -49,9 +49,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_pass(wl, wl_index, M, dev, tables=None):
+def arena_views(sizes, dev, align=256):
+    """One device allocation carved into aligned views: [(uint8 view, bf16 view)] per (bytes, elements)."""
+    import torch
+    offs, total = [], 0
+    for nb, ne in sizes:
+        a = total
+        b = (a + nb + align - 1) // align * align
+        offs.append((a, b))
+        total = (b + 2 * ne + align - 1) // align * align
+    arena = torch.empty(max(total, align), dtype=torch.uint8, device=dev)
+    return [(arena[a:a + nb], arena[b:b + 2 * ne].view(torch.bfloat16)) for (a, b), (nb, ne) in zip(offs, sizes)]
+
+
+def build_pass(wl, wl_index, M, dev, tables=None, arena=True):
     """Quantize and pack every linear of the workload on the GPU; return items and bookkeeping.
-    tables: {layer: {linear: grid per 128-row block}} in place of the seeded mixed allocation."""
+    tables: {layer: {linear: grid per 128-row block}} in place of the seeded mixed allocation.
+    arena: place every packed matrix and scale array in one device allocation (as a model
+    loader would), in pass order, instead of one allocation per tensor."""
     import torch
     from decode_gemv_thinkbit_amd import qlinear as ql
     from decode_gemv_thinkbit_amd import synth
@@ -59,15 +74,22 @@ def build_pass(wl, wl_index, M, dev, tables=None):
     items, meta = [], []
     stored = 0
     xs = {}
+    allocs = [synth.allocation(wl, layer) if tables is None else tables[layer] for layer in range(wl.layers)]
+    views = None
+    if arena:
+        views = iter(arena_views([ql.packed_sizes(lin.N, lin.K, allocs[layer][lin.name])
+                                  for layer in range(wl.layers) for lin in wl.linears], dev))
     for layer in range(wl.layers):
-        alloc = synth.allocation(wl, layer) if tables is None else tables[layer]
+        alloc = allocs[layer]
         for slot in ("attn", "o", "mlp", "down"):
-            K = next(l.K for l in wl.linears if l.x_slot == slot)
-            xs[(layer, slot)] = synth.activations(M, K, synth.x_seed(wl_index, layer, slot, M), device=dev)
+            K = next((l.K for l in wl.linears if l.x_slot == slot), None)
+            if K is not None:
+                xs[(layer, slot)] = synth.activations(M, K, synth.x_seed(wl_index, layer, slot, M), device=dev)
         for mi, lin in enumerate(wl.linears):
             seed = synth.weight_seed(wl_index, layer, mi)
             W = synth.weight(lin.N, lin.K, seed, device=dev)
-            pw = ql.quantize_pack(W, alloc[lin.name])
+            pk, ps = next(views) if views is not None else (None, None)
+            pw = ql.quantize_pack(W, alloc[lin.name], pk, ps)
             del W
             y = torch.empty((M, lin.N), dtype=torch.float32, device=dev)
             items.append((pw, xs[(layer, lin.x_slot)], y))
@@ -99,6 +121,14 @@ def build_container_pass(wl, wl_index, xs, dev):
             stored += cw.nbytes
     torch.cuda.synchronize()
     return items, stored
+
+
+def stats_us(ms_list):
+    """median, p10, p90 (microseconds) of a list of milliseconds."""
+    import numpy as np
+    a = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
 
 
 def time_grouped(grp, warmup, steps):
@@ -227,6 +257,102 @@ def layered_leg(dev, warmup, steps, wl_name="qwen3_8b_pass", Ms=(1, 4)):
     torch.cuda.empty_cache()
     return {"variant": "dependency-respecting: 4 grouped launches per layer in one HIP graph",
             "kernels": "gemv_grouped_kernel<1> (M = 1), gemv_mm_grouped_kernel (M > 1)", "points": out}
+
+
+def small_leg(dev, reps=50, flush_mb=512):
+    """The two small workloads at batch 1: one 2048x2048 2-bit linear and one Qwen3-1.7B-shaped
+    layer (mixed grids).  Their weights (1.1 / 12.7 MB) fit in the last-level cache, so before
+    every timed launch a 512 MB buffer is written, which evicts them: each launch reads its
+    weights from HBM.  HIP events around each launch; median and p10/p90 over `reps`."""
+    import torch
+    from decode_gemv_thinkbit_amd import configs
+    from decode_gemv_thinkbit_amd import qlinear as ql
+
+    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    out = []
+    for wl_name in ("linear2048_i2", "qwen3_1p7b_layer"):
+        wl = configs.WORKLOADS[wl_name]
+        wi = list(configs.WORKLOADS).index(wl_name)
+        items, meta, stored, _ = build_pass(wl, wi, 1, dev)
+        variants = [("grouped", lambda: ql.GroupedGemv(items)),
+                    ("grouped split-K auto", lambda: ql.GroupedGemv(items, split="auto"))]
+        for vname, make in variants:
+            grp = make()
+            for _ in range(3):
+                grp.run()
+            torch.cuda.synchronize()
+            ts = []
+            for r in range(reps):
+                flush.fill_(r & 255)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                grp.run()
+                b.record(st)
+                ts.append((a, b))
+            torch.cuda.synchronize()
+            sts = stats_us([a.elapsed_time(b) for a, b in ts])
+            err, _nw, _ = parity_sample(items, meta, 1, dev, rows_per=64)
+            med = sts["median_us"]
+            out.append({"workload": wl_name, "variant": vname, "launches": 1, "tasks": grp.total,
+                        "stored_bytes": stored, **sts, "gbs_median": round(stored / (med * 1e-6) / 1e9, 1),
+                        "pct_hbm_peak_median": round(100 * stored / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                        "parity_max_err_over_row_norm": err, "parity_ok": err <= 2e-3})
+            log(f"small {wl_name} {vname}: median {med:.2f} us (p10 {sts['p10_us']:.2f}, p90 {sts['p90_us']:.2f}), "
+                f"{stored / (med * 1e-6) / 1e9:.0f} GB/s, parity {err:.3g}")
+        del items
+    del flush
+    torch.cuda.empty_cache()
+    return {"cache": f"{flush_mb} MB written before every launch", "timing": "HIP events per launch",
+            "points": out}
+
+
+def per_matrix_leg(dev, reps=3, wl_name="qwen3_8b_pass"):
+    """The 8B pass as 252 single-matrix launches (split-K chosen per launch), each timed with HIP
+    events: per-linear medians of the kernel durations (a rocprofv3 trace of the same run gives
+    the per-kernel figures).  A matrix is read again only after the other 251, so every launch
+    streams its weights from HBM."""
+    import numpy as np
+    import torch
+    from decode_gemv_thinkbit_amd import configs
+    from decode_gemv_thinkbit_amd import qlinear as ql
+
+    wl = configs.WORKLOADS[wl_name]
+    wi = list(configs.WORKLOADS).index(wl_name)
+    items, meta, stored, _ = build_pass(wl, wi, 1, dev)
+    grps = [ql.GroupedGemv([it], split="auto") for it in items]
+    for g in grps:
+        g.run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = []
+    for _ in range(reps):
+        row = []
+        for g in grps:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            g.run()
+            b.record(st)
+            row.append((a, b))
+        evs.append(row)
+    torch.cuda.synchronize()
+    us = np.array([[a.elapsed_time(b) * 1e3 for a, b in row] for row in evs])  # [reps][matrix]
+    med = np.median(us, axis=0)
+    out = []
+    for lin in wl.linears:
+        idx = [i for i, m in enumerate(meta) if m[2].name == lin.name]
+        nb = [items[i][0].nbytes for i in idx]
+        out.append({"linear": lin.name, "N": lin.N, "K": lin.K, "matrices": len(idx),
+                    "tasks": grps[idx[0]].total, "median_us": round(float(np.median(med[idx])), 2),
+                    "p10_us": round(float(np.percentile(med[idx], 10)), 2),
+                    "p90_us": round(float(np.percentile(med[idx], 90)), 2),
+                    "gbs_median": round(float(np.median(np.array(nb) / (med[idx] * 1e-6) / 1e9)), 1)})
+        log(f"per-matrix {lin.name} {lin.N}x{lin.K}: median {out[-1]['median_us']} us, {out[-1]['gbs_median']} GB/s")
+    total = float(med.sum())
+    del grps, items
+    torch.cuda.empty_cache()
+    return {"variant": "one launch per matrix (252 launches per pass), split-K auto",
+            "sum_of_medians_us": round(total, 1), "stored_bytes": stored, "per_linear": out}
 
 
 def read_ceiling(dev, nbytes, warmup, steps):
@@ -480,39 +606,70 @@ def parity_sample(items, meta, M, dev, rows_per=32):
     return worst, worst_nw, len(picks)
 
 
-def cpu_baseline(wl, wl_index, M, budget_s=20.0):
-    """The oracle (packed decode + fp64 product) on host threads over layer 0's seven linears."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_layer(wl, wl_index, layer, M):
+    """The oracle's packed buffers of one layer's linears (quantized and packed on the host)."""
     import oracle
     from decode_gemv_thinkbit_amd import synth
 
-    threads = os.cpu_count() or 1
-    alloc = synth.allocation(wl, 0)
-    mats = []
-    stored = 0
+    alloc = synth.allocation(wl, layer)
+    mats, stored = [], 0
     for mi, lin in enumerate(wl.linears):
-        W = synth.weight(lin.N, lin.K, synth.weight_seed(wl_index, 0, mi)).numpy()
+        W = synth.weight(lin.N, lin.K, synth.weight_seed(wl_index, layer, mi)).numpy()
         c, s = oracle.quantize(W, alloc[lin.name])
         packed = oracle.pack(c, alloc[lin.name])
         ps = oracle.pack_scales(s, lin.K)
-        x = synth.bf16_bits(synth.activations(M, lin.K, synth.x_seed(wl_index, 0, lin.x_slot, M)))
+        x = synth.bf16_bits(synth.activations(M, lin.K, synth.x_seed(wl_index, layer, lin.x_slot, M)))
         mats.append((packed, ps, x, lin, alloc[lin.name]))
         stored += packed.size + 2 * ps.size
-    reps = 0
-    t0 = time.perf_counter()
+    return mats, stored
+
+
+def time_oracle(mats, threads, budget_s, max_reps=5):
+    """Seconds per pass over `mats` (packed decode + fp64 product), repeated within a time budget."""
+    import oracle
+    reps, t0 = 0, time.perf_counter()
     while True:
         for packed, ps, x, lin, g in mats:
             oracle.gemv_packed(packed, ps, x, lin.N, lin.K, g, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
-        if el > budget_s / 2 or reps >= 5:
-            break
-    sec = el / reps
+        if el > budget_s / 2 or reps >= max_reps:
+            return el / reps, reps
+
+
+def cpu_baseline(wl, wl_index, M, budget_s=20.0):
+    """The oracle (packed decode + fp64 product) on all host threads over layer 0's seven linears;
+    beside it, one thread on the 2048x2048 2-bit linear, the Qwen3-1.7B layer and layer 0 of the pass."""
+    from decode_gemv_thinkbit_amd import configs
+
+    threads = os.cpu_count() or 1
+    mats, stored = oracle_layer(wl, wl_index, 0, M)
+    sec, reps = time_oracle(mats, threads, budget_s)
+    single = []
+    for name in ("linear2048_i2", "qwen3_1p7b_layer", wl.name):
+        w = configs.WORKLOADS[name]
+        m1, st1 = (mats, stored) if name == wl.name else oracle_layer(w, list(configs.WORKLOADS).index(name), 0, M)
+        sec1, reps1 = time_oracle(m1, 1, 4.0, max_reps=3)
+        single.append({"workload": name, "layer": 0, "stored_bytes": st1, "us": round(sec1 * 1e6, 1),
+                       "gbs": round(st1 / sec1 / 1e9, 4), "reps": reps1})
+        log(f"oracle single-thread {name} layer 0: {sec1 * 1e3:.1f} ms ({st1 / sec1 / 1e9:.3f} GB/s)")
     return {"value": round(stored / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"layer 0 of the pass (7 linears, {sum(m[3].N * m[3].K for m in mats) / 1e6:.0f}M weights, "
                       f"{stored / 1e6:.1f} MB stored), packed decode + fp64 product, {reps} rep(s), "
                       f"{sec * 1e3:.0f} ms per layer on {threads} threads",
-            "us_per_pass_extrapolated": round(sec * wl.layers * 1e6, 1)}
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "us_per_pass_extrapolated": round(sec * wl.layers * 1e6, 1), "single_thread": single}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -581,6 +738,11 @@ def main():
     ap.add_argument("--no-batched", action="store_true", help="skip the small-batch (M = 4, 16) decode leg")
     ap.add_argument("--no-layered", action="store_true",
                     help="skip the dependency-respecting pass (4 launches per layer, HIP graph)")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the 2048x2048 2-bit linear and Qwen3-1.7B layer leg (cache flushed per launch)")
+    ap.add_argument("--no-per-matrix", action="store_true", help="skip the one-launch-per-matrix leg")
+    ap.add_argument("--no-arena", action="store_true",
+                    help="allocate every packed tensor separately instead of in one arena")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -604,7 +766,7 @@ def main():
     M = 1
     log(f"building {wl.name}: {wl.layers} layers, {wl.weights / 1e9:.3f}G weights")
     t0 = time.time()
-    items, meta, stored, _ = build_pass(wl, wl_index, M, dev)
+    items, meta, stored, _ = build_pass(wl, wl_index, M, dev, arena=not args.no_arena)
     log(f"packed in {time.time() - t0:.1f}s: {stored / 1e9:.4f} GB stored (codes + scales)")
     grp = ql.GroupedGemv(items)
     codes_b, x_b, y_b = algorithmic_bytes(items, M)
@@ -624,8 +786,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
     avg_kern_ms = sum(kern_ms) / len(kern_ms)
     gbs = stored / (ms_step * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us (kernel avg {avg_kern_ms * 1e3:.1f} us, min {min(kern_ms) * 1e3:.1f}), "
-        f"{gbs:.0f} GB/s")
+    kst = stats_us(kern_ms)
+    log(f"step {ms_step * 1e3:.1f} us (kernel avg {avg_kern_ms * 1e3:.1f} us, median {kst['median_us']:.1f}, "
+        f"p10 {kst['p10_us']:.1f}, p90 {kst['p90_us']:.1f}), {gbs:.0f} GB/s")
 
     result = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -635,7 +798,8 @@ def main():
         "config": {"workload": wl.name, "layers": wl.layers, "hidden": 4096, "M": M,
                    "grids": "mixed per 128-row block: 75.3% ternary / 6.0% 2-bit / 18.7% 3-bit, q,k 3-bit",
                    "variant": "grouped single launch", "stored_bytes": stored,
-                   "us_per_pass": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+                   "us_per_pass": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                   "kernel_us": kst, "arena": not args.no_arena},
     }
     alg = codes_b + x_b + y_b
     ach = alg / (avg_kern_ms * 1e-3) / 1e9
@@ -657,6 +821,10 @@ def main():
         log(f"parity on sampled rows of {nmat} matrices: {err:.3g} (normwise {nw:.3g})")
     del grp, items
     torch.cuda.empty_cache()
+    if not args.no_small:
+        result["small"] = small_leg(dev)
+    if not args.no_per_matrix:
+        result["per_matrix"] = per_matrix_leg(dev)
     if not args.no_ab:
         result["container_ab"] = [container_ab(args.workload, dev, args.warmup, args.steps,
                                                native=(ms_step, stored)),

@@ -120,12 +120,17 @@ ql_status qlinear_quantize(int64_t N, int64_t K, int grid, const int8_t* blk_gri
 }
 
 ql_status qlinear_pack(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
-                       const int8_t* codes, void* packed, hipStream_t stream) {
+                       const int8_t* codes, const uint16_t* scales, void* packed, uint16_t* pscales,
+                       hipStream_t stream) {
   QL_TRY(check_shape(N, K));
   QL_TRY(check_grid(grid, blk_grid, blk_off, true));
   QL_TRY(check_ptrs({codes, packed}));
-  return hip_status(ql::launch_pack(N, K, grid, blk_grid, blk_off, codes, static_cast<uint8_t*>(packed), stream),
-                    "pack launch");
+  if ((scales == nullptr) != (pscales == nullptr)) return fail(QL_EINVAL, "scales and pscales: give both or neither");
+  if (scales) QL_TRY(check_ptrs({scales, pscales}));
+  QL_TRY(hip_status(ql::launch_pack(N, K, grid, blk_grid, blk_off, codes, static_cast<uint8_t*>(packed), stream),
+                    "pack launch"));
+  if (!scales) return QL_OK;
+  return hip_status(ql::launch_scales(N, K, const_cast<uint16_t*>(scales), pscales, 0, stream), "pack scales launch");
 }
 
 ql_status qlinear_pack_scales(int64_t N, int64_t K, const uint16_t* scales, uint16_t* pscales, hipStream_t stream) {

@@ -524,26 +524,42 @@ __device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, in
 constexpr int kWaves = QL_WAVES;          // waves per workgroup
 constexpr int kWgPerCu = QL_WG_PER_CU;    // resident workgroups per CU (LDS tables: 77 KB each)
 
+// Where task t lives: its descriptor, its slab's byte offset and grid.  Split
+// from the task so that a wave's first task can be located (two or three
+// dependent scalar loads) while the workgroup builds its LDS tables.
+struct TaskLoc {
+  int di;       // descriptor index
+  int gr;       // grid of the slab
+  int64_t off;  // byte offset of the slab in the packed matrix
+};
+
+__device__ __forceinline__ TaskLoc locate_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t) {
+  TaskLoc l;
+  l.di = find_desc(descs, count, t);
+  const ql_gemv_desc& d = descs[l.di];
+  const SplitTask st(d, t);
+  l.off = task_in_entry(d, t) ? slab_offset(st.slab, d.K, d.grid, d.blk_grid, d.blk_off, &l.gr) : 0;
+  return l;
+}
+
 // One wave task: one 64-row slab of one descriptor, or one part of its input
 // when the entry is split (partial sums then meet in the state buffer).
 // Descriptor fields are re-read per task, which keeps their live ranges short
 // (the kernels stay free of register spills).
 template <int M>
-__device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t, int Mact,
-                                          const uint8_t* lut, int lane, uint32_t* state) {
+__device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs, const TaskLoc& loc, int64_t t,
+                                          int Mact, const uint8_t* lut, int lane, uint32_t* state) {
   static_assert(M == 1, "split partial sums hold one value per lane");
-  const ql_gemv_desc& d = descs[find_desc(descs, count, t)];
+  const ql_gemv_desc& d = descs[loc.di];
   if (!task_in_entry(d, t)) return;
   const SplitTask st(d, t);
   const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
-  int gr;
-  const int64_t off = slab_offset(st.slab, K, d.grid, d.blk_grid, d.blk_off, &gr);
   float y[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) y[m] = 0.0f;
-  SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + off, d.pscales + st.slab * (int64_t)G8 * kSlab * 8, d.x, K, G,
-               Mact, lane, lut};
-  run_slab<M>(gr, c, st.p0(K), st.p1(K), st.k0(K), st.k1(K), y);
+  SlabCtx<M> c{static_cast<const uint8_t*>(d.packed) + loc.off, d.pscales + st.slab * (int64_t)G8 * kSlab * 8, d.x,
+               K, G, Mact, lane, lut};
+  run_slab<M>(loc.gr, c, st.p0(K), st.p1(K), st.k0(K), st.k1(K), y);
   if (st.split()) {
     float* sl = st.slots(d, state);
     st.put(sl, lane, y[0]);
@@ -566,7 +582,7 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_kernel(ql_g
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t < total; t += (int64_t)gridDim.x * kWaves)
-    gemv_task<M>(&desc, count, t, Mact, lut, lane, nullptr);
+    gemv_task<M>(&desc, locate_task(&desc, count, t), t, Mact, lut, lane, nullptr);
 }
 
 // Many independent matrices in one persistent launch.  Slab costs differ
@@ -581,17 +597,24 @@ __global__ void __launch_bounds__(kWaves * 64, QL_WAVES_PER_EU) gemv_grouped_ker
                                                                       int count, int64_t total, int Mact,
                                                                       uint32_t* __restrict__ sched) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  build_luts<kWaves * 64>(lut);
-  __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  TaskQueues tq(sched, total, (int64_t)gridDim.x * kWaves);
   int64_t t = (int64_t)blockIdx.x * kWaves + wave;
-  if (t >= total) t = tq.next(lane);
+  // the first task's descriptor loads are in flight while the tables are built
+  const TaskLoc first = locate_task(descs, count, t < total ? t : total - 1);
+  build_luts<kWaves * 64>(lut);
+  __syncthreads();
+  TaskQueues tq(sched, total, (int64_t)gridDim.x * kWaves);
+  TaskLoc loc = first;
+  if (t >= total) {
+    t = tq.next(lane);
+    if (t >= 0) loc = locate_task(descs, count, t);
+  }
   while (t >= 0) {
     const uint32_t claim = tq.claim(lane);
-    gemv_task<M>(descs, count, t, Mact, lut, lane, sched);
+    gemv_task<M>(descs, loc, t, Mact, lut, lane, sched);
     t = tq.resolve(claim, lane);
+    if (t >= 0) loc = locate_task(descs, count, t);
   }
   tq.checkout(lane);
 }

@@ -291,11 +291,17 @@ struct TaskQueues {
   __device__ TaskQueues(uint32_t* s, int64_t total, int64_t nw)
       : sched(s), nwaves(nw), rest(total - nw), home((int)(blockIdx.x % kQueues)) {}
 
+  // Every task is some wave's first task (total <= waves): no wave draws from
+  // the queues, so the state is never touched and the check-out is skipped
+  // (it costs short launches two dependent device-scope atomics per wave).
+  __device__ bool single_round() const { return rest <= 0; }
+
   __device__ uint32_t qcount(int q) const {
     return rest > q ? (uint32_t)((rest - q + kQueues - 1) / kQueues) : 0u;
   }
   // the next task of this wave, or -1 once every queue is dry (wave-uniform)
   __device__ int64_t next(int lane) {
+    if (single_round()) return -1;
     for (;;) {
       const uint32_t cnt = qcount(home);
       if (cnt > 0) {
@@ -332,6 +338,7 @@ struct TaskQueues {
   // the wave completing a line counts the line in on the check-out word, and
   // the wave completing that resets every counter.
   __device__ void checkout(int lane) {
+    if (single_round()) return;
     const int h = (int)(blockIdx.x % kQueues);
     const int wgs = (int)gridDim.x;
     const uint32_t line_waves = (uint32_t)(((wgs - 1 - h) / kQueues + 1) * (nwaves / wgs));

@@ -69,7 +69,7 @@ def lib():
         L.qlinear_packed_scales_len.argtypes = [i64, i64]
         L.qlinear_packed_scales_len.restype = i64
         L.qlinear_quantize.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
-        L.qlinear_pack.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
+        L.qlinear_pack.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
         L.qlinear_pack_scales.argtypes = [i64, i64, vp, vp, vp]
         L.qlinear_unpack.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
         L.qlinear_unpack_scales.argtypes = [i64, i64, vp, vp, vp]
@@ -210,23 +210,44 @@ def quantize(W: torch.Tensor, grid) -> tuple[torch.Tensor, torch.Tensor]:
     return codes, scales
 
 
-def pack(codes: torch.Tensor, scales: torch.Tensor, grid) -> PackedWeight:
+def pack(codes: torch.Tensor, scales: torch.Tensor, grid, packed: Optional[torch.Tensor] = None,
+         pscales: Optional[torch.Tensor] = None) -> PackedWeight:
+    """Codes int8 [N, K] and bf16 scales [N, K/128] -> the packed layout (one qlinear_pack call).
+    packed / pscales: optional preallocated outputs (uint8 of the packed size, bf16 of
+    packed_scales_len elements), e.g. views into one arena holding a whole model."""
     _dev(codes, torch.int8, "codes")
     _dev(scales, torch.bfloat16, "scales")
     N, K = codes.shape
     if tuple(scales.shape) != (N, K // GROUP):
         raise ValueError("scales must be [N, K/128]")
     g, bg, bo, size = _grid_tables(N, K, grid, codes.device)
-    packed = torch.empty(size, dtype=torch.uint8, device=codes.device)
-    _check(lib().qlinear_pack(N, K, g, _ptr(bg), _ptr(bo), _ptr(codes), _ptr(packed), _stream()), "pack")
-    ps = torch.empty(packed_scales_len(N, K), dtype=torch.bfloat16, device=codes.device)
-    _check(lib().qlinear_pack_scales(N, K, _ptr(scales), _ptr(ps), _stream()), "pack_scales")
-    return PackedWeight(packed, ps, N, K, g, bg, bo)
+    if packed is None:
+        packed = torch.empty(size, dtype=torch.uint8, device=codes.device)
+    elif packed.dtype != torch.uint8 or packed.numel() != size or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous uint8 tensor of {size} bytes")
+    plen = packed_scales_len(N, K)
+    if pscales is None:
+        pscales = torch.empty(plen, dtype=torch.bfloat16, device=codes.device)
+    elif pscales.dtype != torch.bfloat16 or pscales.numel() != plen or not pscales.is_contiguous():
+        raise ValueError(f"pscales must be a contiguous bf16 tensor of {plen} elements")
+    _check(lib().qlinear_pack(N, K, g, _ptr(bg), _ptr(bo), _ptr(codes), _ptr(scales), _ptr(packed),
+                              _ptr(pscales), _stream()), "pack")
+    return PackedWeight(packed, pscales, N, K, g, bg, bo)
 
 
-def quantize_pack(W: torch.Tensor, grid) -> PackedWeight:
+def packed_sizes(N: int, K: int, grid) -> tuple[int, int]:
+    """(packed code bytes, packed scale elements) of an N x K weight on `grid` (int or per-block table)."""
+    if isinstance(grid, (int, np.integer)):
+        size = int(lib().qlinear_packed_bytes(N, K, int(grid)))
+    else:
+        size = int(block_offsets(N, K, np.asarray(grid))[-1])
+    return size, packed_scales_len(N, K)
+
+
+def quantize_pack(W: torch.Tensor, grid, packed: Optional[torch.Tensor] = None,
+                  pscales: Optional[torch.Tensor] = None) -> PackedWeight:
     codes, scales = quantize(W, grid)
-    return pack(codes, scales, grid)
+    return pack(codes, scales, grid, packed, pscales)
 
 
 def unpack(pw: PackedWeight) -> torch.Tensor:

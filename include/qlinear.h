@@ -107,13 +107,18 @@ int64_t qlinear_packed_scales_len(int64_t N, int64_t K);
 ql_status qlinear_quantize(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const float *W,
                            int8_t *codes, uint16_t *scales, hipStream_t stream);
 
-/* Pack codes int8 [N][K] (dev) into the layout above.  grid/blk_grid as for quantize;
+/* Pack a quantized weight (summary page, section "How it works": codes c and one bf16 scale
+ * per 128 inputs) into the layout above: codes int8 [N][K] (dev) -> packed (dev, the packed
+ * size), and scales bf16 bits [N][K/128] (dev) -> pscales (dev, qlinear_packed_scales_len
+ * elements), the packed scale array that the products read.  grid/blk_grid as for quantize;
  * blk_off (dev, ceil(N/128)+1 int64, from qlinear_block_offsets) is required for
- * QL_GRID_MIXED and ignored otherwise.  packed (dev) has the packed size. */
+ * QL_GRID_MIXED and ignored otherwise.  scales and pscales may both be NULL (codes only). */
 ql_status qlinear_pack(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const int64_t *blk_off,
-                       const int8_t *codes, void *packed, hipStream_t stream);
+                       const int8_t *codes, const uint16_t *scales, void *packed, uint16_t *pscales,
+                       hipStream_t stream);
 
-/* Scales bf16 [N][K/128] (dev) -> packed scale array (dev, qlinear_packed_scales_len elements). */
+/* Scales bf16 [N][K/128] (dev) -> packed scale array (dev, qlinear_packed_scales_len elements);
+ * the scale half of qlinear_pack, for scales recalibrated without repacking the codes. */
 ql_status qlinear_pack_scales(int64_t N, int64_t K, const uint16_t *scales, uint16_t *pscales,
                               hipStream_t stream);
 

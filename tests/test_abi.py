@@ -80,7 +80,10 @@ def test_other_argument_errors():
     L = ql.lib()
     assert L.qlinear_gemm(0, 64, 128, 0, None, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
     assert L.qlinear_quantize(4, 100, 0, None, FAKE, FAKE, FAKE, None) == 1
-    assert L.qlinear_pack(4, 128, 3, None, None, FAKE, FAKE, None) == 1
+    assert L.qlinear_pack(4, 128, 3, None, None, FAKE, None, FAKE, None, None) == 1
+    # scales without a packed scale array (or the reverse) is an argument error
+    assert L.qlinear_pack(4, 128, 0, None, None, FAKE, FAKE, FAKE, None, None) == 1
+    assert L.qlinear_pack(4, 128, 0, None, None, FAKE, None, FAKE, FAKE, None) == 1
     assert L.qlinear_unpack(4, 128, 9, None, None, FAKE, FAKE, None) == 1
     assert L.qlinear_dequant(4, 128, 0, None, None, None, FAKE, 0, FAKE, None) == 1
     assert L.qlinear_gemv_grouped(FAKE, 0, 10, 1, FAKE, None) == 1
@@ -129,7 +132,7 @@ def test_container_sizes_and_argument_errors():
     assert L.qlinear_c4_to_packed(64, 128, 4, None, None, p, p, None) == 1  # 4 is not a ThinkBit grid
     assert L.qlinear_c4_gemv_grouped(p, 1, 1, 4, p, None) == 2
     assert L.qlinear_c4_gemv_grouped(p, 1, 1, 1, None, None) == 1
-    assert L.qlinear_pack(64, 128, ql.GRID_C4, None, None, p, p, None) == 1  # native rejects containers
+    assert L.qlinear_pack(64, 128, ql.GRID_C4, None, None, p, None, p, None, None) == 1  # native rejects containers
 
 
 def test_grouped_prepare_rejects_mixed_container_lists():
