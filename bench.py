@@ -743,6 +743,8 @@ def main():
     ap.add_argument("--no-per-matrix", action="store_true", help="skip the one-launch-per-matrix leg")
     ap.add_argument("--no-arena", action="store_true",
                     help="allocate every packed tensor separately instead of in one arena")
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed back-to-back passes before the warm-up, so clocks and power settle")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -771,6 +773,18 @@ def main():
     grp = ql.GroupedGemv(items)
     codes_b, x_b, y_b = algorithmic_bytes(items, M)
 
+    # Clock and power settle: a fresh GPU first boosts, then throttles and settles
+    # over the first ~25 ms of back-to-back passes (measured: the first 5 passes near
+    # the settled time, the next 20 about 18 % slower, steady after ~75).  The pass
+    # runs untimed for args.settle_ms before the warm-up steps, so the timed steps
+    # measure the sustained rate a serving loop sees.
+    settle = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            grp.run()
+        torch.cuda.synchronize()
+        settle += 10
     for _ in range(args.warmup):
         grp.run()
     torch.cuda.synchronize()
@@ -799,7 +813,7 @@ def main():
                    "grids": "mixed per 128-row block: 75.3% ternary / 6.0% 2-bit / 18.7% 3-bit, q,k 3-bit",
                    "variant": "grouped single launch", "stored_bytes": stored,
                    "us_per_pass": round(ms_step * 1e3, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                   "kernel_us": kst, "arena": not args.no_arena},
+                   "kernel_us": kst, "arena": not args.no_arena, "settle_passes": settle},
     }
     alg = codes_b + x_b + y_b
     ach = alg / (avg_kern_ms * 1e-3) / 1e9

@@ -113,9 +113,9 @@ __device__ __forceinline__ void put32(uint16_t* dst, const uint32_t (&o)[16]) {
 }
 
 // Ternary: codes of period-local inputs [K0, K0+32) of one row (K0 even, compile-time)
-// from the row's chunks (K0/5)/16 and ((K0+31)/5)/16 of the period.
+// from the row's chunks (K0/5)/16 and ((K0+31)/5)/16 of the period, as 16 bf16 pairs.
 template <int K0>
-__device__ __forceinline__ void decode_t32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+__device__ __forceinline__ void decode_t32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint32_t (&o)[16]) {
   constexpr int J0 = K0 / 5, J1 = (K0 + 31) / 5;  // bytes covering the range
   constexpr int C0 = J0 / 16;
   u32x4g_t e[J1 - J0 + 1];
@@ -125,7 +125,6 @@ __device__ __forceinline__ void decode_t32(const u32x4g_t (&ch)[2], const uint8_
     const uint32_t b = (w >> (8 * (j & 3))) & 0xFFu;
     e[decltype(ji)::value] = *(lq4p)(lut + ((j & 1) ? kLutT1 : kLutT0) + b * 16);
   });
-  uint32_t o[16];
   gfor<16>([&](auto pi) __attribute__((always_inline)) {
     constexpr int k = K0 + 2 * decltype(pi)::value;
     constexpr int j = k / 5 - J0, t = k % 5;
@@ -135,14 +134,18 @@ __device__ __forceinline__ void decode_t32(const u32x4g_t (&ch)[2], const uint8_
     else if constexpr (t == 3) o[decltype(pi)::value] = __builtin_amdgcn_alignbit(e[j].z, e[j].y, 16);
     else o[decltype(pi)::value] = __builtin_amdgcn_perm(e[j + 1].x, e[j].z, 0x05040100u);
   });
+}
+template <int K0>
+__device__ __forceinline__ void decode_t32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+  uint32_t o[16];
+  decode_t32<K0>(ch, lut, o);
   put32(dst, o);
 }
 
 // 2-bit: codes [128g + 32q, +32) of one row = group bytes 8q..8q+7, staged as
 // ch[0].x, ch[0].y.
-__device__ __forceinline__ void decode_i2_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+__device__ __forceinline__ void decode_i2_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint32_t (&o)[16]) {
   const uint32_t wd[2] = {ch[0].x, ch[0].y};
-  uint32_t o[16];
   gfor<8>([&](auto bi) __attribute__((always_inline)) {
     constexpr int j = decltype(bi)::value;  // byte of the quarter
     const uint32_t b = (wd[j >> 2] >> (8 * (j & 3))) & 0xFFu;
@@ -150,14 +153,17 @@ __device__ __forceinline__ void decode_i2_32(const u32x4g_t (&ch)[2], const uint
     o[2 * j] = e.x;
     o[2 * j + 1] = e.y;
   });
+}
+__device__ __forceinline__ void decode_i2_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+  uint32_t o[16];
+  decode_i2_32(ch, lut, o);
   put32(dst, o);
 }
 
 // 3-bit: codes [128g + 32q, +32) of one row = the 96-bit triple at group bytes
 // 12q..12q+11, staged as ch[0].x, ch[0].y, ch[0].z (low word first).
-__device__ __forceinline__ void decode_i3_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+__device__ __forceinline__ void decode_i3_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint32_t (&o)[16]) {
   const uint32_t w0 = ch[0].x, w1 = ch[0].y, w2 = ch[0].z;
-  uint32_t o[16];
   gfor<16>([&](auto pi) __attribute__((always_inline)) {
     constexpr int P = decltype(pi)::value;
     constexpr int bit = 6 * P;  // first bit of the 6-bit field
@@ -169,6 +175,10 @@ __device__ __forceinline__ void decode_i3_32(const u32x4g_t (&ch)[2], const uint
     else f = (w2 >> (bit - 64)) & 63u;
     o[P] = *(lq1p)(lut + kLutI3 + f * 4);
   });
+}
+__device__ __forceinline__ void decode_i3_32(const u32x4g_t (&ch)[2], const uint8_t* lut, uint16_t* dst) {
+  uint32_t o[16];
+  decode_i3_32(ch, lut, o);
   put32(dst, o);
 }
 
@@ -372,6 +382,194 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
   }
 }
 
+// ---------------------------------------------------------------- large-tile kernel
+// The contraction of 16 and more tokens.  A workgroup of 8 waves owns 256
+// weight rows (two grid blocks) x 64*TA tokens; each wave computes 64 rows x
+// 32*TA tokens with v_mfma_f32_32x32x16_bf16 (x fragments as the first operand,
+// weight fragments as the second, so the 32 lanes of a D register hold 32
+// consecutive weight rows of one token and y is stored in 128-byte runs).
+// Stages of 64 inputs are double-buffered in LDS with one barrier per stage:
+// while the waves run the MFMAs of stage s from one buffer, the loads of stage
+// s+1 (codes, x, scales) are in flight, and stage s+1 is then decoded into the
+// other buffer.
+//
+// The weight operand is bf16 RNE(c * s), the group scale folded into the code
+// (the dequantize-to-bf16 tile of the pages' BF16 reading: k-quant calibration
+// page, section "Not just any noise").  For ternary and 2-bit codes, and 3-bit
+// codes of magnitude 0, 1, 2 and 4, c * s is exact in bf16; only 3-bit codes of
+// magnitude 3 are rounded.  Products are exact in fp32 and sums are fp32.
+constexpr int kG2Rows = 256;  // weight rows per workgroup
+constexpr int kG2K = 64;      // inputs per stage
+constexpr int kG2Pad = 72;    // bf16 per LDS row: 64 + 8, so 16 lanes' 16-byte reads of 16 rows hit distinct banks
+constexpr int kG2Threads = 512;
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// bf16 pair (c0, c1) times (s, s), each product rounded to nearest even
+__device__ __forceinline__ uint32_t scale_pair(uint32_t codes, uint32_t s2) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(bf16x2_t, codes) * __builtin_bit_cast(bf16x2_t, s2));
+}
+
+template <int TA>
+__global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, int nsplit, float* __restrict__ part) {
+  constexpr int MT = 64 * TA;         // tokens per workgroup
+  constexpr int XQ = 8 / TA;          // threads per token row of a stage (16 * TA bytes each)
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][kG2Rows * kG2Pad];
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][MT * kG2Pad];
+  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
+  gemm_build_luts(lut);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, G8 = (K / kGroup + 7) / 8;
+  const int S = K / kG2K;  // stages of the row
+  const int64_t n0 = (int64_t)blockIdx.x * kG2Rows;
+  const int m0 = blockIdx.y * MT;
+  const int z = blockIdx.z;
+  const int s_lo = (int)((int64_t)S * z / nsplit), s_hi = (int)((int64_t)S * (z + 1) / nsplit);
+  const int64_t nslabs = ((int64_t)a.N + kSlab - 1) / kSlab;
+
+  // decode mapping: row dr of the tile, half dh of the stage (wave-uniform), grid
+  // block tid >> 8 of the tile (wave-uniform)
+  const int dr = (tid & 127) + 128 * (tid >> 8);
+  const int dh = __builtin_amdgcn_readfirstlane((tid >> 7) & 1);
+  const int64_t dn = n0 + dr;
+  const int64_t dslab_i = dn / kSlab;
+  int gr = QL_GRID_T;
+  const uint8_t* dslab = nullptr;
+  if (dslab_i < nslabs) {
+    const int64_t off = slab_offset(dslab_i, K, a.grid, a.blk_grid, a.blk_off, &gr);
+    dslab = a.packed + off;
+  }
+  gr = __builtin_amdgcn_readfirstlane(gr);  // uniform: the wave's rows share one grid block
+  const int dslab_r = (int)(dn & (kSlab - 1));
+  const bool drow_ok = dn < a.N;
+  // x mapping: token xr of the tile, piece xp (16 * TA bytes of the stage's 128)
+  const int xr = tid / XQ, xp = tid % XQ;
+  const bool x_ok = m0 + xr < M;
+  const uint16_t* xrow = a.x + (int64_t)(x_ok ? m0 + xr : 0) * K + 8 * TA * xp;
+
+  struct Regs {
+    u32x4g_t xv[TA];
+    u32x4g_t ch[2];
+    uint32_t sc;
+  } st;
+  auto load = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < TA; ++q) {
+      st.xv[q] = u32x4g_t{0u, 0u, 0u, 0u};
+      if (x_ok) st.xv[q] = *(gq4p)(xrow + (int64_t)s * kG2K + 8 * q);
+    }
+    const int k0 = kG2K * s + 32 * dh;  // first input of this thread's 32
+    if (gr == QL_GRID_T) {
+      const int64_t p = k0 / kPeriodK;
+      const int kp = k0 - (int)p * kPeriodK;
+      st.ch[0] = row_chunk(dslab, dslab_r, 8 * p + (kp / 5) / 16);
+      st.ch[1] = row_chunk(dslab, dslab_r, 8 * p + ((kp + 31) / 5) / 16);
+    } else if (gr == QL_GRID_I2) {
+      const u32x2g_t v = row_dword2(dslab, dslab_r, k0 / 4);
+      st.ch[0] = u32x4g_t{v.x, v.y, 0u, 0u};
+      st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
+    } else {
+      const int64_t b0 = 3 * (int64_t)k0 / 8;
+      st.ch[0] = u32x4g_t{row_dword(dslab, dslab_r, b0), row_dword(dslab, dslab_r, b0 + 4),
+                          row_dword(dslab, dslab_r, b0 + 8), 0u};
+      st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
+    }
+    st.sc = drow_ok ? (uint32_t)a.pscales[pscale_index(dn, k0 / kGroup, G8)] : 0u;
+  };
+  // decode the loaded stage s (codes times scale, bf16) and its x tile into buffer b
+  auto put = [&](int s, int b) __attribute__((always_inline)) {
+    uint32_t o[16];
+    if (gr == QL_GRID_T) {
+      const int pos = (2 * ((kG2K * s) % kPeriodK) / kG2K) + dh;  // 32-input quarter within the period (0..19)
+      switch (pos) {
+#define QL_T_CASE(i) \
+  case i:            \
+    decode_t32<32 * i>(st.ch, lut, o); \
+    break;
+        QL_T_CASE(0) QL_T_CASE(1) QL_T_CASE(2) QL_T_CASE(3) QL_T_CASE(4) QL_T_CASE(5) QL_T_CASE(6)
+        QL_T_CASE(7) QL_T_CASE(8) QL_T_CASE(9) QL_T_CASE(10) QL_T_CASE(11) QL_T_CASE(12) QL_T_CASE(13)
+        QL_T_CASE(14) QL_T_CASE(15) QL_T_CASE(16) QL_T_CASE(17) QL_T_CASE(18)
+        default: decode_t32<32 * 19>(st.ch, lut, o); break;
+#undef QL_T_CASE
+      }
+    } else if (gr == QL_GRID_I2) {
+      decode_i2_32(st.ch, lut, o);
+    } else {
+      decode_i3_32(st.ch, lut, o);
+    }
+    const uint32_t s2 = st.sc | (st.sc << 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = scale_pair(o[i], s2);
+    uint16_t* dst = wt[b] + dr * kG2Pad + 32 * dh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    uint16_t* xd = xt[b] + xr * kG2Pad + 8 * TA * xp;
+#pragma unroll
+    for (int q = 0; q < TA; ++q) *reinterpret_cast<u32x4g_t*>(xd + 8 * q) = st.xv[q];
+  };
+
+  // MFMA mapping: wave (th, rq) computes tokens [32 TA th, +32 TA) x rows [64 rq, +64)
+  const int th = wave & 1, rq = wave >> 1;
+  f32x16_t acc[TA][2];
+#pragma unroll
+  for (int ta = 0; ta < TA; ++ta)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ta][rb][r] = 0.0f;
+  auto mma = [&](int b) __attribute__((always_inline)) {
+    const uint16_t* xb = xt[b] + (32 * TA * th + (lane & 31)) * kG2Pad + 8 * (lane >> 5);
+    const uint16_t* wb = wt[b] + (64 * rq + (lane & 31)) * kG2Pad + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kG2K / 16; ++ks) {
+      bf16x8_t av[TA], bv[2];
+#pragma unroll
+      for (int ta = 0; ta < TA; ++ta) av[ta] = *reinterpret_cast<const bf16x8_t*>(xb + 32 * ta * kG2Pad + 16 * ks);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) bv[rb] = *reinterpret_cast<const bf16x8_t*>(wb + 32 * rb * kG2Pad + 16 * ks);
+#pragma unroll
+      for (int ta = 0; ta < TA; ++ta)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[ta][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ta], bv[rb], acc[ta][rb], 0, 0, 0);
+    }
+  };
+
+  __syncthreads();  // tables ready
+  if (s_lo < s_hi) {
+    load(s_lo);
+    put(s_lo, 0);
+  }
+  __syncthreads();
+  for (int s = s_lo; s < s_hi; ++s) {
+    const int b = (s - s_lo) & 1;
+    const bool more = s + 1 < s_hi;
+    if (more) load(s + 1);
+    mma(b);
+    if (more) put(s + 1, b ^ 1);
+    lds_barrier();
+  }
+
+  // D register r of lane l: token 8 (r / 4) + 4 (l / 32) + r % 4 of the 32-token block,
+  // weight row l % 32 of the 32-row block
+  float* out = nsplit > 1 ? part + (int64_t)z * M * a.N : a.y;
+#pragma unroll
+  for (int ta = 0; ta < TA; ++ta)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int64_t n = n0 + 64 * rq + 32 * rb + (lane & 31);
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = m0 + 32 * TA * th + 32 * ta + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t < M) out[(int64_t)t * a.N + n] = acc[ta][rb][r];
+      }
+    }
+}
+
 // y = sum over splits of the partials, in split order.
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(const float* __restrict__ part, float* __restrict__ y,
                                                           int64_t n, int nsplit) {
@@ -383,19 +581,49 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(const float* __restric
 }
 
 namespace {
-// row slices per workgroup: 8 (32 tokens), 4 (64 tokens) or 2 (128 tokens)
+// row slices per workgroup of the small-batch kernel: 8 (32 tokens), 4 (64 tokens) or 2 (128 tokens)
 int row_slices(int64_t M) { return M <= 32 ? 8 : (M <= 64 ? 4 : 2); }
 int64_t tile_tokens(int64_t M) { return 256 / row_slices(M); }
 
-// K splits that bring the launch to about two workgroups per CU (at least two
-// groups per split); 1 when the matrix alone fills the device.
+// Batches of at least this many tokens run on the large-tile kernel.
+constexpr int64_t kLargeM = 16;
+// 32-token blocks per wave of the large-tile kernel (workgroup tokens 64 * TA)
+int large_ta(int64_t M) { return M <= 64 ? 1 : (M <= 128 ? 2 : 4); }
+
+// K splits.  Large-tile kernel (one workgroup per CU): the split count minimising a
+// cost model of whole workgroup rounds times the stages each workgroup runs, plus the
+// partial sums a split writes and the reduction reads back (8 bytes per output and
+// split, at about 5 TB/s, against about 3 us per stage and round).  Small-batch
+// kernel: enough splits for about two workgroups per CU.  At least two groups (or
+// two stages) per split, at most 16 splits.
 int choose_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t mt = tile_tokens(M);
-  const int64_t tiles = ((N + kTileN - 1) / kTileN) * ((M + mt - 1) / mt);
-  const int64_t want = 2 * (int64_t)device_cu_count();
+  int64_t tiles, units, per_cu;
+  if (M >= kLargeM) {
+    const int64_t mt = 64 * large_ta(M);
+    tiles = ((N + kG2Rows - 1) / kG2Rows) * ((M + mt - 1) / mt);
+    units = K / kG2K;
+    const int64_t slots = device_cu_count();
+    int best = 1;
+    double best_us = 0.0;
+    for (int64_t s = 1; s <= 16 && s <= (units < 2 ? 1 : units / 2); ++s) {
+      const int64_t rounds = (tiles * s + slots - 1) / slots;
+      const double us = (double)rounds * (double)((units + s - 1) / s) * 3.0 +
+                        (s > 1 ? (double)s * (double)M * (double)N * 8.0 / 5.0e6 : 0.0);
+      if (s == 1 || us < best_us) {
+        best = (int)s;
+        best_us = us;
+      }
+    }
+    return best;
+  } else {
+    const int64_t mt = tile_tokens(M);
+    tiles = ((N + kTileN - 1) / kTileN) * ((M + mt - 1) / mt);
+    units = K / kGroup;
+  }
+  per_cu = 2;
+  const int64_t want = per_cu * (int64_t)device_cu_count();
   int64_t s = (want + tiles - 1) / tiles;
-  const int64_t G = K / kGroup;
-  if (s > G / 2) s = G / 2;
+  if (s > units / 2) s = units / 2;
   if (s > 16) s = 16;
   return s < 1 ? 1 : (int)s;
 }
@@ -407,18 +635,36 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return launch_gemm_as(a, M, workspace, ws_bytes, M >= kLargeM, stream);
+}
+
+// large: the large-tile kernel (bf16 c*s operands); otherwise the small-batch kernel
+// (bf16 codes, fp32 scale per group: every product exact).
+hipError_t launch_gemm_as(const MatArgs& a, int M, void* workspace, size_t ws_bytes, bool large, hipStream_t stream) {
   int s = choose_splits(M, a.N, a.K);
   if (s > 1 && (!workspace || ws_bytes < (size_t)s * M * a.N * sizeof(float))) s = 1;
-  const int wr = row_slices(M);
-  const int64_t mt = tile_tokens(M);
-  const dim3 grid((unsigned)((a.N + kTileN - 1) / kTileN), (unsigned)((M + mt - 1) / mt), (unsigned)s);
   float* part = static_cast<float*>(workspace);
-  if (wr == 8)
-    hipLaunchKernelGGL(gemm_kernel<8>, grid, dim3(kThreads), 0, stream, a, M, s, part);
-  else if (wr == 4)
-    hipLaunchKernelGGL(gemm_kernel<4>, grid, dim3(kThreads), 0, stream, a, M, s, part);
-  else
-    hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(kThreads), 0, stream, a, M, s, part);
+  if (large) {
+    const int ta = large_ta(M);
+    const int64_t mt = 64 * ta;
+    const dim3 grid((unsigned)((a.N + kG2Rows - 1) / kG2Rows), (unsigned)((M + mt - 1) / mt), (unsigned)s);
+    if (ta == 1)
+      hipLaunchKernelGGL(gemm2_kernel<1>, grid, dim3(kG2Threads), 0, stream, a, M, s, part);
+    else if (ta == 2)
+      hipLaunchKernelGGL(gemm2_kernel<2>, grid, dim3(kG2Threads), 0, stream, a, M, s, part);
+    else
+      hipLaunchKernelGGL(gemm2_kernel<4>, grid, dim3(kG2Threads), 0, stream, a, M, s, part);
+  } else {
+    const int wr = row_slices(M);
+    const int64_t mt = tile_tokens(M);
+    const dim3 grid((unsigned)((a.N + kTileN - 1) / kTileN), (unsigned)((M + mt - 1) / mt), (unsigned)s);
+    if (wr == 8)
+      hipLaunchKernelGGL(gemm_kernel<8>, grid, dim3(kThreads), 0, stream, a, M, s, part);
+    else if (wr == 4)
+      hipLaunchKernelGGL(gemm_kernel<4>, grid, dim3(kThreads), 0, stream, a, M, s, part);
+    else
+      hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(kThreads), 0, stream, a, M, s, part);
+  }
   if (s > 1) {
     const int64_t n = (int64_t)M * a.N;
     const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);

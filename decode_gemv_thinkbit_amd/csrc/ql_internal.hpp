@@ -44,6 +44,8 @@ hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int6
                                   hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream);
+// large: the large-tile kernel (bf16 c*s operands), else the small-batch exact kernel
+hipError_t launch_gemm_as(const MatArgs& a, int M, void* workspace, size_t ws_bytes, bool large, hipStream_t stream);
 
 hipError_t launch_rtn_noise(int64_t N, int64_t K, const float* W, double* noise, hipStream_t stream);
 hipError_t launch_block_sensitivity(int64_t N, int64_t K, const uint16_t* x, const float* grad, double* S,

@@ -136,17 +136,33 @@ def test_gemv_one_hot_decodes_every_position(ora, dev, grid):
             assert np.array_equal(y[j], w32[:, k]), k
 
 
+LARGE_M = 16  # qlinear_gemm runs the large-tile kernel (bf16 RNE(c*s) operands) from here on
+
+
+def check_gemm(ora, y, y64, c_ref, s_ref, x, M):
+    """The MFMA path's bar against the fp64 product; the tripwire against the product its operands
+    define: below LARGE_M every product is exact (normwise 1e-4 of the fp64 product), from LARGE_M
+    on the weights are bf16 RNE(c*s), and the result must match the oracle's bf16-weight product to
+    fp32 summation error (normwise 1e-5)."""
+    err, normwise = ora.rel_err(y, y64)
+    assert err <= GEMM_TOL, (err, normwise)
+    if M < LARGE_M:
+        assert normwise <= TRIP_GEMM, normwise
+    else:
+        y16 = ora.gemv_w16(c_ref, s_ref, synth.bf16_bits(x.cpu()))
+        _, nw16 = ora.rel_err(y, y16)
+        assert nw16 <= TRIP_GEMV, nw16
+
+
 @pytest.mark.parametrize("N,K", [(64, 128), (129, 1280), (1000, 4096), (70, 384), (256, 5120)])
 @pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
 @pytest.mark.parametrize("M", [1, 16, 17, 64, 100])
 def test_gemm_parity(ora, dev, N, K, grid, M):
     note(f"gemm N={N} K={K} grid={grid} M={M}")
-    pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=N * 7 + K + M)
+    pw, x, y64, c_ref, s_ref = _gemv_case(ora, dev, N, K, grid, M, seed=N * 7 + K + M)
     y = ql.gemm(x, pw)
     torch.cuda.synchronize()
-    err, normwise = ora.rel_err(y.cpu().numpy(), y64)
-    assert err <= GEMM_TOL, (err, normwise)
-    assert normwise <= TRIP_GEMM, normwise
+    check_gemm(ora, y.cpu().numpy(), y64, c_ref, s_ref, x, M)
 
 
 BIG_GEMM_CASES = [(64, 128, 128), (129, 1280, 200), (1000, 4096, 128), (70, 384, 384), (256, 5120, 256),
@@ -157,15 +173,37 @@ BIG_GEMM_CASES = [(64, 128, 128), (129, 1280, 200), (1000, 4096, 128), (70, 384,
 @pytest.mark.parametrize("N,K,M", BIG_GEMM_CASES)
 @pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
 def test_gemm_large_batch_parity(ora, dev, N, K, M, grid):
-    """Batches of 128 tokens and more: ragged token tiles (M = 130, 200, 257, 300), rows past N,
-    mixed grid blocks, long rows and K splits; every product exact, fp32 sums."""
+    """Batches of 128 tokens and more (the large-tile kernel): ragged token tiles (M = 130, 200,
+    257, 300), rows past N, mixed grid blocks, long rows and K splits."""
     note(f"gemm large batch N={N} K={K} grid={grid} M={M}")
-    pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=N * 5 + K + M)
+    pw, x, y64, c_ref, s_ref = _gemv_case(ora, dev, N, K, grid, M, seed=N * 5 + K + M)
     y = ql.gemm(x, pw)
     torch.cuda.synchronize()
-    err, normwise = ora.rel_err(y.cpu().numpy(), y64)
-    assert err <= GEMM_TOL, (err, normwise)
-    assert normwise <= TRIP_GEMM, normwise
+    check_gemm(ora, y.cpu().numpy(), y64, c_ref, s_ref, x, M)
+
+
+@pytest.mark.parametrize("N,K", [(300, 1280), (256, 4096), (130, 384)])
+@pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
+@pytest.mark.parametrize("M", [16, 100, 256])
+def test_gemm_large_tile_one_hot(ora, dev, N, K, grid, M):
+    """x rows = e_k: the large-tile kernel returns bf16 RNE(c*s) of every weight exactly (one
+    exact product per output), at every position residue of the decoders and across tiles."""
+    note(f"gemm one-hot N={N} K={K} grid={grid} M={M}")
+    g = grid_arg(N, grid, seed=N + K)
+    W = synth.weight(N, K, seed=31 * N + K)
+    c_ref, s_ref = ora.quantize(W.numpy(), g)
+    _, w16 = ora.dequant(c_ref, s_ref)
+    w16f = (w16.astype(np.uint32) << 16).view(np.float32)
+    pw = ql.quantize_pack(W.to(dev), g)
+    ks = sorted(set(list(range(0, min(K, 160))) + list(range(max(0, K - 100), K))))
+    for i0 in range(0, len(ks), M):
+        sel = ks[i0:i0 + M]
+        X = torch.zeros((M, K), dtype=torch.bfloat16)
+        X[torch.arange(len(sel)), torch.tensor(sel)] = 1.0
+        y = ql.gemm(X.to(dev), pw).cpu().numpy()
+        for j, k in enumerate(sel):
+            assert np.array_equal(y[j], w16f[:, k]), (k, np.flatnonzero(y[j] != w16f[:, k])[:5])
+        assert not y[len(sel):].any()
 
 
 def test_grouped_gemv_parity(ora, dev):
