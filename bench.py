@@ -510,7 +510,7 @@ def littlebit_leg(dev, reps=100, shapes=((28672, 8192), (11008, 4096), (8192, 81
             lws = [lw0] + [ql.LittleBitWeight(lw0.u_bits.clone(), lw0.v_bits.clone(), lw0.g.clone(), lw0.l.clone(),
                                               lw0.h.clone(), do, di, r) for _ in range(copies - 1)]
             y = torch.empty(do, dtype=torch.float32, device=dev)
-            ws = torch.empty(int(ql.lib().qlinear_lb_workspace_bytes(do, di, r)), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(int(ql.lib().qlinear_lb_workspace_bytes(do, di, r)), dtype=torch.uint8, device=dev)
             us = timed(lambda i: ql.lb_gemv(x, lws[i], out=y, workspace=ws), copies)
             out.append({"d_out": do, "d_in": di, "bpw": b, "rank": r, "us": round(us, 2),
                         "stored_bytes": lw0.nbytes, "gbs": round(lw0.nbytes / (us * 1e-6) / 1e9, 1),

@@ -9,15 +9,15 @@
 // The page's own kernel packs the signs 32 to a word and flips the sign bit of
 // 16-bit inputs instead of multiplying (section "Memory, KV cache, speed").
 //
-// Here, three launches:
+// Here, two launches:
 //   lb_latent_kernel  one wave per (64 latent rows, slice of inputs): for each
 //                     input pair a table turns a sign byte into four sign masks
 //                     that flip the bf16 scales g, and v_dot2_f32_bf16 takes
 //                     (+-g_i, +-g_i+1) . (x_i, x_i+1): exact products, fp32
-//                     partial sums per slice;
-//   lb_reduce_kernel  z = l . (sum of the slices, in slice order), split into
-//                     three bf16 terms hi + mid + lo that reproduce z to fp32
-//                     accuracy;
+//                     partial sums per slice.  The wave that completes a slab's
+//                     last slice (a counter per slab) forms its z = l . (sum of
+//                     the slices, in slice order), split into three bf16 terms
+//                     hi + mid + lo that reproduce z to fp32 accuracy;
 //   lb_output_kernel  one workgroup per 64 output rows, its waves splitting the
 //                     latent dimension: a table turns a sign byte into four
 //                     (+-1, +-1) bf16 pairs, dotted with the three z terms
@@ -64,11 +64,53 @@ __device__ __forceinline__ uint32_t lut_addr(const uint4& d, int B, uint32_t lan
 }
 
 // partial[q][row] = sum over inputs of slice q of s(row, i) * g_i * x_i
-__global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, int32_t RP, int32_t slice_chunks,
-                                                                  int32_t nslices, const uint8_t* __restrict__ v_bits,
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return f32_to_bf16_bits(f); }
+
+// z of the 64 latent rows of slab `slab` (lane = row), as three bf16 terms per
+// element: zs[(path*ZP + P)*3 + t] holds term t of elements 2P (low half) and
+// 2P+1 (high half).  Rows at or past r have z = 0; the path's last slab also
+// zeroes the pairs between its padded row count and ZP.
+__device__ __forceinline__ void lb_z_terms(int slab, int lane, int r, int RP, int ZP, int nslices,
+                                           const float* __restrict__ partial, const uint16_t* __restrict__ l,
+                                           uint32_t* __restrict__ zs) {
+  const int spp = RP / kSlab;  // slabs per path
+  const int path = slab / spp, j = (slab % spp) * kSlab + lane;
+  float z = 0.0f;
+  if (j < r) {
+    float sum = 0.0f;
+#pragma unroll 16  // loads issued ahead of the in-order adds
+    for (int q = 0; q < nslices; ++q)
+      sum += __hip_atomic_load(partial + (int64_t)q * 2 * RP + path * RP + j, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    z = sum * bf16_bits_to_f32(l[path * r + j]);
+  }
+  const uint32_t hi = bf16_rne_bits(z);
+  const float r1 = z - bf16_bits_to_f32(hi);
+  const uint32_t mid = bf16_rne_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(mid);
+  const uint32_t lo = bf16_rne_bits(r2);
+  // the odd lane's halves join the even lane's
+  const uint32_t ohi = __shfl_down(hi, 1, 64), omid = __shfl_down(mid, 1, 64), olo = __shfl_down(lo, 1, 64);
+  if ((lane & 1) == 0) {
+    uint32_t* d = zs + ((int64_t)path * ZP + (j >> 1)) * 3;
+    d[0] = hi | (ohi << 16);
+    d[1] = mid | (omid << 16);
+    d[2] = lo | (olo << 16);
+  }
+  if (slab % spp == spp - 1)
+    for (int P = RP / 2 + lane; P < ZP; P += 64)
+      for (int t = 0; t < 3; ++t) zs[((int64_t)path * ZP + P) * 3 + t] = 0u;
+}
+
+__global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, int32_t r, int32_t RP, int32_t ZP,
+                                                                  int32_t slice_chunks, int32_t nslices,
+                                                                  const uint8_t* __restrict__ v_bits,
                                                                   const uint16_t* __restrict__ g,
+                                                                  const uint16_t* __restrict__ l,
                                                                   const uint16_t* __restrict__ x,
-                                                                  float* __restrict__ partial) {
+                                                                  float* __restrict__ partial,
+                                                                  uint32_t* __restrict__ counters,
+                                                                  uint32_t* __restrict__ zs) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLbLutBytes];
   build_sign_masks(lut);
   __syncthreads();
@@ -97,42 +139,22 @@ __global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, 
         }
       }
     }
-    partial[(int64_t)q * 2 * RP + slab * kSlab + lane] = acc;
-  }
-}
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return f32_to_bf16_bits(f); }
-
-// z of latent pairs, as three bf16 terms per element: zs[(path*ZP + P)*3 + t]
-// holds term t of elements 2P (low half) and 2P+1 (high half).
-__global__ void __launch_bounds__(256) lb_reduce_kernel(int32_t r, int32_t RP, int32_t ZP, int32_t nslices,
-                                                        const float* __restrict__ partial,
-                                                        const uint16_t* __restrict__ l, uint32_t* __restrict__ zs) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= 2 * ZP) return;
-  const int path = t / ZP, P = t % ZP;
-  uint32_t term[3] = {0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int j = 2 * P + e;
-    float z = 0.0f;
-    if (j < r) {
-      float s = 0.0f;
-#pragma unroll 16  // loads issued ahead of the in-order adds
-      for (int q = 0; q < nslices; ++q) s += partial[(int64_t)q * 2 * RP + path * RP + j];
-      z = s * bf16_bits_to_f32(l[path * r + j]);
+    // partial sums travel at device scope (the XCDs' L2 caches are not coherent with
+    // each other); the counter increment waits for this wave's stores, and the wave
+    // that completes the slab reads them only after its increment has returned
+    __hip_atomic_store(partial + (int64_t)q * 2 * RP + slab * kSlab + lane, acc, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (nslices > 1) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      uint32_t old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(counters + slab * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if (old != (uint32_t)nslices - 1u) continue;
+      asm volatile("" ::: "memory");
+      if (lane == 0) __hip_atomic_store(counters + slab * 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const uint32_t hi = bf16_rne_bits(z);
-    const float r1 = z - bf16_bits_to_f32(hi);
-    const uint32_t mid = bf16_rne_bits(r1);
-    const float r2 = r1 - bf16_bits_to_f32(mid);
-    const uint32_t lo = bf16_rne_bits(r2);
-    term[0] |= hi << (16 * e);
-    term[1] |= mid << (16 * e);
-    term[2] |= lo << (16 * e);
+    lb_z_terms(slab, lane, r, RP, ZP, nslices, partial, l, zs);
   }
-#pragma unroll
-  for (int k = 0; k < 3; ++k) zs[(int64_t)t * 3 + k] = term[k];
 }
 
 // y[n] = h0[n] * sum_j s0(n, j) z0_j + h1[n] * sum_j s1(n, j) z1_j.  A
@@ -247,10 +269,17 @@ static int lb_slice_chunks(int64_t d_in, int64_t r) {
   return (int)(s < 1 ? 1 : (s > 16 ? 16 : s));
 }
 
+// workspace: per-slab counters (one 128-byte line each), then the slices' partial
+// sums, then the z terms
+static size_t lb_counter_bytes(int64_t r) { return (size_t)(2 * lb_latent_rows(r) / 64) * 128; }
+static size_t lb_partial_bytes(int64_t d_in, int64_t r) {
+  const int64_t sc = lb_slice_chunks(d_in, r), nslices = (d_in / 128 + sc - 1) / sc;
+  return ((size_t)nslices * 2 * lb_latent_rows(r) * 4 + 255) / 256 * 256;
+}
+
 size_t lb_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r) {
   (void)d_out;
-  const int64_t sc = lb_slice_chunks(d_in, r), nslices = (d_in / 128 + sc - 1) / sc;
-  return (size_t)(nslices * 2 * lb_latent_rows(r) * 4 + 2 * lb_z_pairs(r) * 3 * 4 + 256);
+  return lb_counter_bytes(r) + lb_partial_bytes(d_in, r) + (size_t)(2 * lb_z_pairs(r) * 3 * 4);
 }
 
 hipError_t launch_lb_pack(int64_t d_out, int64_t d_in, int64_t r, const int8_t* u_signs, const int8_t* v_signs,
@@ -269,15 +298,15 @@ hipError_t launch_lb_gemv(const ql_littlebit& w, const uint16_t* x, float* y, vo
   const int64_t r = w.rank, RP = lb_latent_rows(r), ZP = lb_z_pairs(r);
   const int sc = lb_slice_chunks(w.d_in, r);
   const int nslices = (int)((w.d_in / 128 + sc - 1) / sc);
-  float* partial = static_cast<float*>(ws);
-  uint32_t* zs = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) +
-                                             ((size_t)nslices * 2 * RP * 4 + 255) / 256 * 256);
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* partial = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + lb_counter_bytes(r));
+  uint32_t* zs = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + lb_counter_bytes(r) +
+                                             lb_partial_bytes(w.d_in, r));
   const int64_t tasks = 2 * RP / 64 * nslices, slots = 2 * (int64_t)device_cu_count();
   const int64_t wg_lat = (tasks + kLbWaves - 1) / kLbWaves;
   hipLaunchKernelGGL(lb_latent_kernel, dim3((unsigned)(wg_lat < slots ? wg_lat : slots)), dim3(kLbWaves * 64), 0,
-                     stream, w.d_in, (int)RP, sc, nslices, static_cast<const uint8_t*>(w.v_bits), w.g, x, partial);
-  hipLaunchKernelGGL(lb_reduce_kernel, dim3((unsigned)((2 * ZP + 255) / 256)), dim3(256), 0, stream, (int)r, (int)RP,
-                     (int)ZP, nslices, partial, w.l, zs);
+                     stream, w.d_in, (int)r, (int)RP, (int)ZP, sc, nslices, static_cast<const uint8_t*>(w.v_bits),
+                     w.g, w.l, x, partial, counters, zs);
   const int64_t slabs = (w.d_out + 63) / 64;
   hipLaunchKernelGGL(lb_output_kernel, dim3((unsigned)(slabs < slots ? slabs : slots)), dim3(kLbWaves * 64), 0,
                      stream, w.d_out, (int)lb_u_row_bytes(r), (int)ZP, static_cast<const uint8_t*>(w.u_bits), zs, w.h,

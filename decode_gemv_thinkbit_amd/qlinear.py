@@ -373,7 +373,8 @@ def lb_pack(u_signs: torch.Tensor, v_signs: torch.Tensor, g: torch.Tensor, l: to
 
 def lb_gemv(x: torch.Tensor, lw: LittleBitWeight, out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y [d_out] fp32 of the LittleBit linear at batch 1 (x [d_in] or [1, d_in] bf16)."""
+    """y [d_out] fp32 of the LittleBit linear at batch 1 (x [d_in] or [1, d_in] bf16).
+    workspace: reusable uint8 device buffer, zeroed once at allocation."""
     _dev(x, torch.bfloat16, "x")
     if x.numel() != lw.d_in:
         raise ValueError(f"x has {x.numel()} elements, the linear takes {lw.d_in}")
@@ -385,7 +386,8 @@ def lb_gemv(x: torch.Tensor, lw: LittleBitWeight, out: Optional[torch.Tensor] = 
             raise ValueError("out must hold d_out values")
     need = int(lib().qlinear_lb_workspace_bytes(lw.d_out, lw.d_in, lw.rank))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        # zeroed once: its slab counters must start at zero (every call leaves them zero)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     d = lw.desc()
     _check(lib().qlinear_lb_gemv(ctypes.byref(d), _ptr(x), _ptr(out), _ptr(workspace), need, _stream()), "lb_gemv")
     return out

@@ -334,7 +334,10 @@ ql_status qlinear_lb_pack(int64_t d_out, int64_t d_in, int64_t rank, const int8_
 
 /* Batch-1 product y [d_out] fp32 = the two-path LittleBit linear applied to x [d_in] bf16.
  * Products are exact (sign flips of bf16 values), sums fp32 in a fixed order: deterministic.
- * w (host struct holding device pointers); workspace (dev) of qlinear_lb_workspace_bytes. */
+ * w (host struct holding device pointers); workspace (dev, 16-byte aligned) of
+ * qlinear_lb_workspace_bytes: it holds per-slab counters that must be zero when the first
+ * call starts; every completed call leaves them zero again (zero the workspace once at
+ * allocation).  Calls that share a workspace must not overlap (enqueue them on one stream). */
 size_t qlinear_lb_workspace_bytes(int64_t d_out, int64_t d_in, int64_t rank);
 ql_status qlinear_lb_gemv(const ql_littlebit *w, const uint16_t *x, float *y, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);

@@ -77,3 +77,20 @@ def test_littlebit_deterministic(ora, dev):
     lw, x, y = run_case(ora, dev, 1000, 4096, 150, seed=3)
     for _ in range(3):
         assert torch.equal(ql.lb_gemv(x, lw), y)
+
+
+@pytest.mark.parametrize("do,di,bpw", [(28672, 8192, 0.1), (1000, 4096, 0.55), (130, 256, 1.0)])
+def test_littlebit_reused_workspace(ora, dev, do, di, bpw):
+    """One workspace for many calls: the latent kernel's slab counters are zero again after every
+    call, and the results match a fresh workspace bitwise, also for a new activation."""
+    r = ql.lb_rank(do, di, bpw)
+    lw = ql.lb_pack(*synth.littlebit_params(do, di, r, 19, device=dev))
+    ws = torch.zeros(int(ql.lib().qlinear_lb_workspace_bytes(do, di, r)), dtype=torch.uint8, device=dev)
+    for seed in (21, 22):
+        x = synth.activations(1, di, seed, device=dev).view(-1)
+        y0 = ql.lb_gemv(x, lw)
+        for _ in range(3):
+            y = ql.lb_gemv(x, lw, workspace=ws)
+            assert torch.equal(y, y0)
+        nslab = 2 * ((r + 63) // 64)
+        assert int(ws[: nslab * 128].abs().sum().item()) == 0
