@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libqlinear.so")
-SOURCES = ["ql_api.hip", "ql_pack.hip", "ql_gemv.hip", "ql_gemv_mm.hip", "ql_gemm.hip", "ql_c4.hip", "ql_alloc.hip", "ql_littlebit.hip", "ql_probe.hip", "ql_noalloc.hip"]
+SOURCES = ["ql_api.hip", "ql_pack.hip", "ql_gemv.hip", "ql_gemv_mm.hip", "ql_gemm.hip", "ql_c4.hip", "ql_alloc.hip", "ql_littlebit.hip", "ql_probe.hip", "ql_noalloc.hip", "ql_check.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -166,6 +166,24 @@ ql_status qlinear_dequant(int64_t N, int64_t K, int grid, const int8_t* blk_grid
                     "dequant launch");
 }
 
+ql_status qlinear_validate_codes(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int8_t* codes,
+                                 uint32_t* counts, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, nullptr, false));
+  QL_TRY(check_ptrs({codes, counts}));
+  return hip_status(ql::launch_validate_codes(N, K, grid, blk_grid, codes, counts, stream), "validate_codes launch");
+}
+
+ql_status qlinear_validate_packed(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                                  const void* packed, uint32_t* counts, hipStream_t stream) {
+  QL_TRY(check_shape(N, K));
+  QL_TRY(check_grid(grid, blk_grid, blk_off, true));
+  QL_TRY(check_ptrs({packed, counts}));
+  return hip_status(ql::launch_validate_packed(N, K, grid, blk_grid, blk_off, static_cast<const uint8_t*>(packed),
+                                               counts, stream),
+                    "validate_packed launch");
+}
+
 static ql_status mat_args(int64_t M, int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
                           const void* packed, const uint16_t* pscales, const uint16_t* x, float* y, ql::MatArgs* a) {
   QL_TRY(check_shape(N, K));

@@ -47,6 +47,10 @@ hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes
 // large: the large-tile kernel (bf16 c*s operands), else the small-batch exact kernel
 hipError_t launch_gemm_as(const MatArgs& a, int M, void* workspace, size_t ws_bytes, bool large, hipStream_t stream);
 
+hipError_t launch_validate_codes(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int8_t* codes,
+                                 uint32_t* counts, hipStream_t stream);
+hipError_t launch_validate_packed(int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
+                                  const uint8_t* packed, uint32_t* counts, hipStream_t stream);
 hipError_t launch_rtn_noise(int64_t N, int64_t K, const float* W, double* noise, hipStream_t stream);
 hipError_t launch_block_sensitivity(int64_t N, int64_t K, const uint16_t* x, const float* grad, double* S,
                                     hipStream_t stream);

@@ -91,6 +91,8 @@ def lib():
         L.qlinear_rtn_noise.argtypes = [i64, i64, vp, vp, vp]
         L.qlinear_allocate.argtypes = [vp, i64, ctypes.c_double, vp, vp, vp]
         L.qlinear_block_sensitivity.argtypes = [i64, i64, vp, vp, vp, vp]
+        L.qlinear_validate_codes.argtypes = [i64, i64, i32, vp, vp, vp, vp]
+        L.qlinear_validate_packed.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
         L.qlinear_lb_bpw.argtypes = [i64, i64, i64]
         L.qlinear_lb_bpw.restype = ctypes.c_double
         L.qlinear_lb_rank.argtypes = [i64, i64, ctypes.c_double]
@@ -114,7 +116,7 @@ def lib():
                      "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
                      "qlinear_gemv_grouped", "qlinear_gemv_grouped_noalloc", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
                      "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped", "qlinear_rtn_noise",
-                     "qlinear_allocate", "qlinear_block_sensitivity", "qlinear_lb_pack", "qlinear_lb_gemv"):
+                     "qlinear_allocate", "qlinear_block_sensitivity", "qlinear_validate_codes", "qlinear_validate_packed", "qlinear_lb_pack", "qlinear_lb_gemv"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -248,6 +250,30 @@ def quantize_pack(W: torch.Tensor, grid, packed: Optional[torch.Tensor] = None,
                   pscales: Optional[torch.Tensor] = None) -> PackedWeight:
     codes, scales = quantize(W, grid)
     return pack(codes, scales, grid, packed, pscales)
+
+
+def validate_codes(codes: torch.Tensor, grid) -> np.ndarray:
+    """Counts [codes outside their grid, -, bad block grids, -] of int8 codes [N, K] (device).
+    grid: a grid id, or a per-block table (uploaded as is, unchecked on the host)."""
+    _dev(codes, torch.int8, "codes")
+    N, K = codes.shape
+    bg = None
+    if isinstance(grid, (int, np.integer)):
+        g = int(grid)
+    else:
+        g = GRID_MIXED
+        bg = torch.from_numpy(np.ascontiguousarray(grid, dtype=np.int8)).to(codes.device)
+    out = torch.zeros(4, dtype=torch.int32, device=codes.device)
+    _check(lib().qlinear_validate_codes(N, K, g, _ptr(bg), _ptr(codes), _ptr(out), _stream()), "validate_codes")
+    return out.cpu().numpy()
+
+
+def validate_packed(pw: PackedWeight) -> np.ndarray:
+    """Counts [ternary bytes above 242, padding not coding 0, bad block grids, -] of a packed weight."""
+    out = torch.zeros(4, dtype=torch.int32, device=pw.packed.device)
+    _check(lib().qlinear_validate_packed(pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
+                                         _ptr(out), _stream()), "validate_packed")
+    return out.cpu().numpy()
 
 
 def unpack(pw: PackedWeight) -> torch.Tensor:

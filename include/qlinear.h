@@ -136,6 +136,21 @@ ql_status qlinear_dequant(int64_t N, int64_t K, int grid, const int8_t *blk_grid
                           const void *packed, const uint16_t *pscales, int out_bf16, void *out,
                           hipStream_t stream);
 
+/* ---------------------------------------------------------------- data validation (device)
+ *
+ * The products leave codes outside the grid, ternary bytes above 242 and bad padding outside
+ * their contract (undefined results, never an out-of-bounds access).  These checks find such
+ * data (summary page, section "How it works": the three grids' value sets; a base-3 byte of
+ * five trits is at most 242) and ADD their counts to counts (dev, 4 uint32, 16-byte aligned,
+ * zeroed by the caller): counts[0] codes outside their row's grid (ternary bytes above 242 in
+ * packed data), counts[1] padding that does not code c = 0 (rows past N, trits past K),
+ * counts[2] 128-row blocks whose blk_grid entry is not a grid (such blocks are skipped),
+ * counts[3] unused (0).  Read counts back after the stream reaches the call. */
+ql_status qlinear_validate_codes(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const int8_t *codes,
+                                 uint32_t *counts, hipStream_t stream);
+ql_status qlinear_validate_packed(int64_t N, int64_t K, int grid, const int8_t *blk_grid, const int64_t *blk_off,
+                                  const void *packed, uint32_t *counts, hipStream_t stream);
+
 /* ---------------------------------------------------------------- products (device) */
 
 /* Decode-time GEMV, 1 <= M <= 8 (the per-token weight stream that the summary page,
