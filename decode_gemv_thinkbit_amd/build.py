@@ -9,7 +9,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-OUT_DIR = os.path.join(HERE, "_build")
+# QLINEAR_SANITIZE=1: host code built with AddressSanitizer and UndefinedBehaviorSanitizer into
+# _build_san/ (device code unchanged); load it in a process that preloads clang's ASan runtime
+SANITIZE = os.environ.get("QLINEAR_SANITIZE") == "1"
+OUT_DIR = os.path.join(HERE, "_build_san" if SANITIZE else "_build")
 LIB = os.path.join(OUT_DIR, "libqlinear.so")
 SOURCES = ["ql_api.hip", "ql_pack.hip", "ql_gemv.hip", "ql_gemv_mm.hip", "ql_gemm.hip", "ql_c4.hip", "ql_alloc.hip", "ql_littlebit.hip", "ql_probe.hip", "ql_noalloc.hip", "ql_check.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -24,6 +27,9 @@ FLAGS = [
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+if SANITIZE:
+    FLAGS += ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libsan", "-g"]
 
 
 def _compile(src: str) -> str:
@@ -41,6 +47,8 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    if SANITIZE:
+        cmd[1:1] = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-shared-libsan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -23,7 +23,11 @@ QL_MAX_KPARTS = 16  # split-K parts per slab at most
 QL_NOALLOC_STATE_WORDS = 4194304  # uint32 words of the library's static grouped-launch state
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_build", "libqlinear.so")
+# QLINEAR_SANITIZE=1 loads the build whose host code carries AddressSanitizer and
+# UndefinedBehaviorSanitizer (decode_gemv_thinkbit_amd/build.py); the process must preload
+# clang's ASan runtime
+LIB_PATH = os.path.join(_HERE, "_build_san" if os.environ.get("QLINEAR_SANITIZE") == "1" else "_build",
+                        "libqlinear.so")
 
 _lib = None
 

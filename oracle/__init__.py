@@ -22,7 +22,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "thinkbit_oracle.cpp")
-_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+# ORACLE_SANITIZE=1 selects a build with AddressSanitizer and UndefinedBehaviorSanitizer (host
+# code only; load it in a process that preloads the sanitizer runtime)
+_SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle_san.so" if _SANITIZE else "liboracle.so")
 
 GRID_T, GRID_I2, GRID_I3 = 0, 1, 2
 GROUP = 128
@@ -35,7 +38,9 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC,
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+               "-g"] if _SANITIZE else []
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", *san, "-o", tmp, _SRC,
                                "-lpthread"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
