@@ -4,7 +4,15 @@ the target rules (CPU only: hipcc cross-compiles without a GPU).
 - No write goes through the scalar data cache: no scalar memory stores or atomics and no
   write-back or discard of that cache (all stores are vector stores).
 - No packed-fp32 VALU operation is emitted (the build turns the feature off).
-- The batch-1 GEMV kernels use no scratch (their VGPRs do not spill).
+- The batch-1 GEMV kernels use no scratch (their VGPRs do not spill); every other kernel's
+  private segment stays within a stated bound (zero for all but the batched-decode kernel,
+  whose few spills sit outside its inner loop).
+- The split-K protocol (a part's partial sums stored at agent scope, a wait for those
+  stores, then an agent-scope counter increment; the last part loads the partials at agent
+  scope) is emitted with those properties: agent-scope stores and loads carry sc1 (they go
+  to and come from L2, which every CU of the device shares), the counter atomics return
+  their old value (sc0), and no counter atomic follows an agent-scope store without an
+  intervening vmcnt(0) wait.
 """
 import concurrent.futures as cf
 import os
@@ -49,3 +57,65 @@ def test_batch1_gemv_kernels_do_not_spill(asm):
         body = text[text.index(k + ":"):]
         body = body[: body.index(".Lfunc_end")]
         assert "scratch_" not in body, k
+
+
+def kernel_bodies(text):
+    """name -> assembly of each kernel in one compiled source."""
+    out = {}
+    for k in re.findall(r"^(_ZN2ql\w*kernel\w*):", text, re.M):
+        body = text[text.index(k + ":"):]
+        out[k] = body[: body.index(".Lfunc_end")]
+    return out
+
+
+def kernel_metadata(text):
+    """name -> private segment bytes, from the code object's metadata."""
+    meta = text[text.index(".amdgpu_metadata"): text.index(".end_amdgpu_metadata")]
+    out = {}
+    for entry in meta.split("\n  - ")[1:]:
+        name = re.search(r"^\s+\.name:\s+(\S+)", entry, re.M)
+        priv = re.search(r"^\s+\.private_segment_fixed_size:\s+(\d+)", entry, re.M)
+        if name and priv:
+            out[name.group(1)] = int(priv.group(1))
+    return out
+
+
+# Largest private segment (bytes per lane) a kernel may use; kernels not listed use none.
+SCRATCH_BOUND = {"gemv_mm_grouped_kernel": 64}
+
+
+@pytest.mark.parametrize("src", qb.SOURCES)
+def test_private_segment_bounds(asm, src):
+    meta = kernel_metadata(asm[src])
+    assert meta or src == "ql_api.hip", src
+    for name, priv in meta.items():
+        bound = next((b for key, b in SCRATCH_BOUND.items() if key in name), 0)
+        assert priv <= bound, (src, name, priv, bound)
+
+
+# Kernels that run the split-K protocol (or its LittleBit form) and where they are compiled.
+SPLIT_KERNELS = [("ql_gemv.hip", "gemv_kernel"), ("ql_gemv.hip", "gemv_grouped_kernel"),
+                 ("ql_gemv_mm.hip", "gemv_mm_grouped_kernel"), ("ql_c4.hip", "c4_gemv_grouped_kernel"),
+                 ("ql_littlebit.hip", "lb_latent_kernel")]
+STORE_SC1 = re.compile(r"^\s+(global|flat)_store_dword\w*\s[^;\n]*\bsc1\b", re.M)
+LOAD_SC1 = re.compile(r"^\s+(global|flat)_load_dword\w*\s[^;\n]*\bsc1\b", re.M)
+
+
+@pytest.mark.parametrize("src,kernel", SPLIT_KERNELS)
+def test_split_protocol_scope_bits(asm, src, kernel):
+    bodies = {k: b for k, b in kernel_bodies(asm[src]).items() if kernel in k}
+    assert bodies, (src, kernel)
+    for name, body in bodies.items():
+        assert STORE_SC1.search(body), (name, "no agent-scope store")
+        assert LOAD_SC1.search(body), (name, "no agent-scope load")
+        pending = None
+        for line in body.split("\n"):
+            code = line.split(";")[0]
+            m = re.match(r"\s+((global|flat)_atomic\w*)(.*)", code)
+            if STORE_SC1.match(code):
+                pending = code.strip()
+            elif re.match(r"\s+s_waitcnt\b.*\bvmcnt\(0\)", code):
+                pending = None
+            elif m:
+                assert re.search(r"\bsc0\b", m.group(3)), (name, "atomic without return", code.strip())
+                assert pending is None, (name, "counter atomic after an unwaited store", pending, code.strip())
