@@ -187,7 +187,8 @@ def batched_leg(dev, warmup, steps, workloads=("qwen3_14b_stack", "qwen3_8b_pass
             del its
         del items
         torch.cuda.empty_cache()
-    return {"kernel": "gemv_mm_grouped_kernel (grouped launch, 2 <= M <= 16)", "points": out}
+    return {"kernel": "grouped launch: gemv_b4_grouped_kernel (2 <= M <= 4, 4x4x4 MFMA, lane per row), "
+                      "gemv_mm_grouped_kernel (5 <= M <= 16, 16x16x32 MFMA)", "points": out}
 
 
 def layered_leg(dev, warmup, steps, wl_name="qwen3_8b_pass", Ms=(1, 4)):

@@ -30,6 +30,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool grid_valid(int g) { return g == QL_GRID_T || g == QL_GRID_I2 || g == QL_GRID_I3; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxGroupedK = (int64_t)1 << 26;  // 2 * 16 tokens * K bytes of x stay below 2^31
 
 ql_status check_shape(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0) return fail(QL_EINVAL, "N and K must be positive (N=%lld, K=%lld)", (long long)N, (long long)K);
@@ -216,6 +217,10 @@ int64_t qlinear_grouped_prepare_split(ql_gemv_desc* descs, int32_t count, int64_
       return fail(QL_EINVAL, "descriptor %d: a list must not mix 4-bit containers and native grids", i), -1;
     if (!containers && check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
     if (check_ptrs({d.packed, d.pscales, d.x, d.y}) != QL_OK) return -1;
+    // the batched kernels address all 16 tokens' activations through one 32-bit buffer range
+    if (d.K > kMaxGroupedK)
+      return fail(QL_EINVAL, "descriptor %d: K=%d above the grouped launch's limit %lld", i, d.K,
+                  (long long)kMaxGroupedK), -1;
     if (d.kparts < 0) return fail(QL_EINVAL, "descriptor %d: kparts must be >= 0", i), -1;
     if (containers && d.kparts > 1) return fail(QL_EINVAL, "descriptor %d: containers are not split", i), -1;
     slabs += (d.N + QL_SLAB - 1) / QL_SLAB;
@@ -270,10 +275,7 @@ ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t
   if (count <= 0 || total_tasks <= 0 || total_tasks >= ((int64_t)1 << 31))
     return fail(QL_EINVAL, "bad count (%d) or task total (%lld)", count, (long long)total_tasks);
   QL_TRY(check_ptrs({descs, sched}));
-  if (M == 1)
-    return hip_status(ql::launch_gemv_grouped(descs, count, total_tasks, M, sched, stream), "grouped gemv launch");
-  return hip_status(ql::launch_gemv_mm_grouped(descs, count, total_tasks, M, sched, stream),
-                    "grouped batched gemv launch");
+  return hip_status(ql::launch_grouped_for(descs, count, total_tasks, M, sched, stream), "grouped gemv launch");
 }
 
 size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return ql::gemm_workspace_bytes(M, N, K); }

@@ -524,24 +524,6 @@ __device__ __forceinline__ void run_slab(int gr, const SlabCtx<M>& c, int p0, in
 constexpr int kWaves = QL_WAVES;          // waves per workgroup
 constexpr int kWgPerCu = QL_WG_PER_CU;    // resident workgroups per CU (LDS tables: 77 KB each)
 
-// Where task t lives: its descriptor, its slab's byte offset and grid.  Split
-// from the task so that a wave's first task can be located (two or three
-// dependent scalar loads) while the workgroup builds its LDS tables.
-struct TaskLoc {
-  int di;       // descriptor index
-  int gr;       // grid of the slab
-  int64_t off;  // byte offset of the slab in the packed matrix
-};
-
-__device__ __forceinline__ TaskLoc locate_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t) {
-  TaskLoc l;
-  l.di = find_desc(descs, count, t);
-  const ql_gemv_desc& d = descs[l.di];
-  const SplitTask st(d, t);
-  l.off = task_in_entry(d, t) ? slab_offset(st.slab, d.K, d.grid, d.blk_grid, d.blk_off, &l.gr) : 0;
-  return l;
-}
-
 // One wave task: one 64-row slab of one descriptor, or one part of its input
 // when the entry is split (partial sums then meet in the state buffer).
 // Descriptor fields are re-read per task, which keeps their live ranges short
@@ -650,7 +632,15 @@ hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream) {
 
 int64_t grouped_wave_slots(int M) {
   if (M == 1) return (int64_t)device_cu_count() * kWgPerCu * kWaves;
+  if (M <= 4) return b4_wave_slots();
   return mm_wave_slots();
+}
+
+hipError_t launch_grouped_for(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
+                              hipStream_t stream) {
+  if (M == 1) return launch_gemv_grouped(descs, count, total_tasks, M, sched, stream);
+  if (M <= 4) return launch_gemv_b4_grouped(descs, count, total_tasks, M, sched, stream);
+  return launch_gemv_mm_grouped(descs, count, total_tasks, M, sched, stream);
 }
 
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,

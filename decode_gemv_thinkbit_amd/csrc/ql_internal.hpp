@@ -36,9 +36,15 @@ struct MatArgs {
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
                                hipStream_t stream);
-// 2 <= M <= 16: the batched-decode kernel (MFMA), same descriptors and scheduler state
+// 2 <= M <= 16: the batched-decode kernel (16x16x32 MFMA), same descriptors and scheduler state
 hipError_t launch_gemv_mm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
                                   uint32_t* sched, hipStream_t stream);
+// 1 <= M <= 4: the lane-per-row batched-decode kernel (4x4x4 MFMA with broadcast activations)
+hipError_t launch_gemv_b4_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
+                                  uint32_t* sched, hipStream_t stream);
+// the grouped kernel for batch size M (1: batch-1, 2..4: lane-per-row MFMA, 5..16: 16x16x32 MFMA)
+hipError_t launch_grouped_for(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
+                              hipStream_t stream);
 hipError_t launch_c4_gemv(const MatArgs& a, hipStream_t stream);
 hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, uint32_t* sched,
                                   hipStream_t stream);
@@ -71,5 +77,6 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipS
 // waves of a persistent grouped launch at batch size M (1: batch-1 kernel, else batched)
 int64_t grouped_wave_slots(int M);
 int64_t mm_wave_slots();
+int64_t b4_wave_slots();
 
 }  // namespace ql

@@ -264,6 +264,24 @@ struct SplitTask {
   }
 };
 
+// Where task t lives: its descriptor, its slab's byte offset and grid.  Split
+// from the task so that a wave's first task can be located (two or three
+// dependent scalar loads) while the workgroup builds its LDS tables.
+struct TaskLoc {
+  int di;       // descriptor index
+  int gr;       // grid of the slab
+  int64_t off;  // byte offset of the slab in the packed matrix
+};
+
+__device__ __forceinline__ TaskLoc locate_task(const ql_gemv_desc* __restrict__ descs, int count, int64_t t) {
+  TaskLoc l;
+  l.di = find_desc(descs, count, t);
+  const ql_gemv_desc& d = descs[l.di];
+  const SplitTask st(d, t);
+  l.off = task_in_entry(d, t) ? slab_offset(st.slab, d.K, d.grid, d.blk_grid, d.blk_off, &l.gr) : 0;
+  return l;
+}
+
 // ---------------------------------------------------------------- task queues
 // Persistent grouped launches run tasks 0..total-1, numbered by the host
 // longest first.  Wave w of the launch takes task w; the rest, r = t - nwaves,

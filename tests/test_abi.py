@@ -236,8 +236,9 @@ def test_split_periods_tile_every_row():
 def test_wave_slots_query():
     L = ql.lib()
     assert L.qlinear_grouped_wave_slots(0) == -1 and L.qlinear_grouped_wave_slots(17) == -1
-    n1, n4 = L.qlinear_grouped_wave_slots(1), L.qlinear_grouped_wave_slots(4)
-    assert n1 > 0 and n4 > 0 and n1 % 16 == 0 and n4 % 12 == 0
+    n1, n4, n16 = (L.qlinear_grouped_wave_slots(m) for m in (1, 4, 16))
+    # batch 1 and 2..4 tokens: 2 workgroups x 8 waves per CU; 5..16 tokens: 2 x 6
+    assert n1 > 0 and n1 == n4 and n1 % 16 == 0 and n16 > 0 and n16 % 12 == 0
 
 
 def test_read_probe_argument_errors():
@@ -248,3 +249,14 @@ def test_read_probe_argument_errors():
     assert L.qlinear_read_probe(p, 1 << 32, p, None) == 1       # offsets are 32-bit
     assert L.qlinear_read_probe(None, 1024, p, None) == 1
     assert L.qlinear_read_probe(p, 1024, ctypes.c_void_p(0x10004), None) == 1  # misaligned out
+
+
+def test_grouped_prepare_rejects_rows_beyond_the_batched_range():
+    """The batched kernels address all tokens' activations in one 32-bit range: K above 2^26
+    is refused before any launch."""
+    L = ql.lib()
+    arr = _descs([(64, (1 << 26) + 128, 0)], [1])
+    assert L.qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), 1) == -1
+    assert b"K=" in L.qlinear_last_error()
+    arr = _descs([(64, 1 << 26, 0)], [1])
+    assert L.qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), 1) == 1

@@ -95,7 +95,8 @@ def test_private_segment_bounds(asm, src):
 
 # Kernels that run the split-K protocol (or its LittleBit form) and where they are compiled.
 SPLIT_KERNELS = [("ql_gemv.hip", "gemv_kernel"), ("ql_gemv.hip", "gemv_grouped_kernel"),
-                 ("ql_gemv_mm.hip", "gemv_mm_grouped_kernel"), ("ql_c4.hip", "c4_gemv_grouped_kernel"),
+                 ("ql_gemv_mm.hip", "gemv_mm_grouped_kernel"), ("ql_gemv_b4.hip", "gemv_b4_grouped_kernel"),
+                 ("ql_c4.hip", "c4_gemv_grouped_kernel"),
                  ("ql_littlebit.hip", "lb_latent_kernel")]
 STORE_SC1 = re.compile(r"^\s+(global|flat)_store_dword\w*\s[^;\n]*\bsc1\b", re.M)
 LOAD_SC1 = re.compile(r"^\s+(global|flat)_load_dword\w*\s[^;\n]*\bsc1\b", re.M)
