@@ -632,15 +632,13 @@ hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream) {
 
 int64_t grouped_wave_slots(int M) {
   if (M == 1) return (int64_t)device_cu_count() * kWgPerCu * kWaves;
-  if (M <= 4) return b4_wave_slots();
-  return mm_wave_slots();
+  return b4_wave_slots(M);
 }
 
 hipError_t launch_grouped_for(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
                               hipStream_t stream) {
   if (M == 1) return launch_gemv_grouped(descs, count, total_tasks, M, sched, stream);
-  if (M <= 4) return launch_gemv_b4_grouped(descs, count, total_tasks, M, sched, stream);
-  return launch_gemv_mm_grouped(descs, count, total_tasks, M, sched, stream);
+  return launch_gemv_b4_grouped(descs, count, total_tasks, M, sched, stream);
 }
 
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,

@@ -1,5 +1,5 @@
-// Batched decode at 2..4 tokens over ThinkBit-packed weights (gfx950), on the
-// matrix cores with the batch-1 kernel's mapping.
+// Batched decode, 2 <= M <= 16 tokens, over ThinkBit-packed weights (gfx950), on
+// the matrix cores with the batch-1 kernel's mapping.
 //
 // A decode step at a small batch is still one pass over the weights: each
 // packed byte is read once and used by every token (ThinkBit summary page,
@@ -16,11 +16,12 @@
 // (CBSZ = 4, ABID = the source block), so per 128-input group one 16-byte load
 // per lane holds every activation the group needs: lane 4b + t holds token t's
 // inputs 8b .. 8b+7, and MFMA j of the group (inputs 4j .. 4j+3) takes block
-// j / 2, half j % 2.  Tokens past M read as zero.
+// j / 2, half j % 2.  Tokens past M read as zero.  Up to 16 tokens run as
+// token groups of four: every code operand feeds one MFMA per group.
 //
 // Per stored byte the VALU issues only the table address (and, for ternary,
-// one OR per byte pair); the products leave the VALU entirely, so the four
-// token sums cost about what one dot2 chain costs in the batch-1 kernel.
+// one OR per byte pair and the copies that pair operands across entries); the
+// products leave the VALU entirely.
 //
 // Decode operands (four consecutive inputs per MFMA):
 //   ternary: a byte pair covers 10 inputs.  The table entry of a byte is
@@ -42,16 +43,19 @@ namespace {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-#ifndef QL_B4_WAVES
-#define QL_B4_WAVES 8
-#endif
-#ifndef QL_B4_WAVES_PER_EU
-#define QL_B4_WAVES_PER_EU 4
-#endif
-constexpr int kB4Waves = QL_B4_WAVES;  // waves per workgroup
-constexpr int kB4WgPerCu = 2;          // resident workgroups per CU (LDS tables: 77 KB each)
-constexpr int kB4Tokens = 4;
-static_assert(kB4Tokens * 64 <= kPartWords, "a split part stores 4 tokens per lane");
+// Token groups: TG groups of four tokens (M <= 4 TG), one MFMA per group per code
+// operand, all against the same decoded codes.  Up to two groups the kernel keeps
+// the batch-1 occupancy (8-wave workgroups, 4 waves per SIMD); three and four
+// groups need more registers for activations and sums (6-wave workgroups, 3 per SIMD).
+constexpr int b4_waves(int TG) { return TG <= 2 ? 8 : 6; }
+constexpr int b4_waves_per_eu(int TG) { return TG <= 2 ? 4 : 3; }
+constexpr int kB4WgPerCu = 2;  // resident workgroups per CU (LDS tables: 77 KB each)
+constexpr int kB4MaxTG = 4;
+static_assert(4 * kB4MaxTG * 64 <= kPartWords, "a split part stores 16 tokens per lane");
+// MFMA chains per token group within one 128-input group: one group of tokens
+// alternates two chains, so that consecutive MFMAs do not wait on each other;
+// with several token groups their chains interleave instead.
+constexpr int b4_chains(int TG) { return TG == 1 ? 2 : 1; }
 
 // acc + x(block ABID, broadcast) * codes(lane's row): one MFMA of four inputs.
 template <int ABID>
@@ -61,47 +65,70 @@ __device__ __forceinline__ f32x4_t mma4(uint32_t x0, uint32_t x1, uint32_t c0, u
                                                 ABID, 0);
 }
 
-// MFMA jj (0..31) of a group: x half jj % 2 of block jj / 2, into chain jj % 2
-// (two independent chains, so consecutive MFMAs do not wait on each other);
-// the first MFMA of each chain starts from zero.
-template <int JJ>
-__device__ __forceinline__ void group_mma(const u32x4_t& xg, uint32_t c0, uint32_t c1, f32x4_t (&ch)[2]) {
+// Sums of one 128-input group: chain c of token group tg.
+template <int TG>
+struct Chains {
+  f32x4_t v[TG][b4_chains(TG)];
+};
+
+// MFMA jj (0..31) of a group, for every token group: x half jj % 2 of block
+// jj / 2, into chain jj % chains; the first MFMA of each chain starts from zero.
+template <int TG, int JJ>
+__device__ __forceinline__ void group_mma(const u32x4_t (&xg)[TG], uint32_t c0, uint32_t c1, Chains<TG>& ch) {
+  constexpr int NC = b4_chains(TG);
   constexpr f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t x0 = (JJ & 1) ? xg.z : xg.x, x1 = (JJ & 1) ? xg.w : xg.y;
-  ch[JJ & 1] = mma4<(JJ >> 1)>(x0, x1, c0, c1, JJ < 2 ? z : ch[JJ & 1]);
-}
-
-// y[t] += s * (sum of the group's chains), token t = component t.
-__device__ __forceinline__ void flush(float s, const f32x4_t (&ch)[2], float (&y)[kB4Tokens]) {
 #pragma unroll
-  for (int t = 0; t < kB4Tokens; ++t) y[t] = fmaf(s, ch[0][t] + ch[1][t], y[t]);
+  for (int tg = 0; tg < TG; ++tg) {
+    const uint32_t x0 = (JJ & 1) ? xg[tg].z : xg[tg].x, x1 = (JJ & 1) ? xg[tg].w : xg[tg].y;
+    ch.v[tg][JJ % NC] = mma4<(JJ >> 1)>(x0, x1, c0, c1, JJ < NC ? z : ch.v[tg][JJ % NC]);
+  }
 }
 
-// Activations: token t = lane & 3 of the M x K bf16 batch, inputs 8 (lane >> 2)
-// .. +7 of each 128-input group.  Tokens past M, and groups at or past G, read
-// as zero through the buffer's range check.
-struct XSrc4 {
+// y[4 tg + t] += s * (sum of token group tg's chains), token t = component t.
+template <int TG>
+__device__ __forceinline__ void flush(float s, const Chains<TG>& ch, float (&y)[4 * TG]) {
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float v = ch.v[tg][0][t];
+#pragma unroll
+      for (int c = 1; c < b4_chains(TG); ++c) v += ch.v[tg][c][t];
+      y[4 * tg + t] = fmaf(s, v, y[4 * tg + t]);
+    }
+}
+
+// Activations: token 4 tg + (lane & 3) of the M x K bf16 batch, inputs
+// 8 (lane >> 2) .. +7 of each 128-input group.  Tokens past M, and groups at
+// or past G, read as zero through the buffer's range check.
+template <int TG>
+struct XSrc {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t base;
-  int G;
-  __device__ __forceinline__ XSrc4(const uint16_t* x, int M, int K, int lane)
+  uint32_t base;  // token (lane & 3) of token group 0
+  int M, G, K;
+  __device__ __forceinline__ XSrc(const uint16_t* x, int M_, int K_, int lane)
       : rsrc(__builtin_amdgcn_make_buffer_rsrc(uniform_ptr(x), (short)0,
-                                               __builtin_amdgcn_readfirstlane(2 * M * K), 0x00020000)),
-        G(K / kGroup) {
-    const int t = lane & 3;
-    base = (t < M ? (uint32_t)(2 * t * K) : (uint32_t)(2 * M * K)) + 16u * (uint32_t)(lane >> 2);
+                                               __builtin_amdgcn_readfirstlane(2 * M_ * K_), 0x00020000)),
+        M(M_), G(K_ / kGroup), K(K_) {
+    base = (uint32_t)(2 * (lane & 3) * K) + 16u * (uint32_t)(lane >> 2);
   }
-  __device__ __forceinline__ u32x4_t group(int g) const {
-    const uint32_t off = g < G ? 256u * (uint32_t)g : 0x80000000u;
+  // token group tg's x of group g (tokens past M land past the buffer's range)
+  __device__ __forceinline__ u32x4_t load(int g, int tg) const {
+    const uint32_t off = g < G ? 256u * (uint32_t)g + (uint32_t)(8 * tg * K) : 0x80000000u;
     const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, base + off, 0, 0);
     return u32x4_t{(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
   }
+  __device__ __forceinline__ void group(u32x4_t (&xg)[TG], int g) const {
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) xg[tg] = load(g, tg);
+  }
 };
 
+template <int TG>
 struct Ctx {
   const uint8_t* codes;    // slab base
   const uint16_t* scales;  // slab's scale block
-  XSrc4 xs;
+  XSrc<TG> xs;
   int K, G, lane;
   const uint8_t* lut;
 };
@@ -174,7 +201,8 @@ __device__ __forceinline__ void t_scales(const u32x4_t& sa, const u32x2_t& sb, i
 #endif
 
 // Periods p0..p1-1 of the slab (the last may be partial).
-__device__ void run_t(const Ctx& c, int p0, int p1, float (&y)[kB4Tokens]) {
+template <int TG>
+__device__ void run_t(const Ctx<TG>& c, int p0, int p1, float (&y)[4 * TG]) {
   if (p0 >= p1) return;
   const int nchunks = (c.K + 79) / 80;
   const bool last_half = nchunks - 8 * (p1 - 1) <= 4;  // the row ends in the first half of period p1 - 1
@@ -190,15 +218,15 @@ __device__ void run_t(const Ctx& c, int p0, int p1, float (&y)[kB4Tokens]) {
   u32x2_t sb = ld_scale_blk_lo(c.scales, ((5 * p0) >> 3) + 1 < G8 ? ((5 * p0) >> 3) + 1 : (5 * p0) >> 3, c.lane);
   // x of group gl of the period lives in xg[gl & 1]; group 5 (the next
   // period's group 0) lands in xg[1] and moves to xg[0] at the period's end
-  u32x4_t xg[2];
-  xg[0] = c.xs.group(5 * p0);
+  u32x4_t xg[2][TG];
+  c.xs.group(xg[0], 5 * p0);
   TEnt A, B;
   t_lds<0, R>(A, d, lane_off, c.lut);
   lgkm_wait0();
   for (int p = p0; p < p1; ++p) {
     const bool more = p + 1 < p1;
     float sc[5];
-    f32x4_t ch[2];
+    Chains<TG> ch;
     auto step = [&](auto u) __attribute__((always_inline)) {
       constexpr int U = decltype(u)::value;
       constexpr bool odd = (U & 1) != 0;
@@ -221,9 +249,9 @@ __device__ void run_t(const Ctx& c, int p0, int p1, float (&y)[kB4Tokens]) {
         constexpr int m = decltype(m_)::value;
         constexpr int j = kTMfma * U + m;  // MFMA within the period
         constexpr int gl = j / 32, jj = j % 32;
-        if constexpr (jj == 0) xg[(gl + 1) & 1] = c.xs.group(5 * p + gl + 1);  // next group's x
+        if constexpr (jj == 0) c.xs.group(xg[(gl + 1) & 1], 5 * p + gl + 1);  // next group's x
         const u32x2_t cv = t_code<m / 5, m % 5>(cur);
-        group_mma<jj>(xg[gl & 1], cv.x, cv.y, ch);
+        group_mma<TG, jj>(xg[gl & 1], cv.x, cv.y, ch);
         if constexpr (j == 31) {
           // the period's scales, needed from here on; then the next period's blocks
           // (loaded a period ahead, so the first flush of a period never waits on them)
@@ -240,7 +268,8 @@ __device__ void run_t(const Ctx& c, int p0, int p1, float (&y)[kB4Tokens]) {
     };
     sfor<kTUnits / 2>(step);
     if (more || !last_half) sfor_from<kTUnits / 2, kTUnits / 2>(step);
-    xg[0] = xg[1];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) xg[0][tg] = xg[1][tg];
   }
 }
 
@@ -261,14 +290,15 @@ __device__ __forceinline__ void i2_lds(I2E& b, const uint4 (&d)[4], uint32_t lan
   });
 }
 
-__device__ void run_i2(const Ctx& c, int g0, int g1, float (&y)[kB4Tokens]) {
+template <int TG>
+__device__ void run_i2(const Ctx<TG>& c, int g0, int g1, float (&y)[4 * TG]) {
   if (g0 >= g1) return;
   uint32_t lane_off = (uint32_t)(c.lane & 3) << 3;
   const ChunkSrc src(c.codes, 2 * g1, c.lane);
   uint4 d[4];
   sfor<4>([&](auto q) __attribute__((always_inline)) { d[decltype(q)::value] = src.load(2 * g0 + decltype(q)::value); });
-  u32x4_t xg[2];
-  xg[0] = c.xs.group(g0);
+  u32x4_t xg[2][TG];
+  c.xs.group(xg[0], g0);
   I2E A, B;
   i2_lds<0, 0>(A, d, lane_off, c.lut);
   lgkm_wait0();
@@ -278,9 +308,9 @@ __device__ void run_i2(const Ctx& c, int g0, int g1, float (&y)[kB4Tokens]) {
       const int g = gb + S;
       if (g < g1) {
         const float sc = ld_scale(c.scales, g, c.lane);
-        xg[S ^ 1] = c.xs.group(g + 1);
+        c.xs.group(xg[S ^ 1], g + 1);
         const bool more = g + 1 < g1;
-        f32x4_t ch[2];
+        Chains<TG> ch;
         sfor<4>([&](auto u) __attribute__((always_inline)) {
           constexpr int U = decltype(u)::value;
           constexpr bool even = ((4 * S + U) & 1) == 0;  // buffer of this unit
@@ -297,7 +327,7 @@ __device__ void run_i2(const Ctx& c, int g0, int g1, float (&y)[kB4Tokens]) {
           sched_fence();
           sfor<8>([&](auto bi) __attribute__((always_inline)) {
             constexpr int jj = 8 * U + decltype(bi)::value;
-            group_mma<jj>(xg[S], cur.e[decltype(bi)::value].x, cur.e[decltype(bi)::value].y, ch);
+            group_mma<TG, jj>(xg[S], cur.e[decltype(bi)::value].x, cur.e[decltype(bi)::value].y, ch);
           });
           after(lane_off, y);
           sched_fence();
@@ -331,13 +361,14 @@ __device__ __forceinline__ void i3_lds(I3E& b, const uint4 (&d)[6], const uint8_
   });
 }
 
-__device__ void run_i3(const Ctx& c, int g0, int g1, float (&y)[kB4Tokens]) {
+template <int TG>
+__device__ void run_i3(const Ctx<TG>& c, int g0, int g1, float (&y)[4 * TG]) {
   if (g0 >= g1) return;
   const ChunkSrc src(c.codes, 3 * g1, c.lane);
   uint4 d[6];
   sfor<6>([&](auto q) __attribute__((always_inline)) { d[decltype(q)::value] = src.load(3 * g0 + decltype(q)::value); });
-  u32x4_t xg[2];
-  xg[0] = c.xs.group(g0);
+  u32x4_t xg[2][TG];
+  c.xs.group(xg[0], g0);
   const uint32_t lane_off = i3_lane_off(c.lane);
   uint32_t tok = 0;  // step token: rewritten (as far as the compiler knows) after each step's arithmetic
   I3E A, B;
@@ -349,9 +380,9 @@ __device__ void run_i3(const Ctx& c, int g0, int g1, float (&y)[kB4Tokens]) {
       const int g = gb + S;
       if (g < g1) {
         const float sc = ld_scale(c.scales, g, c.lane);
-        xg[S ^ 1] = c.xs.group(g + 1);
+        c.xs.group(xg[S ^ 1], g + 1);
         const bool more = g + 1 < g1;
-        f32x4_t ch[2];
+        Chains<TG> ch;
         sfor<4>([&](auto u) __attribute__((always_inline)) {
           constexpr int U = decltype(u)::value;
           constexpr bool even = ((4 * S + U) & 1) == 0;
@@ -370,7 +401,7 @@ __device__ void run_i3(const Ctx& c, int g0, int g1, float (&y)[kB4Tokens]) {
           sfor<8>([&](auto m_) __attribute__((always_inline)) {
             constexpr int m = decltype(m_)::value;
             constexpr int jj = 8 * U + m;
-            group_mma<jj>(xg[S], cur.e[2 * m], cur.e[2 * m + 1], ch);
+            group_mma<TG, jj>(xg[S], cur.e[2 * m], cur.e[2 * m + 1], ch);
           });
           after(tok, y);
           sched_fence();
@@ -385,44 +416,49 @@ __device__ void run_i3(const Ctx& c, int g0, int g1, float (&y)[kB4Tokens]) {
 // ---------------------------------------------------------------- task, kernel
 // One wave task: one 64-row slab of one descriptor, all tokens, or one part of
 // its input when the entry is split (partial sums meet in the state buffer).
+template <int TG>
 __device__ __forceinline__ void b4_task(const ql_gemv_desc* __restrict__ descs, const TaskLoc& loc, int64_t t, int M,
                                         const uint8_t* lut, int lane, uint32_t* state) {
+  constexpr int NT = 4 * TG;
   const ql_gemv_desc& d = descs[loc.di];
   if (!task_in_entry(d, t)) return;
   const SplitTask st(d, t);
   const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
-  float y[kB4Tokens];
+  float y[NT];
 #pragma unroll
-  for (int i = 0; i < kB4Tokens; ++i) y[i] = 0.0f;
-  const Ctx c{static_cast<const uint8_t*>(d.packed) + loc.off, d.pscales + st.slab * (int64_t)G8 * kSlab * 8,
-              XSrc4(d.x, M, K, lane), K, G, lane, lut};
+  for (int i = 0; i < NT; ++i) y[i] = 0.0f;
+  const Ctx<TG> c{static_cast<const uint8_t*>(d.packed) + loc.off, d.pscales + st.slab * (int64_t)G8 * kSlab * 8,
+                  XSrc<TG>(d.x, M, K, lane), K, G, lane, lut};
   if (loc.gr == QL_GRID_T) {
-    run_t(c, st.p0(K), st.p1(K), y);
+    run_t<TG>(c, st.p0(K), st.p1(K), y);
   } else {
     const int k0 = st.k0(K), k1 = st.k1(K);
     const int g0 = 2 * k0, g1 = (2 * k1 < G) ? 2 * k1 : G;
     if (loc.gr == QL_GRID_I2)
-      run_i2(c, g0, g1, y);
+      run_i2<TG>(c, g0, g1, y);
     else
-      run_i3(c, g0, g1, y);
+      run_i3<TG>(c, g0, g1, y);
   }
   if (st.split()) {
     float* sl = st.slots(d, state);
 #pragma unroll
-    for (int i = 0; i < kB4Tokens; ++i) st.put(sl, 64 * i + lane, y[i]);
+    for (int i = 0; i < NT; ++i)
+      if (i < M) st.put(sl, 64 * i + lane, y[i]);
     if (!st.arrive(st.counter(d, state), lane)) return;
-    st.totals<kB4Tokens, 4>(sl, y, lane);
+    st.totals<NT, 4>(sl, y, lane);
   }
   const int64_t row = (int64_t)st.slab * kSlab + lane;
   if (row < d.N)
 #pragma unroll
-    for (int i = 0; i < kB4Tokens; ++i)
+    for (int i = 0; i < NT; ++i)
       if (i < M) d.y[(int64_t)i * d.N + row] = y[i];
 }
 
 // The grouped launch of the batch-1 kernel with this task body.
-__global__ void __launch_bounds__(kB4Waves * 64, QL_B4_WAVES_PER_EU) gemv_b4_grouped_kernel(
+template <int TG>
+__global__ void __launch_bounds__(b4_waves(TG) * 64, b4_waves_per_eu(TG)) gemv_b4_grouped_kernel(
     const ql_gemv_desc* __restrict__ descs, int count, int64_t total, int M, uint32_t* __restrict__ sched) {
+  constexpr int kB4Waves = b4_waves(TG);
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -438,7 +474,7 @@ __global__ void __launch_bounds__(kB4Waves * 64, QL_B4_WAVES_PER_EU) gemv_b4_gro
   }
   while (t >= 0) {
     const uint32_t claim = tq.claim(lane);
-    b4_task(descs, loc, t, M, lut, lane, sched);
+    b4_task<TG>(descs, loc, t, M, lut, lane, sched);
     t = tq.resolve(claim, lane);
     if (t >= 0) loc = locate_task(descs, count, t);
   }
@@ -447,17 +483,31 @@ __global__ void __launch_bounds__(kB4Waves * 64, QL_B4_WAVES_PER_EU) gemv_b4_gro
 
 }  // namespace
 
-int64_t b4_wave_slots() { return (int64_t)device_cu_count() * kB4WgPerCu * kB4Waves; }
+int64_t b4_wave_slots(int M) {
+  return (int64_t)device_cu_count() * kB4WgPerCu * b4_waves((M + 3) / 4);
+}
+
+template <int TG>
+static hipError_t launch_tg(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
+                            hipStream_t stream) {
+  constexpr int W = b4_waves(TG);
+  const int slots = device_cu_count() * kB4WgPerCu;
+  const int64_t wg_needed = (total_tasks + W - 1) / W;
+  const int grid = (int)(wg_needed < slots ? wg_needed : slots);
+  hipLaunchKernelGGL(gemv_b4_grouped_kernel<TG>, dim3(grid), dim3(W * 64), 0, stream, descs, count, total_tasks, M,
+                     sched);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv_b4_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
                                   uint32_t* sched, hipStream_t stream) {
-  if (M < 1 || M > kB4Tokens) return hipErrorInvalidValue;
-  const int slots = device_cu_count() * kB4WgPerCu;
-  const int64_t wg_needed = (total_tasks + kB4Waves - 1) / kB4Waves;
-  const int grid = (int)(wg_needed < slots ? wg_needed : slots);
-  hipLaunchKernelGGL(gemv_b4_grouped_kernel, dim3(grid), dim3(kB4Waves * 64), 0, stream, descs, count, total_tasks, M,
-                     sched);
-  return hipGetLastError();
+  switch ((M + 3) / 4) {
+    case 1: return launch_tg<1>(descs, count, total_tasks, M, sched, stream);
+    case 2: return launch_tg<2>(descs, count, total_tasks, M, sched, stream);
+    case 3: return launch_tg<3>(descs, count, total_tasks, M, sched, stream);
+    case 4: return launch_tg<4>(descs, count, total_tasks, M, sched, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace ql

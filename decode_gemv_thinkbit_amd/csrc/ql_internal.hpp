@@ -36,13 +36,11 @@ struct MatArgs {
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
                                hipStream_t stream);
-// 2 <= M <= 16: the batched-decode kernel (16x16x32 MFMA), same descriptors and scheduler state
-hipError_t launch_gemv_mm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
-                                  uint32_t* sched, hipStream_t stream);
-// 1 <= M <= 4: the lane-per-row batched-decode kernel (4x4x4 MFMA with broadcast activations)
+// 1 <= M <= 16: the batched-decode kernel (lane per row, 4x4x4 MFMA with broadcast activations),
+// same descriptors and scheduler state as the batch-1 launch
 hipError_t launch_gemv_b4_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
                                   uint32_t* sched, hipStream_t stream);
-// the grouped kernel for batch size M (1: batch-1, 2..4: lane-per-row MFMA, 5..16: 16x16x32 MFMA)
+// the grouped kernel for batch size M (1: batch-1, 2..16: batched decode)
 hipError_t launch_grouped_for(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
                               hipStream_t stream);
 hipError_t launch_c4_gemv(const MatArgs& a, hipStream_t stream);
@@ -76,7 +74,6 @@ int device_cu_count();
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
 // waves of a persistent grouped launch at batch size M (1: batch-1 kernel, else batched)
 int64_t grouped_wave_slots(int M);
-int64_t mm_wave_slots();
-int64_t b4_wave_slots();
+int64_t b4_wave_slots(int M);
 
 }  // namespace ql

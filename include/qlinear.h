@@ -225,11 +225,11 @@ int64_t qlinear_grouped_wave_slots(int32_t M);
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
  * descs (dev), count entries) in one persistent launch, at one batch size M for all entries
  * (1 <= M <= 16; each x is M x K, each y M x N).  M = 1 runs the batch-1 kernel (v_dot2);
- * 2 <= M <= 4 a kernel with the batch-1 mapping (lane = weight row) whose products run on
- * 4x4x4 MFMA with the activations broadcast to every row block; 5 <= M <= 16 the batched-
- * decode kernel on 16x16x32 MFMA.  Both decode each packed byte once for all M tokens
- * (products exact, fp32 sums; summary page, section "What it is": a decode step at a small
- * batch still streams every weight once).  M outside 1..16 returns QL_EINVAL.  Waves take tasks (64-row slabs, or parts of them after prepare_split) from
+ * 2 <= M <= 16 the batched-decode kernel: the batch-1 mapping (lane = weight row), with the
+ * products on 4x4x4 MFMA and the activations of four tokens at a time broadcast to every
+ * row block.  It decodes each packed byte once for all M tokens (products exact, fp32 sums;
+ * summary page, section "What it is": a decode step at a small batch still streams every
+ * weight once).  M outside 1..16 returns QL_EINVAL.  Waves take tasks (64-row slabs, or parts of them after prepare_split) from
  * atomic queue counters in the state buffer `sched` (dev, 16-byte aligned, owned by the
  * caller; QL_SCHED_WORDS uint32 after qlinear_grouped_prepare, the state_words reported by
  * qlinear_grouped_prepare_split otherwise): its counters must be all zero when a launch

@@ -5,8 +5,7 @@ the target rules (CPU only: hipcc cross-compiles without a GPU).
   write-back or discard of that cache (all stores are vector stores).
 - No packed-fp32 VALU operation is emitted (the build turns the feature off).
 - The batch-1 GEMV kernels use no scratch (their VGPRs do not spill); every other kernel's
-  private segment stays within a stated bound (zero for all but the batched-decode kernel,
-  whose few spills sit outside its inner loop).
+  private segment stays within a stated bound (at present zero for every kernel).
 - The split-K protocol (a part's partial sums stored at agent scope, a wait for those
   stores, then an agent-scope counter increment; the last part loads the partials at agent
   scope) is emitted with those properties: agent-scope stores and loads carry sc1 (they go
@@ -81,7 +80,7 @@ def kernel_metadata(text):
 
 
 # Largest private segment (bytes per lane) a kernel may use; kernels not listed use none.
-SCRATCH_BOUND = {"gemv_mm_grouped_kernel": 64}
+SCRATCH_BOUND = {}
 
 
 @pytest.mark.parametrize("src", qb.SOURCES)
@@ -95,7 +94,7 @@ def test_private_segment_bounds(asm, src):
 
 # Kernels that run the split-K protocol (or its LittleBit form) and where they are compiled.
 SPLIT_KERNELS = [("ql_gemv.hip", "gemv_kernel"), ("ql_gemv.hip", "gemv_grouped_kernel"),
-                 ("ql_gemv_mm.hip", "gemv_mm_grouped_kernel"), ("ql_gemv_b4.hip", "gemv_b4_grouped_kernel"),
+                 ("ql_gemv_b4.hip", "gemv_b4_grouped_kernel"),
                  ("ql_c4.hip", "c4_gemv_grouped_kernel"),
                  ("ql_littlebit.hip", "lb_latent_kernel")]
 STORE_SC1 = re.compile(r"^\s+(global|flat)_store_dword\w*\s[^;\n]*\bsc1\b", re.M)
