@@ -187,7 +187,7 @@ def batched_leg(dev, warmup, steps, workloads=("qwen3_14b_stack", "qwen3_8b_pass
             del its
         del items
         torch.cuda.empty_cache()
-    return {"kernel": "gemv_b4_grouped_kernel (grouped launch, 2 <= M <= 16: lane per row, 4x4x4 MFMA, "
+    return {"kernel": "gemv_grouped_kernel (grouped launch, 2 <= M <= 16: lane per row, 4x4x4 MFMA, "
                       "activations broadcast from one row block)", "points": out}
 
 
@@ -257,7 +257,7 @@ def layered_leg(dev, warmup, steps, wl_name="qwen3_8b_pass", Ms=(1, 4)):
     del items1
     torch.cuda.empty_cache()
     return {"variant": "dependency-respecting: 4 grouped launches per layer in one HIP graph",
-            "kernels": "gemv_grouped_kernel<1> (M = 1), gemv_b4_grouped_kernel (M > 1)", "points": out}
+            "kernels": "gemv_grouped_kernel (every M)", "points": out}
 
 
 def small_leg(dev, reps=50, flush_mb=512):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 SANITIZE = os.environ.get("QLINEAR_SANITIZE") == "1"
 OUT_DIR = os.path.join(HERE, "_build_san" if SANITIZE else "_build")
 LIB = os.path.join(OUT_DIR, "libqlinear.so")
-SOURCES = ["ql_api.hip", "ql_pack.hip", "ql_gemv.hip", "ql_gemv_b4.hip", "ql_gemm.hip", "ql_c4.hip", "ql_alloc.hip", "ql_littlebit.hip", "ql_probe.hip", "ql_noalloc.hip", "ql_check.hip"]
+SOURCES = ["ql_api.hip", "ql_pack.hip", "ql_gemv.hip", "ql_gemm.hip", "ql_c4.hip", "ql_alloc.hip", "ql_littlebit.hip", "ql_probe.hip", "ql_noalloc.hip", "ql_check.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -198,12 +198,11 @@ static ql_status mat_args(int64_t M, int64_t N, int64_t K, int grid, const int8_
 
 ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t* blk_grid, const int64_t* blk_off,
                        const void* packed, const uint16_t* pscales, const uint16_t* x, float* y, hipStream_t stream) {
-  if (M < 1 || M > 8) return fail(QL_EINVAL, "gemv needs 1 <= M <= 8 (M=%lld)", (long long)M);
+  if (M < 1 || M > 16) return fail(QL_EINVAL, "gemv needs 1 <= M <= 16 (M=%lld)", (long long)M);
   ql::MatArgs a;
   QL_TRY(mat_args(M, N, K, grid, blk_grid, blk_off, packed, pscales, x, y, &a));
-  if (M == 1) return hip_status(ql::launch_gemv(a, 1, stream), "gemv launch");
-  // 2 <= M <= 8: a multi-token contraction, run on the MFMA path
-  return hip_status(ql::launch_gemm(a, (int)M, nullptr, 0, stream), "gemv (MFMA) launch");
+  if (K > ((int64_t)1 << 26)) return fail(QL_EINVAL, "gemv needs K <= 2^26 (K=%lld)", (long long)K);
+  return hip_status(ql::launch_gemv(a, (int)M, stream), "gemv launch");
 }
 
 int64_t qlinear_grouped_prepare_split(ql_gemv_desc* descs, int32_t count, int64_t min_tasks, int64_t* state_words) {
@@ -275,7 +274,7 @@ ql_status qlinear_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t
   if (count <= 0 || total_tasks <= 0 || total_tasks >= ((int64_t)1 << 31))
     return fail(QL_EINVAL, "bad count (%d) or task total (%lld)", count, (long long)total_tasks);
   QL_TRY(check_ptrs({descs, sched}));
-  return hip_status(ql::launch_grouped_for(descs, count, total_tasks, M, sched, stream), "grouped gemv launch");
+  return hip_status(ql::launch_gemv_grouped(descs, count, total_tasks, M, sched, stream), "grouped gemv launch");
 }
 
 size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return ql::gemm_workspace_bytes(M, N, K); }

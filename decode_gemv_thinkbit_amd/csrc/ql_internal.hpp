@@ -33,16 +33,12 @@ struct MatArgs {
   int32_t N, K, grid;
 };
 
+// The decode GEMV (ql_gemv.hip): one lane per weight row, LDS decode tables, products on
+// 4x4x4 MFMA; 1 <= M <= 16 tokens.  A single matrix (static slab striding) or a grouped
+// descriptor list (task queues and split-K state in `sched`).
 hipError_t launch_gemv(const MatArgs& a, int M, hipStream_t stream);
 hipError_t launch_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
                                hipStream_t stream);
-// 1 <= M <= 16: the batched-decode kernel (lane per row, 4x4x4 MFMA with broadcast activations),
-// same descriptors and scheduler state as the batch-1 launch
-hipError_t launch_gemv_b4_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M,
-                                  uint32_t* sched, hipStream_t stream);
-// the grouped kernel for batch size M (1: batch-1, 2..16: batched decode)
-hipError_t launch_grouped_for(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int M, uint32_t* sched,
-                              hipStream_t stream);
 hipError_t launch_c4_gemv(const MatArgs& a, hipStream_t stream);
 hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_slabs, uint32_t* sched,
                                   hipStream_t stream);
@@ -72,8 +68,7 @@ hipError_t launch_lb_gemv(const ql_littlebit& w, const uint16_t* x, float* y, vo
 int device_cu_count();
 // read-bandwidth probe over `bytes` (a multiple of 1024) of device memory; out ^= XOR of the data
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
-// waves of a persistent grouped launch at batch size M (1: batch-1 kernel, else batched)
+// waves of a persistent grouped launch at batch size M
 int64_t grouped_wave_slots(int M);
-int64_t b4_wave_slots(int M);
 
 }  // namespace ql

@@ -67,7 +67,7 @@ ql_status qlinear_gemv_grouped_noalloc(const ql_gemv_desc* descs, int32_t count,
   uint32_t* state = nullptr;
   const ql_status st = state_on_device(stream, &state);
   if (st != QL_OK) return st;
-  const hipError_t e = ql::launch_grouped_for(descs, count, total_tasks, M, state, stream);
+  const hipError_t e = ql::launch_gemv_grouped(descs, count, total_tasks, M, state, stream);
   if (e != hipSuccess) return ql::set_error(QL_EHIP, "grouped gemv launch: %s", hipGetErrorString(e));
   return QL_OK;
 }

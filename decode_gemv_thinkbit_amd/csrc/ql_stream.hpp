@@ -1,7 +1,8 @@
-// Streaming helpers shared by the batch-1 GEMV kernels (gfx950): 128-bit
-// buffer loads of slab chunks, scalar buffer loads of activations, LDS table
-// reads, v_dot2_f32_bf16, compile-time loops and zero-instruction step
-// boundaries for the software pipelines.
+// Streaming helpers shared by the decode kernels (gfx950): 128-bit buffer
+// loads of slab chunks, scalar buffer loads of activations, LDS table reads,
+// v_dot2_f32_bf16, compile-time loops, zero-instruction step boundaries for the
+// software pipelines, and the grouped launches' task location, split-K and
+// task queues.
 #pragma once
 
 #include <utility>
@@ -136,8 +137,6 @@ __device__ __forceinline__ uint32_t word_of(const uint4& d, int w) {
 }
 
 __device__ i32x4_t ql_sbuf_load_x4(i32x4_t rsrc, int offset, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v4i32");
-typedef int i32x16_t __attribute__((ext_vector_type(16)));
-__device__ i32x16_t ql_sbuf_load_x16(i32x4_t rsrc, int offset, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v16i32");
 
 // Buffer resource over n_bytes of uniform memory at p (raw, stride 0).
 __device__ __forceinline__ i32x4_t scalar_rsrc(const void* p, uint32_t n_bytes) {

@@ -495,7 +495,7 @@ def _xy(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor]):
 
 
 def gemv(x: torch.Tensor, pw: PackedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y [M, N] fp32 = x [M, K] bf16 times the packed weight transposed, M <= 8."""
+    """y [M, N] fp32 = x [M, K] bf16 times the packed weight transposed, M <= 16."""
     x, M, out = _xy(x, pw, out)
     _check(lib().qlinear_gemv(M, pw.N, pw.K, pw.grid, _ptr(pw.blk_grid), _ptr(pw.blk_off), _ptr(pw.packed),
                               _ptr(pw.pscales), _ptr(x), _ptr(out), _stream()), "gemv")

@@ -153,12 +153,13 @@ ql_status qlinear_validate_packed(int64_t N, int64_t K, int grid, const int8_t *
 
 /* ---------------------------------------------------------------- products (device) */
 
-/* Decode-time GEMV, 1 <= M <= 8 (the per-token weight stream that the summary page,
- * section "What it is", names as the bandwidth-bound step of decoding):
- * y[m][n] = sum_k c[n][k] * s[n][k/128] * x[m][k].  At M = 1 codes are read at 1.6/2/3
- * bits with 128-bit loads and decoded in registers; products c*x are exact in fp32 and
- * are summed in fp32, each scale applied once per group.  2 <= M <= 8 is a multi-token
- * contraction and runs on the MFMA path of qlinear_gemm (same numerics contract).
+/* Decode-time GEMV of one matrix, 1 <= M <= 16 (the per-token weight stream that the
+ * summary page, section "What it is", names as the bandwidth-bound step of decoding):
+ * y[m][n] = sum_k c[n][k] * s[n][k/128] * x[m][k].  Codes are read at 1.6/2/3 bits with
+ * 128-bit loads, one lane per weight row, and decoded once for all M tokens through LDS
+ * tables into bf16; the products c*x are exact and run on MFMA with fp32 sums, each
+ * scale applied once per 128-input group.  K must be at most 2^26.  The kernel is the
+ * grouped launch's (qlinear_gemv_grouped) without its task queues or split-K.
  *   x (dev) bf16 bits [M][K]; y (dev) fp32 [M][N]. */
 ql_status qlinear_gemv(int64_t M, int64_t N, int64_t K, int grid, const int8_t *blk_grid,
                        const int64_t *blk_off, const void *packed, const uint16_t *pscales,
@@ -224,12 +225,11 @@ int64_t qlinear_grouped_wave_slots(int32_t M);
 
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
  * descs (dev), count entries) in one persistent launch, at one batch size M for all entries
- * (1 <= M <= 16; each x is M x K, each y M x N).  M = 1 runs the batch-1 kernel (v_dot2);
- * 2 <= M <= 16 the batched-decode kernel: the batch-1 mapping (lane = weight row), with the
- * products on 4x4x4 MFMA and the activations of four tokens at a time broadcast to every
- * row block.  It decodes each packed byte once for all M tokens (products exact, fp32 sums;
- * summary page, section "What it is": a decode step at a small batch still streams every
- * weight once).  M outside 1..16 returns QL_EINVAL.  Waves take tasks (64-row slabs, or parts of them after prepare_split) from
+ * (1 <= M <= 16; each x is M x K, each y M x N).  Every M runs one kernel: lane =
+ * weight row (as in qlinear_gemv's batch-1 kernel), products on 4x4x4 MFMA with the
+ * activations of four tokens at a time broadcast to every row block.  It decodes each
+ * packed byte once for all M tokens (products exact, fp32 sums; summary page, section
+ * "What it is": a decode step at a small batch still streams every weight once).  M outside 1..16 returns QL_EINVAL.  Waves take tasks (64-row slabs, or parts of them after prepare_split) from
  * atomic queue counters in the state buffer `sched` (dev, 16-byte aligned, owned by the
  * caller; QL_SCHED_WORDS uint32 after qlinear_grouped_prepare, the state_words reported by
  * qlinear_grouped_prepare_split otherwise): its counters must be all zero when a launch

@@ -60,7 +60,7 @@ def test_gemv_argument_errors():
     args = lambda M, N, K, grid, p=FAKE: (M, N, K, grid, None, None, p, FAKE, FAKE, FAKE, None)
     rc, msg = status_and_msg(L.qlinear_gemv(*args(0, 64, 128, 0)))
     assert rc == 1 and "M" in msg
-    rc, msg = status_and_msg(L.qlinear_gemv(*args(9, 64, 128, 0)))
+    rc, msg = status_and_msg(L.qlinear_gemv(*args(17, 64, 128, 0)))
     assert rc == 1
     rc, msg = status_and_msg(L.qlinear_gemv(*args(1, 64, 100, 0)))
     assert rc == 1 and "multiple of 128" in msg

@@ -15,7 +15,7 @@ Paths:
   * the grouped batch-1 launch (gemv_grouped_kernel<1>), every item a
     different position against the same weight, with and without split-K;
   * the grouped batched-decode launch at M = 4 and 16
-    (gemv_b4_grouped_kernel, one and four token groups), token t of an item
+    (gemv_grouped_kernel, one and four token groups), token t of an item
     holding its own position.
 """
 import sys

@@ -102,7 +102,7 @@ def _gemv_case(ora, dev, N, K, grid, M, seed):
 
 @pytest.mark.parametrize("N,K", SHAPES)
 @pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
-@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
 def test_gemv_parity(ora, dev, N, K, grid, M):
     note(f"gemv N={N} K={K} grid={grid} M={M}")
     pw, x, y64, _, _ = _gemv_case(ora, dev, N, K, grid, M, seed=N * 31 + K + M)
