@@ -447,7 +447,7 @@ __device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs
     for (int i = 0; i < NT; ++i)
       if (i < M) st.put(sl, 64 * i + lane, y[i]);
     if (!st.arrive(st.counter(d, state), lane)) return;
-    st.totals<NT, 4>(sl, y, lane);
+    st.totals<NT, (NT == 4 ? 8 : 4)>(sl, y, lane);  // 8 parts per load round at batch <= 4
   }
   const int64_t row = (int64_t)st.slab * kSlab + lane;
   if (row < d.N)
