@@ -721,7 +721,7 @@ def gemm_leg(dev, Ms=(64, 256, 512), reps=10):
                     "stored_bytes": sum(pw.nbytes for _, pw in mats)})
         log(f"gemm M={M}: {us:.1f} us per 8B layer, {tf:.1f} TFLOP/s ({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA)")
     return {"workload": "qwen3_8b_layer mixed grids", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-            "kernels": "gemm_kernel (+ gemm_reduce_kernel when K is split)", "points": out}
+            "kernels": "gemm2_kernel (M >= 16; gemm_kernel below) + gemm_reduce_kernel when K is split", "points": out}
 
 
 def main():
