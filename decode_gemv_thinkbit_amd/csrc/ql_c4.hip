@@ -140,7 +140,8 @@ __device__ __forceinline__ void c4_task(const ql_gemv_desc* __restrict__ descs, 
   const uint8_t* codes = static_cast<const uint8_t*>(d.packed) + slab * (int64_t)kSlab * (K / 2);
   const float y = c4_slab(codes, d.pscales + slab * (int64_t)G8 * kSlab * 8, d.x, K, lane, lut);
   const int64_t row = slab * kSlab + lane;
-  if (row < d.N) d.y[row] = y;
+  // a global store (a flat one would also hold up the next task's lgkmcnt waits)
+  if (row < d.N) ((__attribute__((address_space(1))) float*)d.y)[row] = y;
 }
 
 __global__ void __launch_bounds__(kC4Waves * 64, 4) c4_gemv_kernel(ql_gemv_desc desc, int count, int64_t total) {

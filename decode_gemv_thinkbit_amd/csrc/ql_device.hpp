@@ -57,9 +57,12 @@ __host__ __device__ inline int c4_code_at(const uint8_t* c4, int64_t K, int64_t 
 __device__ inline int64_t slab_offset(int64_t s, int64_t K, int grid, const int8_t* blk_grid,
                                       const int64_t* blk_off, int* grid_out) {
   if (grid == QL_GRID_MIXED) {
-    const int g = blk_grid[s >> 1];
+    // global-address-space reads: flat ones would also count against lgkmcnt, which the
+    // decode loops wait on for their LDS reads
+    const int g = ((const __attribute__((address_space(1))) int8_t*)blk_grid)[s >> 1];
     *grid_out = g;
-    return blk_off[s >> 1] + (s & 1) * (int64_t)kSlab * row_bytes(g, K);
+    return ((const __attribute__((address_space(1))) int64_t*)blk_off)[s >> 1] +
+           (s & 1) * (int64_t)kSlab * row_bytes(g, K);
   }
   *grid_out = grid;
   return s * (int64_t)kSlab * row_bytes(grid, K);

@@ -418,12 +418,16 @@ __device__ void run_i3(const Ctx<TG>& c, int g0, int g1, float (&y)[4 * TG]) {
 // ---------------------------------------------------------------- task, kernel
 // One wave task: one 64-row slab of one descriptor, all tokens, or one part of
 // its input when the entry is split (partial sums meet in the state buffer).
-template <int TG>
+// `done` runs once the sums are complete and before anything is stored: the
+// grouped launch reads its next task's draw there, so that wait (which covers
+// every vector memory operation in flight) does not also wait for this task's
+// stores to reach memory.
+template <int TG, class Done>
 __device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs, const TaskLoc& loc, int64_t t, int M,
-                                        const uint8_t* lut, int lane, uint32_t* state) {
+                                          const uint8_t* lut, int lane, uint32_t* state, Done&& done) {
   constexpr int NT = 4 * TG;
   const ql_gemv_desc& d = descs[loc.di];
-  if (!task_in_entry(d, t)) return;
+  if (!task_in_entry(d, t)) return done();
   const SplitTask st(d, t);
   const int K = d.K, G = K / kGroup, G8 = (G + 7) / 8;
   float y[NT];
@@ -441,19 +445,21 @@ __device__ __forceinline__ void gemv_task(const ql_gemv_desc* __restrict__ descs
     else
       run_i3<TG>(c, g0, g1, y);
   }
+  done();
   if (st.split()) {
     float* sl = st.slots(d, state);
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
-      if (i < M) st.put(sl, 64 * i + lane, y[i]);
+    for (int i = 0; i < NT; ++i) st.put(sl, 64 * i + lane, y[i]);  // all slots, straight-line before the wait
     if (!st.arrive(st.counter(d, state), lane)) return;
     st.totals<NT, (NT == 4 ? 8 : 4)>(sl, y, lane);  // 8 parts per load round at batch <= 4
   }
   const int64_t row = (int64_t)st.slab * kSlab + lane;
+  // a global store (a flat one would also hold up the next task's lgkmcnt waits)
+  typedef __attribute__((address_space(1))) float* gf32p;
   if (row < d.N)
 #pragma unroll
     for (int i = 0; i < NT; ++i)
-      if (i < M) d.y[(int64_t)i * d.N + row] = y[i];
+      if (i < M) ((gf32p)d.y)[(int64_t)i * d.N + row] = y[i];
 }
 
 // A single matrix: all slabs cost the same, so waves stride over them (no task
@@ -470,7 +476,7 @@ __global__ void __launch_bounds__(gemv_waves(TG) * 64, gemv_waves_per_eu(TG)) ge
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t < total; t += (int64_t)gridDim.x * kWaves)
-    gemv_task<TG>(&desc, locate_task(&desc, count, t), t, M, lut, lane, nullptr);
+    gemv_task<TG>(&desc, locate_task(&desc, count, t), t, M, lut, lane, nullptr, [] {});
 }
 
 // Many independent matrices in one persistent launch.  Slab costs differ (row
@@ -500,8 +506,10 @@ __global__ void __launch_bounds__(gemv_waves(TG) * 64, gemv_waves_per_eu(TG)) ge
   }
   while (t >= 0) {
     const uint32_t claim = tq.claim(lane);
-    gemv_task<TG>(descs, loc, t, M, lut, lane, sched);
-    t = tq.resolve(claim, lane);
+    int64_t tn = -1;
+    gemv_task<TG>(descs, loc, t, M, lut, lane, sched, [&]() __attribute__((always_inline)) { tn = tq.drawn(claim); });
+    if (tn < 0) tn = tq.next(lane);  // the home queue was dry: scan the others
+    t = tn;
     if (t >= 0) loc = locate_task(descs, count, t);
   }
   tq.checkout(lane);

@@ -341,11 +341,15 @@ struct TaskQueues {
       t = __hip_atomic_fetch_add(sched + home * kQueueStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return t;
   }
+  // the task a claim drew, or -1 if its queue was dry (then next() finds one)
+  __device__ int64_t drawn(uint32_t claimed) const {
+    const uint32_t t = __builtin_amdgcn_readfirstlane(claimed);
+    return t < qcount(home) ? nwaves + home + (int64_t)t * kQueues : -1;
+  }
   // the task a claim drew, or the next one found by next() if it drew nothing
   __device__ int64_t resolve(uint32_t claimed, int lane) {
-    const uint32_t t = __builtin_amdgcn_readfirstlane(claimed);
-    if (t < qcount(home)) return nwaves + home + (int64_t)t * kQueues;
-    return next(lane);
+    const int64_t t = drawn(claimed);
+    return t >= 0 ? t : next(lane);
   }
   // Every wave checks out once, after its last draw; the last one zeroes the
   // state for the next launch.  Check-out is two-level so that no address takes
