@@ -151,8 +151,8 @@ def time_grouped(grp, warmup, steps):
 
 
 def batched_leg(dev, warmup, steps, workloads=("qwen3_14b_stack", "qwen3_8b_pass"), Ms=(4, 16)):
-    """Decode at a small batch: the same grouped weight pass at M = 4 and 16 tokens (the
-    batched-decode kernel: each packed byte decoded once, the M-token products on MFMA).
+    """Decode at a small batch: the same grouped weight pass at M = 4 and 16 tokens (each packed
+    byte decoded once, the M-token products on MFMA in token groups of four).
     Reported as stored-weight GB/s, the same numerator as the M = 1 headline, with the
     oracle on sampled rows."""
     import torch

@@ -216,7 +216,7 @@ int64_t qlinear_grouped_prepare_split(ql_gemv_desc* descs, int32_t count, int64_
       return fail(QL_EINVAL, "descriptor %d: a list must not mix 4-bit containers and native grids", i), -1;
     if (!containers && check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
     if (check_ptrs({d.packed, d.pscales, d.x, d.y}) != QL_OK) return -1;
-    // the batched kernels address all 16 tokens' activations through one 32-bit buffer range
+    // the GEMV kernel addresses up to 16 tokens' activations through one 32-bit buffer range
     if (d.K > kMaxGroupedK)
       return fail(QL_EINVAL, "descriptor %d: K=%d above the grouped launch's limit %lld", i, d.K,
                   (long long)kMaxGroupedK), -1;

@@ -8,9 +8,8 @@
 // onedev.kr/papers/1416, section "What it is"; w = c * s with one bf16 scale
 // per 128 inputs, section "How it works").
 //
-// Mapping.  As in the batch-1 kernel one wave owns a 64-row slab and lane r is
-// row r: it streams its row's code bytes and turns them into bf16 codes with
-// the same per-lane LDS tables.  The products run on
+// Mapping.  One wave owns a 64-row slab and lane r is row r: it streams its
+// row's code bytes and turns them into bf16 codes with per-lane LDS tables.  The products run on
 // v_mfma_f32_4x4x4_16b_bf16, whose 64 lanes form 16 blocks of four: lane
 // 4b + j supplies four inputs of weight row 4b + j (the second operand, so
 // lane = row holds) and receives the four token sums of that row.  The first

@@ -187,7 +187,7 @@ typedef struct {
  * the entries by task length (K / kparts; here kparts = 1, so by K), largest first (stable;
  * the products are independent, so their order is free), fill slab_begin and return the
  * total number of 64-row slabs (the task count), or -1 on a bad descriptor (K above 2^26
- * included: the batched kernels address 16 tokens' activations in one 32-bit range).  Longest-first task order plus dynamic task fetching keeps
+ * included: the GEMV kernel addresses 16 tokens' activations in one 32-bit range).  Longest-first task order plus dynamic task fetching keeps
  * the persistent launch balanced when row lengths differ (a K = 12288 row costs three
  * K = 4096 rows).  Entries of equal K keep the caller's order: listing them by stored
  * bytes per row, largest first (3-bit before 2-bit before ternary), ends the launch on
@@ -226,7 +226,7 @@ int64_t qlinear_grouped_wave_slots(int32_t M);
 /* Run every GEMV of a prepared descriptor list (copied to device memory by the caller,
  * descs (dev), count entries) in one persistent launch, at one batch size M for all entries
  * (1 <= M <= 16; each x is M x K, each y M x N).  Every M runs one kernel: lane =
- * weight row (as in qlinear_gemv's batch-1 kernel), products on 4x4x4 MFMA with the
+ * weight row (as in qlinear_gemv), products on 4x4x4 MFMA with the
  * activations of four tokens at a time broadcast to every row block.  It decodes each
  * packed byte once for all M tokens (products exact, fp32 sums; summary page, section
  * "What it is": a decode step at a small batch still streams every weight once).  M outside 1..16 returns QL_EINVAL.  Waves take tasks (64-row slabs, or parts of them after prepare_split) from

@@ -252,7 +252,7 @@ def test_read_probe_argument_errors():
 
 
 def test_grouped_prepare_rejects_rows_beyond_the_batched_range():
-    """The batched kernels address all tokens' activations in one 32-bit range: K above 2^26
+    """The GEMV kernel addresses all tokens' activations in one 32-bit range: K above 2^26
     is refused before any launch."""
     L = ql.lib()
     arr = _descs([(64, (1 << 26) + 128, 0)], [1])

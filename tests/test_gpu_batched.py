@@ -1,4 +1,4 @@
-"""GPU parity of the batched-decode kernel: grouped launches at 2 <= M <= 16 (needs gfx950).
+"""GPU parity of grouped launches at a decode batch, 2 <= M <= 16 (needs gfx950).
 
 The kernel decodes each packed byte once and runs the M-token products on the
 matrix cores; products of codes and bf16 activations are exact and sums are
@@ -82,8 +82,8 @@ def test_batched_grouped_parity(ora, dev, M):
 
 
 def test_batched_matches_batch1_rows(ora, dev):
-    """Each token row of a batched launch agrees with the batch-1 kernel on that row
-    (both within the bar of the exact result; they sum in different orders)."""
+    """Each token row of a batched launch agrees with a batch-1 launch of that row (both
+    within the bar of the exact result; their MFMA sums of the other token groups differ)."""
     note("batched vs batch-1 rows")
     N, K, M = 384, 4096, 6
     g = grid_arg(N, "mixed", 77)

@@ -92,9 +92,9 @@ def test_config1_qwen3_1p7b_layer_every_row(ora, dev):
 @pytest.mark.parametrize("M,path", [(1, "grouped"), (4, "grouped"), (16, "grouped"), (4, "mfma"), (16, "mfma")])
 def test_config3_qwen3_14b_layer_sampled(ora, dev, layer, M, path):
     """A Qwen3-14B layer at full size (down_proj K = 17408 included), mixed grids, 48 seeded rows
-    per matrix.  path "grouped": the grouped launch the benchmark times (batch-1 kernel at M = 1,
-    batched-decode kernel at M = 4 and 16; GEMV bar).  path "mfma": qlinear_gemv (M = 4) and
-    qlinear_gemm (M = 16) on the LDS-tile MFMA path (GEMM bar)."""
+    per matrix.  path "grouped": the grouped launch the benchmark times (the decode GEMV with one
+    and four token groups; GEMV bar).  path "mfma": qlinear_gemm, the small-batch LDS-tile kernel
+    at M = 4 and the large-tile kernel at M = 16 (GEMM bar)."""
     wl = configs.WORKLOADS["qwen3_14b_stack"]
     wi = wl_index(wl.name)
     alloc = synth.allocation(wl, layer)
@@ -111,8 +111,6 @@ def test_config3_qwen3_14b_layer_sampled(ora, dev, layer, M, path):
         items = [(pw, xs[lin.x_slot], torch.full((M, lin.N), float("nan"), device=dev)) for lin, _, pw in mats]
         ql.GroupedGemv(items).run()
         ys = [y for _, _, y in items]
-    elif M <= 8:
-        ys = [ql.gemv(xs[lin.x_slot], pw) for lin, _, pw in mats]
     else:
         ys = [ql.gemm(xs[lin.x_slot], pw) for lin, _, pw in mats]
     torch.cuda.synchronize()

@@ -92,7 +92,7 @@ GRIDS = [T, I2, I3, "mixed"]
 @pytest.mark.parametrize("N,K", SHAPES)
 @pytest.mark.parametrize("grid", GRIDS)
 def test_gemv_batch1_one_hot(ora, dev, N, K, grid):
-    """qlinear_gemv at M = 1 (the batch-1 kernel), one launch per position."""
+    """qlinear_gemv at M = 1 (the single-matrix form of the decode GEMV), one launch per position."""
     note(f"one-hot gemv M=1 N={N} K={K} grid={grid}")
     pw, w32 = weight_case(ora, dev, N, K, grid, seed=11 * N + K)
     ks = positions(K)
@@ -130,7 +130,7 @@ def test_grouped_batch1_one_hot(ora, dev, N, K, grid, split):
 @pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("M", [4, 16])
 def test_grouped_batched_one_hot(ora, dev, N, K, grid, M):
-    """The batched-decode kernel: token t of item i probes position ks[i*M + t]."""
+    """The grouped launch at M = 4 and 16: token t of item i probes position ks[i*M + t]."""
     note(f"one-hot batched M={M} N={N} K={K} grid={grid}")
     pw, w32 = weight_case(ora, dev, N, K, grid, seed=17 * N + K + M)
     ks = positions(K)

@@ -156,7 +156,7 @@ def check_gemm(ora, y, y64, c_ref, s_ref, x, M):
 
 @pytest.mark.parametrize("N,K", [(64, 128), (129, 1280), (1000, 4096), (70, 384), (256, 5120)])
 @pytest.mark.parametrize("grid", [T, I2, I3, "mixed"])
-@pytest.mark.parametrize("M", [1, 16, 17, 64, 100])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 17, 64, 100])
 def test_gemm_parity(ora, dev, N, K, grid, M):
     note(f"gemm N={N} K={K} grid={grid} M={M}")
     pw, x, y64, c_ref, s_ref = _gemv_case(ora, dev, N, K, grid, M, seed=N * 7 + K + M)
@@ -261,7 +261,7 @@ def test_workload_linear2048_i2(ora, dev):
 
 
 def test_grouped_gemv_batch_above_one_goes_to_batched_kernel(ora, dev):
-    """M = 4 in a grouped launch runs the batched-decode kernel and meets the GEMV bar."""
+    """M = 4 in a grouped launch (one token group of four) meets the GEMV bar."""
     pw, x, y64, _, _ = _gemv_case(ora, dev, 128, 640, T, 4, seed=9)
     y = torch.full((4, 128), float("nan"), device=dev)
     ql.GroupedGemv([(pw, x, y)]).run()

@@ -3,8 +3,8 @@
 Each slab's input is cut into parts of whole 640-input periods, each part a
 task; the wave that finishes a slab's last part sums the parts' fp32 partial
 sums in part order.  The bar is the GEMV's: max_n |dy| / ||y_row||_2 <= 2e-3
-against the oracle (fp64), normwise tripwire 1e-5, at batch 1 and on the
-batched-decode kernel.  Shapes cover one-period rows (no split possible),
+against the oracle (fp64), normwise tripwire 1e-5, at batch 1 and at batches of
+four and sixteen tokens.  Shapes cover one-period rows (no split possible),
 ternary tails inside a chunk or period, every grid and mixed blocks, parts that
 do not divide the periods, and as many parts as periods.  Repeat launches are
 bitwise identical and leave every counter at zero.
