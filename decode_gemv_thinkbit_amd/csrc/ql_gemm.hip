@@ -182,6 +182,76 @@ __device__ __forceinline__ void decode_i3_32(const u32x4g_t (&ch)[2], const uint
   put32(dst, o);
 }
 
+// Selector tables of the large-tile kernel: the layout of the code tables above
+// (ternary and 2-bit offsets identical, so decode_t32 / decode_i2_32 assemble
+// selector pairs exactly as they assemble code pairs), but each 16-bit half is a
+// v_perm byte selector that picks the bf16 value c * s of its code out of a
+// register pair built once per group:
+//   ternary, 2-bit: bytes 0-1 = s, 2-3 = -s, 4-5 = -2s (code 0 -> selector 0x0C, a zero byte);
+//   3-bit: bytes 0-1 = s, 2-3 = 2s, 4-5 = 3s, 6-7 = 4s picked by |c|, with a
+//   sign mask per code (entries 8 B: selector pair, sign pair).
+// Each value is RNE(c * s) in bf16, so one v_perm per pair (and one xor for
+// 3-bit) replaces the multiply and rounding of every pair.
+constexpr int kSelI3 = kLutI2 + 256 * 8;
+constexpr int kSelBytes = kSelI3 + 64 * 8;
+
+__device__ __forceinline__ uint32_t sel_tern(int c) { return c == 1 ? 0x0100u : (c == -1 ? 0x0302u : (c == -2 ? 0x0504u : 0x0C0Cu)); }
+__device__ __forceinline__ uint32_t sel_mag(int c) {
+  const int m = c < 0 ? -c : c;
+  return m == 0 ? 0x0C0Cu : (uint32_t)(((2 * m - 1) << 8) | (2 * m - 2));
+}
+
+__device__ void gemm2_build_luts(uint8_t* lut) {
+  for (int e = threadIdx.x; e < 2 * 243; e += blockDim.x) {
+    const int odd = e >= 243, b = odd ? e - 243 : e;
+    int d[5], v = b;
+    for (int i = 0; i < 5; ++i) {
+      d[i] = v % 3 - 1;
+      v /= 3;
+    }
+    int c[5];
+    for (int t = 0; t < 5; ++t) c[t] = odd ? (t == 0 ? d[4] : d[t - 1]) : d[t];
+    uint4 q;
+    q.x = sel_tern(c[0]) | (sel_tern(c[1]) << 16);
+    q.y = sel_tern(c[2]) | (sel_tern(c[3]) << 16);
+    q.z = sel_tern(c[4]);
+    q.w = 0;
+    *reinterpret_cast<uint4*>(lut + (odd ? kLutT1 : kLutT0) + b * 16) = q;
+  }
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) {
+    uint2 q;
+    q.x = sel_tern((b & 3) - 2) | (sel_tern(((b >> 2) & 3) - 2) << 16);
+    q.y = sel_tern(((b >> 4) & 3) - 2) | (sel_tern(((b >> 6) & 3) - 2) << 16);
+    *reinterpret_cast<uint2*>(lut + kLutI2 + b * 8) = q;
+  }
+  for (int e = threadIdx.x; e < 64; e += blockDim.x) {
+    const int c0 = (e & 7) - 4, c1 = (e >> 3) - 4;
+    uint2 q;
+    q.x = sel_mag(c0) | (sel_mag(c1) << 16);
+    q.y = (c0 < 0 ? 0x8000u : 0u) | (c1 < 0 ? 0x80000000u : 0u);
+    *reinterpret_cast<uint2*>(lut + kSelI3 + e * 8) = q;
+  }
+}
+
+// 3-bit through the selector table: magnitude selector pairs o and sign masks sg.
+__device__ __forceinline__ void decode_i3_32_sel(const u32x4g_t (&ch)[2], const uint8_t* lut, uint32_t (&o)[16],
+                                                 uint32_t (&sg)[16]) {
+  const uint32_t w0 = ch[0].x, w1 = ch[0].y, w2 = ch[0].z;
+  gfor<16>([&](auto pi) __attribute__((always_inline)) {
+    constexpr int P = decltype(pi)::value;
+    constexpr int bit = 6 * P;
+    uint32_t f;
+    if constexpr (bit + 6 <= 32) f = (w0 >> bit) & 63u;
+    else if constexpr (bit < 32) f = __builtin_amdgcn_alignbit(w1, w0, bit) & 63u;
+    else if constexpr (bit + 6 <= 64) f = (w1 >> (bit - 32)) & 63u;
+    else if constexpr (bit < 64) f = __builtin_amdgcn_alignbit(w2, w1, bit - 32) & 63u;
+    else f = (w2 >> (bit - 64)) & 63u;
+    const u32x2g_t e = *(lq2p)(lut + kSelI3 + f * 8);
+    o[P] = e.x;
+    sg[P] = e.y;
+  });
+}
+
 // Workgroup barrier that orders LDS only: the next group's global loads stay
 // in flight across it (a plain __syncthreads would wait for them).
 __device__ __forceinline__ void lds_barrier() {
@@ -405,10 +475,6 @@ constexpr int kG2Threads = 512;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// bf16 pair (c0, c1) times (s, s), each product rounded to nearest even
-__device__ __forceinline__ uint32_t scale_pair(uint32_t codes, uint32_t s2) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(bf16x2_t, codes) * __builtin_bit_cast(bf16x2_t, s2));
-}
 
 template <int TA>
 __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, int nsplit, float* __restrict__ part) {
@@ -416,8 +482,8 @@ __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, 
   constexpr int XQ = 8 / TA;          // threads per token row of a stage (16 * TA bytes each)
   __shared__ __attribute__((aligned(16))) uint16_t wt[2][kG2Rows * kG2Pad];
   __shared__ __attribute__((aligned(16))) uint16_t xt[2][MT * kG2Pad];
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  gemm_build_luts(lut);
+  __shared__ __attribute__((aligned(16))) uint8_t lut[kSelBytes];
+  gemm2_build_luts(lut);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, G8 = (K / kGroup + 7) / 8;
@@ -477,10 +543,13 @@ __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, 
     }
     st.sc = drow_ok ? (uint32_t)a.pscales[pscale_index(dn, k0 / kGroup, G8)] : 0u;
   };
-  // decode the loaded stage s (codes times scale, bf16) and its x tile into buffer b
+  // decode the loaded stage s (bf16 c * s) and its x tile into buffer b
   auto put = [&](int s, int b) __attribute__((always_inline)) {
     uint32_t o[16];
-    if (gr == QL_GRID_T) {
+    const float sf = bf16_bits_to_f32(st.sc);
+    if (gr == QL_GRID_T || gr == QL_GRID_I2) {
+      // pair selectors, then v_perm from (s, -s | -2s, 0)
+      if (gr == QL_GRID_T) {
       const int pos = (2 * ((kG2K * s) % kPeriodK) / kG2K) + dh;  // 32-input quarter within the period (0..19)
       switch (pos) {
 #define QL_T_CASE(i) \
@@ -493,14 +562,21 @@ __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, 
         default: decode_t32<32 * 19>(st.ch, lut, o); break;
 #undef QL_T_CASE
       }
-    } else if (gr == QL_GRID_I2) {
-      decode_i2_32(st.ch, lut, o);
-    } else {
-      decode_i3_32(st.ch, lut, o);
-    }
-    const uint32_t s2 = st.sc | (st.sc << 16);
+      } else {
+        decode_i2_32(st.ch, lut, o);
+      }
+      const uint32_t lo = st.sc | ((st.sc ^ 0x8000u) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(2.0f * sf) ^ 0x8000u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] = scale_pair(o[i], s2);
+      for (int i = 0; i < 16; ++i) o[i] = __builtin_amdgcn_perm(hi, lo, o[i]);
+    } else {
+      uint32_t sg[16];
+      decode_i3_32_sel(st.ch, lut, o, sg);
+      const uint32_t lo = st.sc | ((uint32_t)f32_to_bf16_bits(2.0f * sf) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(3.0f * sf) | ((uint32_t)f32_to_bf16_bits(4.0f * sf) << 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] = __builtin_amdgcn_perm(hi, lo, o[i]) ^ sg[i];
+    }
     uint16_t* dst = wt[b] + dr * kG2Pad + 32 * dh;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
