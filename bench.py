@@ -703,25 +703,51 @@ def gemm_leg(dev, Ms=(64, 256, 512), reps=10):
             for (lin, pw), y in zip(mats, ys):
                 ql.gemm(xs[lin.K], pw, out=y, workspace=ws)
 
-        for _ in range(3):
-            layer()
-        torch.cuda.synchronize()
-        st = torch.cuda.current_stream()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(st)
-        for _ in range(reps):
-            layer()
-        e.record(st)
-        torch.cuda.synchronize()
-        us = s.elapsed_time(e) * 1e3 / reps
+        # the layer's matrices in grouped launches: all seven in one (independent products, as
+        # the decode pass's headline launch), and per dependency group (qkv, o, gate_up, down)
+        items = [(pw, xs[lin.K], y) for (lin, pw), y in zip(mats, ys)]
+        one = ql.GroupedGemm(items)
+        names = [lin.name for lin, _ in mats]
+        groups = [ql.GroupedGemm([items[names.index(n)] for n in grp])
+                  for grp in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))]
+
+        def grouped():
+            one.run()
+
+        def grouped_layered():
+            for g in groups:
+                g.run()
+
         flops = 2 * M * sum(lin.N * lin.K for lin, _ in mats)
+        st = torch.cuda.current_stream()
+        res = {}
+        for name, fn in (("per_matrix", layer), ("grouped", grouped), ("grouped_layered", grouped_layered)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(st)
+            for _ in range(reps):
+                fn()
+            e.record(st)
+            torch.cuda.synchronize()
+            res[name] = s.elapsed_time(e) * 1e3 / reps
+        us = res["per_matrix"]
         tf = flops / (us * 1e-6) / 1e12
-        out.append({"M": M, "us_per_layer": round(us, 2), "tflops": round(tf, 1),
-                    "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "stored_bytes": sum(pw.nbytes for _, pw in mats)})
-        log(f"gemm M={M}: {us:.1f} us per 8B layer, {tf:.1f} TFLOP/s ({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA)")
+        pt = {"M": M, "us_per_layer": round(us, 2), "tflops": round(tf, 1),
+              "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "stored_bytes": sum(pw.nbytes for _, pw in mats)}
+        for name in ("grouped", "grouped_layered"):
+            tfg = flops / (res[name] * 1e-6) / 1e12
+            pt[name] = {"us_per_layer": round(res[name], 2), "tflops": round(tfg, 1),
+                        "mfma_util": round(tfg / MFMA_BF16_PEAK_TFLOPS, 4)}
+        pt["grouped"]["splits"] = [[p["N"], p["K"], p["splits"]] for p in one.plan]
+        out.append(pt)
+        log(f"gemm M={M}: {us:.1f} us per 8B layer ({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}% MFMA) per matrix; "
+            f"grouped {res['grouped']:.1f} us, grouped per dependency group {res['grouped_layered']:.1f} us")
+        del one, groups
     return {"workload": "qwen3_8b_layer mixed grids", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-            "kernels": "gemm2_kernel (M >= 16; gemm_kernel below) + gemm_reduce_kernel when K is split", "points": out}
+            "kernels": "gemm2_kernel (M >= 16; gemm_kernel below) + gemm_reduce_kernel when K is split; "
+                       "grouped: gemm2_grouped_kernel + gemm_reduce_grouped_kernel", "points": out}
 
 
 def main():

@@ -433,6 +433,40 @@ ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t* 
   return hip_status(ql::launch_gemm(a, (int)M, workspace, workspace_bytes, stream), "gemm launch");
 }
 
+int64_t qlinear_gemm_grouped_prepare(ql_gemv_desc* descs, int32_t count, int64_t M, int64_t* workspace_bytes) {
+  if (!descs || count <= 0 || count > 65535) return fail(QL_EINVAL, "grouped gemm needs 1..65535 descriptors"), -1;
+  if (M < 16 || M >= ((int64_t)1 << 24))
+    return fail(QL_EINVAL, "grouped gemm needs 16 <= M < 2^24 (M=%lld)", (long long)M), -1;
+  int64_t tasks = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const ql_gemv_desc& d = descs[i];
+    if (check_shape(d.N, d.K) != QL_OK) return -1;
+    if (d.grid == QL_GRID_C4) return fail(QL_EINVAL, "descriptor %d: the grouped gemm takes native grids", i), -1;
+    if (check_grid(d.grid, d.blk_grid, d.blk_off, true) != QL_OK) return -1;
+    if (check_ptrs({d.packed, d.pscales, d.x, d.y}) != QL_OK) return -1;
+    tasks += ((d.N + 255) / 256) * ((M + 63) / 64) * 16;
+    if (tasks >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "too many tasks"), -1;
+  }
+  int64_t ws = 0;
+  const int64_t total = ql::gemm_grouped_plan(descs, count, M, &ws);
+  if (workspace_bytes) *workspace_bytes = ws * (int64_t)sizeof(float);
+  return total;
+}
+
+ql_status qlinear_gemm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total_tasks, int64_t M,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!descs || count <= 0 || count > 65535) return fail(QL_EINVAL, "grouped gemm needs 1..65535 descriptors");
+  if (M < 16 || M >= ((int64_t)1 << 24))
+    return fail(QL_EINVAL, "grouped gemm needs 16 <= M < 2^24 (M=%lld)", (long long)M);
+  if (total_tasks <= 0 || total_tasks >= ((int64_t)1 << 31)) return fail(QL_EINVAL, "bad task count");
+  if (workspace_bytes && !workspace) return fail(QL_EINVAL, "workspace_bytes without a workspace");
+  if (workspace) QL_TRY(check_ptrs({workspace}));
+  QL_TRY(check_ptrs({descs}));
+  return hip_status(ql::launch_gemm_grouped(descs, count, total_tasks, (int)M, static_cast<float*>(workspace),
+                                            (int64_t)(workspace_bytes / sizeof(float)), stream),
+                    "grouped gemm launch");
+}
+
 ql_status qlinear_read_probe(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream) {
   if (bytes <= 0 || bytes % 1024 || bytes >= ((int64_t)1 << 32))
     return fail(QL_EINVAL, "read probe needs 0 < bytes < 2^32, a multiple of 1024 (bytes=%lld)", (long long)bytes);

@@ -15,7 +15,10 @@
 // Matrices with few row blocks split K across workgroups; the partial sums go
 // to the caller's workspace and a second kernel adds them in a fixed order, so
 // results stay bitwise deterministic.
+#include <algorithm>
+#include <numeric>
 #include <utility>
+#include <vector>
 
 #include "ql_internal.hpp"
 
@@ -476,21 +479,33 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 
+// LDS of one large-tile workgroup: double-buffered weight and activation stages
+// and the selector tables.
 template <int TA>
-__global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, int nsplit, float* __restrict__ part) {
+struct G2Smem {
+  uint16_t wt[2][kG2Rows * kG2Pad];
+  uint16_t xt[2][64 * TA * kG2Pad];
+  uint8_t lut[kSelBytes];
+};
+
+// One tile: weight rows [256 bx, +256) x tokens [64 TA by, +64 TA) over stages of
+// split z of nsplit (partial sums to part + z M N when nsplit > 1, else y).  The
+// tables in sm.lut are built; the first barrier also separates this tile's LDS
+// writes from the previous tile's last reads in a persistent launch.
+template <int TA>
+__device__ __forceinline__ void gemm2_tile(const MatArgs& a, int M, int nsplit, float* __restrict__ part, int bx,
+                                           int by, int z, G2Smem<TA>& sm) {
   constexpr int MT = 64 * TA;         // tokens per workgroup
   constexpr int XQ = 8 / TA;          // threads per token row of a stage (16 * TA bytes each)
-  __shared__ __attribute__((aligned(16))) uint16_t wt[2][kG2Rows * kG2Pad];
-  __shared__ __attribute__((aligned(16))) uint16_t xt[2][MT * kG2Pad];
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kSelBytes];
-  gemm2_build_luts(lut);
+  auto& wt = sm.wt;
+  auto& xt = sm.xt;
+  const uint8_t* lut = sm.lut;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, G8 = (K / kGroup + 7) / 8;
   const int S = K / kG2K;  // stages of the row
-  const int64_t n0 = (int64_t)blockIdx.x * kG2Rows;
-  const int m0 = blockIdx.y * MT;
-  const int z = blockIdx.z;
+  const int64_t n0 = (int64_t)bx * kG2Rows;
+  const int m0 = by * MT;
   const int s_lo = (int)((int64_t)S * z / nsplit), s_hi = (int)((int64_t)S * (z + 1) / nsplit);
   const int64_t nslabs = ((int64_t)a.N + kSlab - 1) / kSlab;
 
@@ -520,33 +535,35 @@ __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, 
     uint32_t sc;
   } st;
   auto load = [&](int s) __attribute__((always_inline)) {
+    Regs& r = st;
 #pragma unroll
     for (int q = 0; q < TA; ++q) {
-      st.xv[q] = u32x4g_t{0u, 0u, 0u, 0u};
-      if (x_ok) st.xv[q] = *(gq4p)(xrow + (int64_t)s * kG2K + 8 * q);
+      r.xv[q] = u32x4g_t{0u, 0u, 0u, 0u};
+      if (x_ok) r.xv[q] = *(gq4p)(xrow + (int64_t)s * kG2K + 8 * q);
     }
     const int k0 = kG2K * s + 32 * dh;  // first input of this thread's 32
     if (gr == QL_GRID_T) {
       const int64_t p = k0 / kPeriodK;
       const int kp = k0 - (int)p * kPeriodK;
-      st.ch[0] = row_chunk(dslab, dslab_r, 8 * p + (kp / 5) / 16);
-      st.ch[1] = row_chunk(dslab, dslab_r, 8 * p + ((kp + 31) / 5) / 16);
+      r.ch[0] = row_chunk(dslab, dslab_r, 8 * p + (kp / 5) / 16);
+      r.ch[1] = row_chunk(dslab, dslab_r, 8 * p + ((kp + 31) / 5) / 16);
     } else if (gr == QL_GRID_I2) {
       const u32x2g_t v = row_dword2(dslab, dslab_r, k0 / 4);
-      st.ch[0] = u32x4g_t{v.x, v.y, 0u, 0u};
-      st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
+      r.ch[0] = u32x4g_t{v.x, v.y, 0u, 0u};
+      r.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
     } else {
       const int64_t b0 = 3 * (int64_t)k0 / 8;
-      st.ch[0] = u32x4g_t{row_dword(dslab, dslab_r, b0), row_dword(dslab, dslab_r, b0 + 4),
+      r.ch[0] = u32x4g_t{row_dword(dslab, dslab_r, b0), row_dword(dslab, dslab_r, b0 + 4),
                           row_dword(dslab, dslab_r, b0 + 8), 0u};
-      st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
+      r.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
     }
-    st.sc = drow_ok ? (uint32_t)a.pscales[pscale_index(dn, k0 / kGroup, G8)] : 0u;
+    r.sc = drow_ok ? (uint32_t)a.pscales[pscale_index(dn, k0 / kGroup, G8)] : 0u;
   };
   // decode the loaded stage s (bf16 c * s) and its x tile into buffer b
   auto put = [&](int s, int b) __attribute__((always_inline)) {
+    const Regs& r = st;
     uint32_t o[16];
-    const float sf = bf16_bits_to_f32(st.sc);
+    const float sf = bf16_bits_to_f32(r.sc);
     if (gr == QL_GRID_T || gr == QL_GRID_I2) {
       // pair selectors, then v_perm from (s, -s | -2s, 0)
       if (gr == QL_GRID_T) {
@@ -554,25 +571,25 @@ __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, 
       switch (pos) {
 #define QL_T_CASE(i) \
   case i:            \
-    decode_t32<32 * i>(st.ch, lut, o); \
+    decode_t32<32 * i>(r.ch, lut, o); \
     break;
         QL_T_CASE(0) QL_T_CASE(1) QL_T_CASE(2) QL_T_CASE(3) QL_T_CASE(4) QL_T_CASE(5) QL_T_CASE(6)
         QL_T_CASE(7) QL_T_CASE(8) QL_T_CASE(9) QL_T_CASE(10) QL_T_CASE(11) QL_T_CASE(12) QL_T_CASE(13)
         QL_T_CASE(14) QL_T_CASE(15) QL_T_CASE(16) QL_T_CASE(17) QL_T_CASE(18)
-        default: decode_t32<32 * 19>(st.ch, lut, o); break;
+        default: decode_t32<32 * 19>(r.ch, lut, o); break;
 #undef QL_T_CASE
       }
       } else {
-        decode_i2_32(st.ch, lut, o);
+        decode_i2_32(r.ch, lut, o);
       }
-      const uint32_t lo = st.sc | ((st.sc ^ 0x8000u) << 16);
+      const uint32_t lo = r.sc | ((r.sc ^ 0x8000u) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_bits(2.0f * sf) ^ 0x8000u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[i] = __builtin_amdgcn_perm(hi, lo, o[i]);
     } else {
       uint32_t sg[16];
-      decode_i3_32_sel(st.ch, lut, o, sg);
-      const uint32_t lo = st.sc | ((uint32_t)f32_to_bf16_bits(2.0f * sf) << 16);
+      decode_i3_32_sel(r.ch, lut, o, sg);
+      const uint32_t lo = r.sc | ((uint32_t)f32_to_bf16_bits(2.0f * sf) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_bits(3.0f * sf) | ((uint32_t)f32_to_bf16_bits(4.0f * sf) << 16);
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[i] = __builtin_amdgcn_perm(hi, lo, o[i]) ^ sg[i];
@@ -583,7 +600,7 @@ __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, 
       *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     uint16_t* xd = xt[b] + xr * kG2Pad + 8 * TA * xp;
 #pragma unroll
-    for (int q = 0; q < TA; ++q) *reinterpret_cast<u32x4g_t*>(xd + 8 * q) = st.xv[q];
+    for (int q = 0; q < TA; ++q) *reinterpret_cast<u32x4g_t*>(xd + 8 * q) = r.xv[q];
   };
 
   // MFMA mapping: wave (th, rq) computes tokens [32 TA th, +32 TA) x rows [64 rq, +64)
@@ -650,6 +667,63 @@ __global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, 
         if (t < M) out[(int64_t)t * a.N + n] = acc[ta][rb][r];
       }
     }
+}
+
+template <int TA>
+__global__ void __launch_bounds__(kG2Threads, 2) gemm2_kernel(MatArgs a, int M, int nsplit, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) G2Smem<TA> sm;
+  gemm2_build_luts(sm.lut);
+  gemm2_tile<TA>(a, M, nsplit, part, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+}
+
+// Many matrices at one M in one persistent launch: task t (tasks numbered by the
+// host in descriptor order, longest tasks first) runs on workgroup t mod grid.
+// Entry d's tasks are its row tiles x token tiles x d.kparts K splits, from task
+// d.slab_begin on; a split entry's partial sums go to ws + d.ws_begin.  Entries
+// whose partials would not fit ws_floats (a workspace smaller than prepare asked
+// for, or another M) run nothing.
+template <int TA>
+__global__ void __launch_bounds__(kG2Threads, 2) gemm2_grouped_kernel(const ql_gemv_desc* __restrict__ descs,
+                                                                     int count, int64_t total, int M,
+                                                                     float* __restrict__ ws, int64_t ws_floats) {
+  __shared__ __attribute__((aligned(16))) G2Smem<TA> sm;
+  gemm2_build_luts(sm.lut);
+  constexpr int MT = 64 * TA;
+  const int64_t mt = (M + MT - 1) / MT;
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    int lo = 0, hi = count - 1;  // the last entry whose first task is at or before t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (descs[mid].slab_begin <= t) lo = mid; else hi = mid - 1;
+    }
+    const ql_gemv_desc& d = descs[lo];
+    const int64_t rt = ((int64_t)d.N + kG2Rows - 1) / kG2Rows;
+    const int s = d.kparts > 1 ? d.kparts : 1;
+    const int64_t local = t - d.slab_begin;
+    if (local >= rt * mt * s) continue;  // past the entry's own tasks (a larger total than prepare's)
+    if (s > 1 && d.ws_begin + (int64_t)s * M * d.N > ws_floats) continue;
+    const MatArgs a{static_cast<const uint8_t*>(d.packed), d.pscales, d.blk_grid, d.blk_off, d.x, d.y, d.N, d.K,
+                    d.grid};
+    gemm2_tile<TA>(a, M, s, s > 1 ? ws + d.ws_begin : nullptr, (int)(local / s / mt), (int)(local / s % mt),
+                   (int)(local % s), sm);
+  }
+}
+
+// y = sum over splits of the partials, in split order, for every split entry of a
+// grouped launch (blockIdx.y = entry).
+__global__ void __launch_bounds__(256) gemm_reduce_grouped_kernel(const ql_gemv_desc* __restrict__ descs, int M,
+                                                                  const float* __restrict__ ws, int64_t ws_floats) {
+  const ql_gemv_desc& d = descs[blockIdx.y];
+  const int s = d.kparts;
+  if (s <= 1) return;
+  const int64_t n = (int64_t)M * d.N;
+  if (d.ws_begin + s * n > ws_floats) return;
+  const float* part = ws + d.ws_begin;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float v = part[i];
+    for (int z = 1; z < s; ++z) v += part[(int64_t)z * n + i];
+    d.y[i] = v;
+  }
 }
 
 // y = sum over splits of the partials, in split order.
@@ -752,6 +826,162 @@ hipError_t launch_gemm_as(const MatArgs& a, int M, void* workspace, size_t ws_by
     const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     hipLaunchKernelGGL(gemm_reduce_kernel, dim3(blocks), dim3(256), 0, stream, part, a.y, n, s);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- grouped plan
+// Split counts of a grouped large-tile launch.  Workgroups (one per CU) take tasks
+// round-robin in descriptor order, longest first; the plan simulates that order
+// with a cost per task of its stages (measured per-stage times of this kernel at
+// 64 / 128 / 256 tokens per tile) plus a fixed part and, for split entries, the
+// partial tile it writes, and adds the reduction pass (every split entry's
+// partials read once, y written once).  It first tries every common task length
+// L (each entry split into the fewest parts of at most L stages) and every pair
+// of lengths over subsets of the entries, keeps the cheapest, then moves, one
+// entry at a time, the split (up or down) that lowers the estimate most, until no
+// move does.
+namespace {
+double g2_stage_us(int ta) { return ta == 1 ? 1.7 : (ta == 2 ? 2.0 : 2.6); }
+
+struct PlanEntry {
+  int64_t tiles, stages, mn;
+  int splits;
+  double task_us(int ta) const {
+    const double st = (double)((stages + splits - 1) / splits);
+    const double part = splits > 1 ? 256.0 * 64.0 * ta * 4.0 / 60.0e3 : 0.0;  // partial tile at ~60 GB/s per CU
+    return st * g2_stage_us(ta) + 3.0 + part;
+  }
+};
+
+double plan_cost(const std::vector<PlanEntry>& e, const std::vector<int>& order, int ta, int cus) {
+  std::vector<double> load(cus, 0.0);
+  int64_t t0 = 0;
+  double red = 0.0;
+  bool any = false;
+  for (int i : order) {
+    const int64_t n = e[i].tiles * e[i].splits;
+    const double us = e[i].task_us(ta);
+    const int64_t full = n / cus, rem = n % cus;
+    const int64_t b = t0 % cus;
+    if (full)
+      for (int w = 0; w < cus; ++w) load[w] += full * us;
+    for (int64_t k = 0; k < rem; ++k) load[(b + k) % cus] += us;
+    t0 += n;
+    if (e[i].splits > 1) {
+      red += (double)(e[i].splits + 1) * e[i].mn * 4.0 / 5.0e6;  // bytes at ~5 TB/s, in us
+      any = true;
+    }
+  }
+  return *std::max_element(load.begin(), load.end()) + (any ? red + 5.0 : 0.0);
+}
+
+std::vector<int> plan_order(const std::vector<PlanEntry>& e, int ta) {
+  std::vector<int> o(e.size());
+  std::iota(o.begin(), o.end(), 0);
+  std::stable_sort(o.begin(), o.end(), [&](int a, int b) { return e[a].task_us(ta) > e[b].task_us(ta); });
+  return o;
+}
+}  // namespace
+
+int64_t gemm_grouped_plan(ql_gemv_desc* descs, int32_t count, int64_t M, int64_t* ws_floats) {
+  const int ta = large_ta(M);
+  const int64_t mt = (M + 64 * ta - 1) / (64 * ta);
+  const int cus = device_cu_count();
+  std::vector<PlanEntry> e(count);
+  for (int32_t i = 0; i < count; ++i)
+    e[i] = PlanEntry{((descs[i].N + kG2Rows - 1) / kG2Rows) * mt, descs[i].K / kG2K, M * descs[i].N, 1};
+  auto max_splits = [](const PlanEntry& p) { return (int)std::max<int64_t>(1, std::min<int64_t>(16, p.stages / 2)); };
+  double cur = -1.0;
+  std::vector<int> best_s(count, 1);
+  int64_t longest = 0;
+  for (const PlanEntry& p : e) longest = std::max(longest, p.stages);
+  for (int64_t L = longest; L >= 2; --L) {
+    for (int32_t i = 0; i < count; ++i)
+      e[i].splits = (int)std::min<int64_t>(max_splits(e[i]), (e[i].stages + L - 1) / L);
+    const double c = plan_cost(e, plan_order(e, ta), ta, cus);
+    if (cur < 0.0 || c < cur - 0.25) {
+      cur = c;
+      for (int32_t i = 0; i < count; ++i) best_s[i] = e[i].splits;
+    }
+  }
+  // Two task lengths: the entries of a subset cut to the shorter one (for instance the
+  // tiles that overflow the first round split in halves while the others stay whole);
+  // every subset when there are at most 10 entries.
+  if (count <= 10) {
+    std::vector<int64_t> Ls;
+    for (const PlanEntry& p : e)
+      for (int k = 1; k <= 16; ++k) Ls.push_back((p.stages + k - 1) / k);
+    std::sort(Ls.begin(), Ls.end());
+    Ls.erase(std::unique(Ls.begin(), Ls.end()), Ls.end());
+    for (size_t a = 0; a + 1 < Ls.size(); ++a)
+      for (size_t b = a + 1; b < Ls.size() && b <= a + 3; ++b)
+        for (uint32_t mask = 1; mask + 1 < (1u << count); ++mask) {
+          for (int32_t i = 0; i < count; ++i) {
+            const int64_t L = (mask >> i) & 1 ? Ls[a] : Ls[b];
+            e[i].splits = (int)std::min<int64_t>(max_splits(e[i]), (e[i].stages + L - 1) / L);
+          }
+          const double c = plan_cost(e, plan_order(e, ta), ta, cus);
+          if (c < cur - 0.25) {
+            cur = c;
+            for (int32_t i = 0; i < count; ++i) best_s[i] = e[i].splits;
+          }
+        }
+  }
+  for (int32_t i = 0; i < count; ++i) e[i].splits = best_s[i];
+  for (int it = 0; it < 4 * count * 16; ++it) {
+    int best = -1, best_step = 0;
+    double best_cost = cur;
+    for (int32_t i = 0; i < count; ++i)
+      for (int step : {1, -1}) {
+        if (e[i].splits + step < 1 || e[i].splits + step > max_splits(e[i])) continue;
+        e[i].splits += step;
+        const double c = plan_cost(e, plan_order(e, ta), ta, cus);
+        e[i].splits -= step;
+        if (c < best_cost - 0.25) {
+          best = i;
+          best_step = step;
+          best_cost = c;
+        }
+      }
+    if (best < 0) break;
+    e[best].splits += best_step;
+    cur = best_cost;
+  }
+  const std::vector<int> order = plan_order(e, ta);
+  std::vector<ql_gemv_desc> sorted(count);
+  int64_t total = 0, ws = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const int i = order[j];
+    ql_gemv_desc d = descs[i];
+    d.kparts = e[i].splits;
+    d.reserved = 0;
+    d.slab_begin = (int32_t)total;
+    total += e[i].tiles * e[i].splits;
+    d.ws_begin = 0;
+    if (e[i].splits > 1) {
+      d.ws_begin = ws;
+      ws += (int64_t)e[i].splits * e[i].mn;
+      ws = (ws + 63) / 64 * 64;  // each entry's partials start 256-byte aligned
+    }
+    sorted[j] = d;
+  }
+  std::copy(sorted.begin(), sorted.end(), descs);
+  if (ws_floats) *ws_floats = ws;
+  return total;
+}
+
+hipError_t launch_gemm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total, int M, float* ws,
+                               int64_t ws_floats, hipStream_t stream) {
+  const int ta = large_ta(M);
+  const int grid = (int)std::min<int64_t>(total, device_cu_count());
+  if (ta == 1)
+    hipLaunchKernelGGL(gemm2_grouped_kernel<1>, dim3(grid), dim3(kG2Threads), 0, stream, descs, count, total, M, ws, ws_floats);
+  else if (ta == 2)
+    hipLaunchKernelGGL(gemm2_grouped_kernel<2>, dim3(grid), dim3(kG2Threads), 0, stream, descs, count, total, M, ws, ws_floats);
+  else
+    hipLaunchKernelGGL(gemm2_grouped_kernel<4>, dim3(grid), dim3(kG2Threads), 0, stream, descs, count, total, M, ws, ws_floats);
+  if (ws_floats > 0)
+    hipLaunchKernelGGL(gemm_reduce_grouped_kernel, dim3(512, count), dim3(256), 0, stream, descs, M, ws, ws_floats);
   return hipGetLastError();
 }
 

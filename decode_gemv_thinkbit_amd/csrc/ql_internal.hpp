@@ -44,6 +44,12 @@ hipError_t launch_c4_gemv_grouped(const ql_gemv_desc* descs, int32_t count, int6
                                   hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const MatArgs& a, int M, void* workspace, size_t ws_bytes, hipStream_t stream);
+// Grouped large-tile GEMM (M >= 16): the host plan sorts and splits the entries (slab_begin =
+// first task, kparts = K splits, ws_begin = first partial-sum float) and returns the task
+// count; the launch runs every entry's tiles and then the reduction of the split ones.
+int64_t gemm_grouped_plan(ql_gemv_desc* descs, int32_t count, int64_t M, int64_t* ws_floats);
+hipError_t launch_gemm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t total, int M, float* ws,
+                               int64_t ws_floats, hipStream_t stream);
 // large: the large-tile kernel (bf16 c*s operands), else the small-batch exact kernel
 hipError_t launch_gemm_as(const MatArgs& a, int M, void* workspace, size_t ws_bytes, bool large, hipStream_t stream);
 

@@ -92,6 +92,9 @@ def lib():
         L.qlinear_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.qlinear_gemm_workspace_bytes.restype = sz
         L.qlinear_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qlinear_gemm_grouped_prepare.argtypes = [vp, ctypes.c_int32, i64, ctypes.POINTER(i64)]
+        L.qlinear_gemm_grouped_prepare.restype = i64
+        L.qlinear_gemm_grouped.argtypes = [vp, ctypes.c_int32, i64, i64, vp, sz, vp]
         L.qlinear_rtn_noise.argtypes = [i64, i64, vp, vp, vp]
         L.qlinear_allocate.argtypes = [vp, i64, ctypes.c_double, vp, vp, vp]
         L.qlinear_block_sensitivity.argtypes = [i64, i64, vp, vp, vp, vp]
@@ -118,7 +121,7 @@ def lib():
         L.qlinear_c4_gemv_grouped.argtypes = [vp, ctypes.c_int32, i64, ctypes.c_int32, vp, vp]
         for name in ("qlinear_block_offsets", "qlinear_quantize", "qlinear_pack", "qlinear_pack_scales",
                      "qlinear_unpack", "qlinear_unpack_scales", "qlinear_dequant", "qlinear_gemv",
-                     "qlinear_gemv_grouped", "qlinear_gemv_grouped_noalloc", "qlinear_gemm", "qlinear_c4_pack", "qlinear_c4_unpack",
+                     "qlinear_gemv_grouped", "qlinear_gemv_grouped_noalloc", "qlinear_gemm", "qlinear_gemm_grouped", "qlinear_c4_pack", "qlinear_c4_unpack",
                      "qlinear_c4_to_packed", "qlinear_c4_gemv", "qlinear_c4_gemv_grouped", "qlinear_rtn_noise",
                      "qlinear_allocate", "qlinear_block_sensitivity", "qlinear_validate_codes", "qlinear_validate_packed", "qlinear_lb_pack", "qlinear_lb_gemv"):
             getattr(L, name).restype = i32
@@ -612,3 +615,41 @@ class GroupedGemv:
             return
         fn = lib().qlinear_c4_gemv_grouped if self.containers else lib().qlinear_gemv_grouped
         _check(fn(_ptr(self.descs), self.count, self.total, self.M, _ptr(self.sched), _stream()), "gemv_grouped")
+
+
+class GroupedGemm:
+    """One persistent large-tile GEMM launch (plus one reduction launch when K is split) over many
+    independent (x, W, y) products at one M >= 16: qlinear_gemm_grouped."""
+
+    def __init__(self, items):
+        """items: list of (PackedWeight, x [M, K] bf16, y [M, N] fp32), all with the same M."""
+        if not items:
+            raise ValueError("no items")
+        self.items = items
+        self.M = items[0][1].shape[0]
+        arr = (ql_gemv_desc * len(items))()
+        for i, (pw, x, y) in enumerate(items):
+            _dev(x, torch.bfloat16, "x")
+            _dev(y, torch.float32, "y")
+            if x.dim() != 2 or x.shape[0] != self.M or x.shape[1] != pw.K or y.numel() != self.M * pw.N:
+                raise ValueError(f"item {i}: shapes do not match")
+            arr[i] = ql_gemv_desc(pw.packed.data_ptr(), pw.pscales.data_ptr(),
+                                  pw.blk_grid.data_ptr() if pw.blk_grid is not None else None,
+                                  pw.blk_off.data_ptr() if pw.blk_off is not None else None,
+                                  x.data_ptr(), y.data_ptr(), pw.N, pw.K, pw.grid, 0, 0, 0, 0)
+        wsb = ctypes.c_int64(0)
+        total = lib().qlinear_gemm_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(items), self.M,
+                                                   ctypes.byref(wsb))
+        if total < 0:
+            _check(1, "gemm_grouped_prepare")
+        self.total = int(total)
+        self.count = len(items)
+        self.plan = [{"N": int(d.N), "K": int(d.K), "splits": int(d.kparts), "first_task": int(d.slab_begin),
+                      "ws_begin": int(d.ws_begin)} for d in arr]
+        self.descs = torch.frombuffer(bytearray(bytes(memoryview(arr))), dtype=torch.uint8).to(items[0][1].device)
+        self.ws_bytes = int(wsb.value)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=items[0][1].device)
+
+    def run(self):
+        _check(lib().qlinear_gemm_grouped(_ptr(self.descs), self.count, self.total, self.M, _ptr(self.ws),
+                                          self.ws_bytes, _stream()), "gemm_grouped")

@@ -258,15 +258,44 @@ ql_status qlinear_gemv_grouped_noalloc(const ql_gemv_desc *descs, int32_t count,
                                        int64_t state_words, hipStream_t stream);
 
 /* Batched GEMM for 1 <= M (tuned for 16..512): tiles of codes are decoded into LDS as bf16
- * (codes are exact in bf16) and contracted on MFMA (bf16 x bf16 -> fp32); the group scale
- * is applied to each 128-deep partial product in fp32.  Dequantizing to bf16 and computing
- * in bf16 reproduces the native low-bit result (k-quant calibration page, section "Not just
- * any noise").  workspace (dev) of qlinear_gemm_workspace_bytes(M, N, K) bytes (may be 0). */
+ * and contracted on MFMA (bf16 x bf16 -> fp32).  Below 16 tokens the tile holds the exact
+ * codes and the group scale multiplies each 128-deep partial product in fp32; from 16 tokens
+ * on it holds RNE(c * s) in bf16 (exact except 3-bit codes of magnitude 3).  Dequantizing to
+ * bf16 and computing in bf16 reproduces the native low-bit result (k-quant calibration page,
+ * section "Not just any noise").  workspace (dev) of qlinear_gemm_workspace_bytes(M, N, K)
+ * bytes (may be 0): the K-split partial sums, added by a second kernel in split order. */
 size_t qlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 ql_status qlinear_gemm(int64_t M, int64_t N, int64_t K, int grid, const int8_t *blk_grid,
                        const int64_t *blk_off, const void *packed, const uint16_t *pscales,
                        const uint16_t *x, float *y, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/* Grouped GEMM: many independent y = x * W^T products at one M (16 <= M < 2^24; each x M x K
+ * bf16 bits, each y M x N fp32), e.g. the seven linears of a decoder layer at a prefill or
+ * batched-decode size, in one persistent launch of qlinear_gemm's large-tile kernel (same
+ * operands, same bar) plus, when any entry is split, one reduction launch.  Workgroups take
+ * 256-row x (64, 128 or 256)-token tiles of all entries round-robin, longest first, so small
+ * matrices no longer leave most of the device idle and K is split only where that shortens
+ * the launch (the launch also needs no per-matrix reduction pass).
+ *
+ * qlinear_gemm_grouped_prepare (host) checks every descriptor (ql_gemv_desc: packed, pscales,
+ * blk_grid/blk_off for mixed grids, x, y, N, K, grid; kparts and reserved are ignored), chooses
+ * each entry's K splits for this M and this device, reorders the array (longest tasks first),
+ * fills slab_begin (the entry's first task), kparts (its splits) and ws_begin (the first float
+ * of its partial sums in the workspace), stores the workspace size in *workspace_bytes (0 when
+ * nothing is split) and returns the task count, or -1 (qlinear_last_error()) on a bad
+ * descriptor or M.  The plan depends on M: prepare again for another M.
+ *
+ * qlinear_gemm_grouped runs a prepared list (copied to device memory by the caller: descs
+ * (dev), count entries) with that M and task count; workspace (dev, 16-byte aligned, owned by
+ * the caller, contents need not be zeroed) of the prepared size.  An entry whose partial sums
+ * would not fit workspace_bytes computes nothing (its y is left as it was); tasks past an
+ * entry's own range are dropped.  No y may alias another entry's x or y.  Results are
+ * bitwise reproducible for a given prepared list. */
+int64_t qlinear_gemm_grouped_prepare(ql_gemv_desc *descs, int32_t count, int64_t M,
+                                     int64_t *workspace_bytes);
+ql_status qlinear_gemm_grouped(const ql_gemv_desc *descs, int32_t count, int64_t total_tasks, int64_t M,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- grid allocation (offline)
  *

@@ -260,3 +260,41 @@ def test_grouped_prepare_rejects_rows_beyond_the_batched_range():
     assert b"K=" in L.qlinear_last_error()
     arr = _descs([(64, 1 << 26, 0)], [1])
     assert L.qlinear_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), 1) == 1
+
+
+def test_gemm_grouped_prepare_plan_and_errors():
+    """Host plan of the grouped GEMM: entries longest-first with consecutive task ranges, the
+    workspace covering every split entry's partials, and bad arguments rejected."""
+    L = ql.lib()
+    shapes = [(4096, 4096), (1024, 4096), (4096, 12288), (12288, 4096)]
+
+    def arr_of():
+        arr = (ql.ql_gemv_desc * len(shapes))()
+        for i, (N, K) in enumerate(shapes):
+            base = 0x100000 * (i + 1)
+            arr[i] = ql.ql_gemv_desc(base, base + 0x1000, None, None, base + 0x2000, base + 0x3000, N, K, 0, 0, 0, 0, 0)
+        return arr
+
+    for M in (16, 64, 256, 512):
+        arr = arr_of()
+        ws = ctypes.c_int64(-1)
+        total = L.qlinear_gemm_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(shapes), M, ctypes.byref(ws))
+        assert total > 0
+        mt = (M + 64 * (1 if M <= 64 else 2 if M <= 128 else 4) - 1) // (64 * (1 if M <= 64 else 2 if M <= 128 else 4))
+        first, need, prev = 0, 0, None
+        for d in arr:
+            assert d.slab_begin == first and 1 <= d.kparts <= 16
+            stages = (d.K // 64 + d.kparts - 1) // d.kparts
+            assert prev is None or stages <= prev + 1  # longest tasks first (stage counts)
+            prev = stages
+            first += ((d.N + 255) // 256) * mt * d.kparts
+            if d.kparts > 1:
+                assert d.ws_begin >= need and d.ws_begin % 64 == 0
+                need = d.ws_begin + d.kparts * M * d.N
+        assert first == total and ws.value >= 4 * need
+    arr = arr_of()
+    assert L.qlinear_gemm_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(shapes), 8, None) == -1
+    assert L.qlinear_gemm_grouped_prepare(None, 0, 64, None) == -1
+    arr[1].K = 100  # not a multiple of 128
+    assert L.qlinear_gemm_grouped_prepare(ctypes.cast(arr, ctypes.c_void_p), len(shapes), 64, None) == -1
+    assert L.qlinear_gemm_grouped(None, 1, 1, 64, None, 0, None) != 0
