@@ -77,11 +77,21 @@ __device__ __forceinline__ void lb_z_terms(int slab, int lane, int r, int RP, in
   const int path = slab / spp, j = (slab % spp) * kSlab + lane;
   float z = 0.0f;
   if (j < r) {
+    // 32 loads in flight, then the in-order adds (a slice index past the last rereads
+    // the last slice and is not added)
     float sum = 0.0f;
-#pragma unroll 16  // loads issued ahead of the in-order adds
-    for (int q = 0; q < nslices; ++q)
-      sum += __hip_atomic_load(partial + (int64_t)q * 2 * RP + path * RP + j, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    for (int q0 = 0; q0 < nslices; q0 += 32) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int q = q0 + i < nslices ? q0 + i : nslices - 1;
+        v[i] = __hip_atomic_load(partial + (int64_t)q * 2 * RP + path * RP + j, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (q0 + i < nslices) sum += v[i];
+    }
     z = sum * bf16_bits_to_f32(l[path * r + j]);
   }
   const uint32_t hi = bf16_rne_bits(z);
@@ -102,6 +112,14 @@ __device__ __forceinline__ void lb_z_terms(int slab, int lane, int r, int RP, in
       for (int t = 0; t < 3; ++t) zs[((int64_t)path * ZP + P) * 3 + t] = 0u;
 }
 
+typedef const __attribute__((address_space(1))) uint32_t* lb_gu32p;
+
+// The inner loops read only LDS: the scales g, the activations x and the z terms a
+// chunk needs are staged in a per-wave LDS buffer by vector loads issued one chunk
+// ahead.  (Wave-uniform scalar loads inside these loops would share the LDS reads'
+// completion counter and, returning out of order, force a full drain before every
+// table read.)  A wave writes and then reads its own buffer, and LDS executes one
+// wave's operations in order, so no barrier separates the two.
 __global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, int32_t r, int32_t RP, int32_t ZP,
                                                                   int32_t slice_chunks, int32_t nslices,
                                                                   const uint8_t* __restrict__ v_bits,
@@ -112,31 +130,60 @@ __global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, 
                                                                   uint32_t* __restrict__ counters,
                                                                   uint32_t* __restrict__ zs) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLbLutBytes];
+  // per wave, two chunk buffers of 64 input pairs: (g pair, x pair) dwords
+  __shared__ __attribute__((aligned(16))) uint2 gxs[kLbWaves][2][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ntasks = 2 * RP / kSlab * nslices, stride = gridDim.x * kLbWaves;
+  const int rb = d_in / 8, nchunks = rb / kChunkBytes;
+  const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
+  const lb_gu32p xw = (lb_gu32p)x;
+  // chunk c of task t: its sign bits (lane = latent row) and the (g, x) dwords of its
+  // input pair `lane`
+  uint4 d = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t gv = 0u, xv = 0u;
+  auto issue = [&](int t, int c) {
+    const int slab = t / nslices, path = slab / (RP / kSlab);
+    d = ChunkSrc(v_bits + (int64_t)slab * kSlab * rb, nchunks, lane).load(c);
+    gv = ((lb_gu32p)(g + (int64_t)path * d_in))[64 * c + lane];
+    xv = xw[64 * c + lane];
+  };
+  int task = blockIdx.x * kLbWaves + wave;
+  if (task < ntasks) issue(task, (task % nslices) * slice_chunks);  // in flight during the table build
   build_sign_masks(lut);
   __syncthreads();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int ntasks = 2 * RP / kSlab * nslices;
-  const int rb = d_in / 8, nchunks = rb / kChunkBytes;
-  const cu32p xp = (cu32p)x;
-  const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
+  int buf = 0;
   // persistent: the table is built once per workgroup, tasks stride over the waves
-  for (int task = blockIdx.x * kLbWaves + wave; task < ntasks; task += gridDim.x * kLbWaves) {
+  for (; task < ntasks; task += stride) {
     const int slab = task / nslices, q = task % nslices;
-    const int path = slab / (RP / kSlab);
     const int c0 = q * slice_chunks, c1 = (c0 + slice_chunks < nchunks) ? c0 + slice_chunks : nchunks;
-    const ChunkSrc src(v_bits + (int64_t)slab * kSlab * rb, nchunks, lane);
-    const cu32p gp = (cu32p)(g + (int64_t)path * d_in);
     float acc = 0.0f;
-    for (int c = c0; c < c1; ++c) {
-      const uint4 d = src.load(c);
-#pragma unroll 8  // (full unrolling holds 128 x and g dwords in SGPRs and spills)
-      for (int B = 0; B < 16; ++B) {
-        const u32x4_t e = lds_b128(lut + lut_addr(d, B, lane_off));
+    for (int c = c0; c < c1; ++c, buf ^= 1) {
+      gxs[wave][buf][lane] = make_uint2(gv, xv);
+      const uint4 dc = d;
+      if (c + 1 < c1) issue(task, c + 1);
+      else if (task + stride < ntasks) issue(task + stride, ((task + stride) % nslices) * slice_chunks);
+      const uint8_t* gb = reinterpret_cast<const uint8_t*>(&gxs[wave][buf][0]);
+      // step B reads the sign masks of byte B and the (g, x) of input pairs 4B .. 4B+3,
+      // three steps ahead of their use (a ring of four operand sets)
+      u32x4_t E[4], P0[4], P1[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int P = 64 * c + 4 * B + k;  // input pair (2P, 2P+1)
-          acc = dot2(gp[P] ^ e[k], xp[P], acc);
+      for (int B = 0; B < 3; ++B) {
+        E[B] = lds_b128(lut + lut_addr(dc, B, lane_off));
+        P0[B] = lds_b128(gb + 32 * B);
+        P1[B] = lds_b128(gb + 32 * B + 16);
+      }
+#pragma unroll
+      for (int B = 0; B < 16; ++B) {
+        if (B + 3 < 16) {
+          E[(B + 3) & 3] = lds_b128(lut + lut_addr(dc, B + 3, lane_off));
+          P0[(B + 3) & 3] = lds_b128(gb + 32 * (B + 3));
+          P1[(B + 3) & 3] = lds_b128(gb + 32 * (B + 3) + 16);
         }
+        const u32x4_t e = E[B & 3], p0 = P0[B & 3], p1 = P1[B & 3];
+        acc = dot2(p0[0] ^ e[0], p0[1], acc);
+        acc = dot2(p0[2] ^ e[1], p0[3], acc);
+        acc = dot2(p1[0] ^ e[2], p1[1], acc);
+        acc = dot2(p1[2] ^ e[3], p1[3], acc);
       }
     }
     // partial sums travel at device scope (the XCDs' L2 caches are not coherent with
@@ -159,9 +206,9 @@ __global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, 
 
 // y[n] = h0[n] * sum_j s0(n, j) z0_j + h1[n] * sum_j s1(n, j) z1_j.  A
 // workgroup owns one 64-row slab; its four waves split the row's latent chunks
-// (path 0's, then path 1's) into contiguous quarters, so every wave's z
-// operands stay wave-uniform (scalar loads), and the quarters' per-path sums
-// are added through LDS in wave order.
+// (path 0's, then path 1's) into contiguous quarters, and the quarters' per-path
+// sums are added through LDS in wave order.  A chunk's z terms (64 latent pairs x 3
+// dwords) are staged in the wave's LDS buffer and read back as broadcasts.
 __global__ void __launch_bounds__(kLbWaves * 64) lb_output_kernel(int32_t d_out, int32_t urb, int32_t ZP,
                                                                   const uint8_t* __restrict__ u_bits,
                                                                   const uint32_t* __restrict__ zs,
@@ -169,50 +216,91 @@ __global__ void __launch_bounds__(kLbWaves * 64) lb_output_kernel(int32_t d_out,
                                                                   float* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLbLutBytes];
   __shared__ float part[kLbWaves][2][kSlab];
-  build_pm_ones(lut);
-  __syncthreads();
+  __shared__ __attribute__((aligned(16))) uint32_t zst[kLbWaves][2][kSlab * 3];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int half_chunks = urb / 2 / kChunkBytes;  // chunks of one path's part of a row
   const int nch = 2 * half_chunks;
   const int c0 = nch * wave / kLbWaves, c1 = nch * (wave + 1) / kLbWaves;
   const uint32_t lane_off = (uint32_t)(lane & 15) << 4;
   const int nslabs = (d_out + kSlab - 1) / kSlab;
+  // chunk cc of slab s: its sign bits (lane = output row) and the three z dwords of latent
+  // pair `lane` of the chunk
+  uint4 d = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t z0 = 0u, z1 = 0u, z2 = 0u;
+  auto issue = [&](int s, int cc) {
+    const int p = cc >= half_chunks, c = cc - p * half_chunks;
+    d = ChunkSrc(u_bits + (int64_t)s * kSlab * urb, nch, lane).load(cc);
+    const lb_gu32p zp = (lb_gu32p)(zs + ((int64_t)p * ZP + 64 * c + lane) * 3);
+    z0 = zp[0];
+    z1 = zp[1];
+    z2 = zp[2];
+  };
+  if (c0 < c1) issue(blockIdx.x, c0);  // in flight during the table build
+  build_pm_ones(lut);
+  __syncthreads();
+  int buf = 0;
   // persistent: the table is built once per workgroup, slabs stride over the workgroups
   for (int slab = blockIdx.x; slab < nslabs; slab += gridDim.x) {
-  const ChunkSrc src(u_bits + (int64_t)slab * kSlab * urb, nch, lane);
-  float acc[2] = {0.0f, 0.0f};
-  for (int cc = c0; cc < c1; ++cc) {
-    const int p = cc >= half_chunks, c = cc - p * half_chunks;
-    const cu32p zp = (cu32p)(zs + (int64_t)p * ZP * 3);
-    const uint4 d = src.load(cc);
-    float a = 0.0f;
-#pragma unroll 4  // (full unrolling keeps 192 z dwords of a chunk in SGPRs and spills)
-    for (int B = 0; B < 16; ++B) {
-      const u32x4_t e = lds_b128(lut + lut_addr(d, B, lane_off));
+    float acc[2] = {0.0f, 0.0f};
+    for (int cc = c0; cc < c1; ++cc, buf ^= 1) {
+      const int p = cc >= half_chunks;
+      uint32_t* zb = &zst[wave][buf][0];
+      zb[3 * lane] = z0;
+      zb[3 * lane + 1] = z1;
+      zb[3 * lane + 2] = z2;
+      const uint4 dc = d;
+      if (cc + 1 < c1) issue(slab, cc + 1);
+      else if (slab + (int)gridDim.x < nslabs) issue(slab + gridDim.x, c0);
+      const uint8_t* zr = reinterpret_cast<const uint8_t*>(zb);
+      float a = 0.0f;
+      // step B reads the (+-1, +-1) pairs of byte B and the three terms of latent pairs
+      // 4B .. 4B+3 (twelve dwords), two steps ahead of their use (a ring of three sets)
+      u32x4_t E[3], W0[3], W1[3], W2[3];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int P = 64 * c + 4 * B + k;  // latent pair (2P, 2P+1)
-        a = dot2(e[k], zp[3 * P], a);
-        a = dot2(e[k], zp[3 * P + 1], a);
-        a = dot2(e[k], zp[3 * P + 2], a);
+      for (int B = 0; B < 2; ++B) {
+        E[B] = lds_b128(lut + lut_addr(dc, B, lane_off));
+        W0[B] = lds_b128(zr + 48 * B);
+        W1[B] = lds_b128(zr + 48 * B + 16);
+        W2[B] = lds_b128(zr + 48 * B + 32);
       }
-    }
-    if (p) acc[1] += a; else acc[0] += a;
-  }
-  part[wave][0][lane] = acc[0];
-  part[wave][1][lane] = acc[1];
-  __syncthreads();
-  if (wave == 0) {
-    float s0 = part[0][0][lane], s1 = part[0][1][lane];
 #pragma unroll
-    for (int w = 1; w < kLbWaves; ++w) {
-      s0 += part[w][0][lane];
-      s1 += part[w][1][lane];
+      for (int B = 0; B < 16; ++B) {
+        if (B + 2 < 16) {
+          E[(B + 2) % 3] = lds_b128(lut + lut_addr(dc, B + 2, lane_off));
+          W0[(B + 2) % 3] = lds_b128(zr + 48 * (B + 2));
+          W1[(B + 2) % 3] = lds_b128(zr + 48 * (B + 2) + 16);
+          W2[(B + 2) % 3] = lds_b128(zr + 48 * (B + 2) + 32);
+        }
+        const u32x4_t e = E[B % 3], w0 = W0[B % 3], w1 = W1[B % 3], w2 = W2[B % 3];
+        a = dot2(e[0], w0[0], a);
+        a = dot2(e[0], w0[1], a);
+        a = dot2(e[0], w0[2], a);
+        a = dot2(e[1], w0[3], a);
+        a = dot2(e[1], w1[0], a);
+        a = dot2(e[1], w1[1], a);
+        a = dot2(e[2], w1[2], a);
+        a = dot2(e[2], w1[3], a);
+        a = dot2(e[2], w2[0], a);
+        a = dot2(e[3], w2[1], a);
+        a = dot2(e[3], w2[2], a);
+        a = dot2(e[3], w2[3], a);
+      }
+      if (p) acc[1] += a; else acc[0] += a;
     }
-    const int64_t n = (int64_t)slab * kSlab + lane;
-    if (n < d_out) y[n] = fmaf(bf16_bits_to_f32(h[n]), s0, bf16_bits_to_f32(h[d_out + n]) * s1);
-  }
-  __syncthreads();  // part is rewritten by the next slab
+    part[wave][0][lane] = acc[0];
+    part[wave][1][lane] = acc[1];
+    __syncthreads();
+    if (wave == 0) {
+      float s0 = part[0][0][lane], s1 = part[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < kLbWaves; ++w) {
+        s0 += part[w][0][lane];
+        s1 += part[w][1][lane];
+      }
+      const int64_t n = (int64_t)slab * kSlab + lane;
+      if (n < d_out) y[n] = fmaf(bf16_bits_to_f32(h[n]), s0, bf16_bits_to_f32(h[d_out + n]) * s1);
+    }
+    __syncthreads();  // part is rewritten by the next slab
   }
 }
 
