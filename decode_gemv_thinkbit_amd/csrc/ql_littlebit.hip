@@ -36,26 +36,32 @@ constexpr int kLbLutBytes = 256 * 16 * 16;  // 256 byte values x 16 replicas x 1
 
 __device__ __forceinline__ uint32_t bf16_one(int bit) { return bit ? 0xBF80u : 0x3F80u; }
 
+// The tables: 256 byte values x 16 replicas of a 16-byte entry (byte b's replica q at
+// b * 256 + q * 16; a lane reads replica lane % 16, so the 16 lanes a read serves at once
+// hit distinct banks).  Built by 256 threads, thread b computing byte b's entry once and
+// writing its replicas in the order (b + i) % 16, so that the 16 lanes of one write also
+// hit distinct banks.
+template <typename F>
+__device__ __forceinline__ void build_replicated(uint8_t* lut, F entry_dword) {
+  static_assert(kLbWaves * 64 == 256, "one thread per byte value");
+  const int b = threadIdx.x;
+  const uint4 v = make_uint4(entry_dword(b, 0), entry_dword(b, 1), entry_dword(b, 2), entry_dword(b, 3));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(lut + 256 * b + 16 * ((b + i) & 15)) = v;
+}
+
 // dword k of byte b's entry: sign masks of elements 2k (bit 15) and 2k+1 (bit 31)
 __device__ void build_sign_masks(uint8_t* lut) {
-  for (int e = threadIdx.x; e < 256 * 16; e += blockDim.x) {
-    const int b = e >> 4;
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = ((b >> (2 * k)) & 1 ? 0x8000u : 0u) | ((b >> (2 * k + 1)) & 1 ? 0x80000000u : 0u);
-    *reinterpret_cast<uint4*>(lut + 16 * e) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  build_replicated(lut, [](int b, int k) {
+    return ((b >> (2 * k)) & 1 ? 0x8000u : 0u) | ((b >> (2 * k + 1)) & 1 ? 0x80000000u : 0u);
+  });
 }
 
 // dword k of byte b's entry: the bf16 pair (+-1, +-1) of elements 2k, 2k+1
 __device__ void build_pm_ones(uint8_t* lut) {
-  for (int e = threadIdx.x; e < 256 * 16; e += blockDim.x) {
-    const int b = e >> 4;
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = bf16_one((b >> (2 * k)) & 1) | (bf16_one((b >> (2 * k + 1)) & 1) << 16);
-    *reinterpret_cast<uint4*>(lut + 16 * e) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  build_replicated(lut, [](int b, int k) {
+    return bf16_one((b >> (2 * k)) & 1) | (bf16_one((b >> (2 * k + 1)) & 1) << 16);
+  });
 }
 
 // table row of byte B (0..15) of a 16-byte chunk: byte << 8 | replica offset
@@ -66,34 +72,15 @@ __device__ __forceinline__ uint32_t lut_addr(const uint4& d, int B, uint32_t lan
 // partial[q][row] = sum over inputs of slice q of s(row, i) * g_i * x_i
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return f32_to_bf16_bits(f); }
 
-// z of the 64 latent rows of slab `slab` (lane = row), as three bf16 terms per
-// element: zs[(path*ZP + P)*3 + t] holds term t of elements 2P (low half) and
-// 2P+1 (high half).  Rows at or past r have z = 0; the path's last slab also
-// zeroes the pairs between its padded row count and ZP.
-__device__ __forceinline__ void lb_z_terms(int slab, int lane, int r, int RP, int ZP, int nslices,
-                                           const float* __restrict__ partial, const uint16_t* __restrict__ l,
-                                           uint32_t* __restrict__ zs) {
+// z of the 64 latent rows of slab `slab` (lane = row) from the slab's input sum
+// (ignored at rows past r), as three bf16 terms per element: zs[(path*ZP + P)*3 + t]
+// holds term t of elements 2P (low half) and 2P+1 (high half).  Rows at or past r have
+// z = 0; the path's last slab also zeroes the pairs between its padded row count and ZP.
+__device__ __forceinline__ void lb_z_store(int slab, int lane, int r, int RP, int ZP, float sum,
+                                           const uint16_t* __restrict__ l, uint32_t* __restrict__ zs) {
   const int spp = RP / kSlab;  // slabs per path
   const int path = slab / spp, j = (slab % spp) * kSlab + lane;
-  float z = 0.0f;
-  if (j < r) {
-    // 32 loads in flight, then the in-order adds (a slice index past the last rereads
-    // the last slice and is not added)
-    float sum = 0.0f;
-    for (int q0 = 0; q0 < nslices; q0 += 32) {
-      float v[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int q = q0 + i < nslices ? q0 + i : nslices - 1;
-        v[i] = __hip_atomic_load(partial + (int64_t)q * 2 * RP + path * RP + j, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (q0 + i < nslices) sum += v[i];
-    }
-    z = sum * bf16_bits_to_f32(l[path * r + j]);
-  }
+  const float z = j < r ? sum * bf16_bits_to_f32(l[path * r + j]) : 0.0f;
   const uint32_t hi = bf16_rne_bits(z);
   const float r1 = z - bf16_bits_to_f32(hi);
   const uint32_t mid = bf16_rne_bits(r1);
@@ -110,6 +97,26 @@ __device__ __forceinline__ void lb_z_terms(int slab, int lane, int r, int RP, in
   if (slab % spp == spp - 1)
     for (int P = RP / 2 + lane; P < ZP; P += 64)
       for (int t = 0; t < 3; ++t) zs[((int64_t)path * ZP + P) * 3 + t] = 0u;
+}
+
+// The split form's slab sum: the slices' partial sums in slice order, 32 loads in flight
+// (a slice index past the last rereads the last slice and is not added).
+__device__ __forceinline__ float lb_slice_sum(int slab, int lane, int RP, int nslices,
+                                              const float* __restrict__ partial) {
+  const float* p = partial + (int64_t)slab * kSlab + lane;  // slice q at p + q * 2 * RP
+  float sum = 0.0f;
+  for (int q0 = 0; q0 < nslices; q0 += 32) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int q = q0 + i < nslices ? q0 + i : nslices - 1;
+      v[i] = __hip_atomic_load(p + (int64_t)q * 2 * RP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (q0 + i < nslices) sum += v[i];
+  }
+  return sum;
 }
 
 typedef const __attribute__((address_space(1))) uint32_t* lb_gu32p;
@@ -200,7 +207,7 @@ __global__ void __launch_bounds__(kLbWaves * 64) lb_latent_kernel(int32_t d_in, 
       asm volatile("" ::: "memory");
       if (lane == 0) __hip_atomic_store(counters + slab * 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    lb_z_terms(slab, lane, r, RP, ZP, nslices, partial, l, zs);
+    lb_z_store(slab, lane, r, RP, ZP, lb_slice_sum(slab, lane, RP, nslices, partial), l, zs);
   }
 }
 

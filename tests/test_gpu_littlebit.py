@@ -46,8 +46,16 @@ def run_case(ora, dev, do, di, r, seed):
 
 
 @pytest.mark.parametrize("do,di,r", [(1, 128, 1), (70, 256, 19), (130, 384, 64), (64, 128, 129), (200, 2048, 300),
-                                     (1000, 4096, 33)])
+                                     (1000, 4096, 33), (3, 8192, 65)])
 def test_littlebit_small_shapes(ora, dev, do, di, r):
+    """Inputs of up to 64 chunks of 128 (d_in <= 8192): one workgroup per latent slab."""
+    run_case(ora, dev, do, di, r, seed=do + di + r)
+
+
+@pytest.mark.parametrize("do,di,r", [(300, 8320, 40), (130, 16384, 70), (64, 28672, 129), (257, 12288, 1)])
+def test_littlebit_split_latent_shapes(ora, dev, do, di, r):
+    """Inputs past 64 chunks of 128: the latent step splits each slab's inputs over waves of
+    several workgroups and sums the slices through device memory."""
     run_case(ora, dev, do, di, r, seed=do + di + r)
 
 
@@ -79,7 +87,7 @@ def test_littlebit_deterministic(ora, dev):
         assert torch.equal(ql.lb_gemv(x, lw), y)
 
 
-@pytest.mark.parametrize("do,di,bpw", [(28672, 8192, 0.1), (1000, 4096, 0.55), (130, 256, 1.0)])
+@pytest.mark.parametrize("do,di,bpw", [(28672, 8192, 0.1), (1000, 4096, 0.55), (130, 256, 1.0), (200, 16384, 0.3)])
 def test_littlebit_reused_workspace(ora, dev, do, di, bpw):
     """One workspace for many calls: the latent kernel's slab counters are zero again after every
     call, and the results match a fresh workspace bitwise, also for a new activation."""
