@@ -3,8 +3,6 @@
 // turns packed bytes straight into bf16 operands.
 #pragma once
 
-#include <utility>
-
 #include "ql_device.hpp"
 
 namespace ql {
@@ -21,32 +19,18 @@ constexpr int kTLut = kI2Lut + 256 * 32;      // 243 rows x 256 B (16 replicas x
 constexpr int kLutBytes = kTLut + 243 * 256;  // 78592
 static_assert(kTLut < 65536 && kI2Lut < 65536, "table bases must fit the LDS immediate offset");
 
-typedef uint32_t lut_v4 __attribute__((ext_vector_type(4)));
-typedef uint32_t lut_v2 __attribute__((ext_vector_type(2)));
-
-// Replicas of one table: slot e (row e / REP, replica e % REP, SZ bytes each)
-// takes replica 0 of its row.  Thread t copies slots t, t + NT, ...: all their
-// reads are issued before the first write.
-template <class V, int REP, int SZ, int SLOTS, int NT, int... I>
-__device__ __forceinline__ void lut_copies(uint8_t* tab, int t, std::integer_sequence<int, I...>) {
-  // (past the table: a row is read, never written)
-  const V v[] = {*reinterpret_cast<const V*>(tab + ((t + I * NT < SLOTS ? t + I * NT : SLOTS - 1) / REP) * REP * SZ)...};
-  ((t + I * NT < SLOTS && ((t + I * NT) % REP) != 0 ? (void)(*reinterpret_cast<V*>(tab + (t + I * NT) * SZ) = v[I])
-                                                     : (void)0),
-   ...);
-}
-
-// Every table row is computed once (replica 0), the rows of all three tables
-// spread over all NT threads of the workgroup; after a barrier the other
-// replicas are copied from them, consecutive threads writing consecutive
-// slots, with each thread's copies unrolled so their LDS reads are in flight
-// together.  Computing every slot separately cost about 2 us per launch, which
-// is much of a short launch.
+// Every table row is computed once, the rows of all three tables spread over
+// all NT threads of the workgroup, and the thread that computes a row writes
+// all its replicas, starting at replica (row mod REP): consecutive threads then
+// write different banks at every step, and no barrier or copy pass separates
+// computing from replicating.  (Computing every slot separately cost about
+// 2 us per launch, which is much of a short launch.)  The caller's barrier
+// follows.
 template <int NT>
 __device__ inline void build_luts(uint8_t* smem) {
   const int t = threadIdx.x;
   for (int r = t; r < 243 + 256 + 64; r += NT) {
-    if (r < 243) {
+    if (r < 243) {  // ternary: 243 rows x 16 replicas x 16 B
       int c[5], v = r;
       for (int i = 0; i < 5; ++i) {
         c[i] = v % 3 - 1;
@@ -57,25 +41,22 @@ __device__ inline void build_luts(uint8_t* smem) {
       q.y = code_bf16(c[2]) | (code_bf16(c[3]) << 16);
       q.z = code_bf16(c[4]);
       q.w = code_bf16(c[4]) << 16;
-      *reinterpret_cast<uint4*>(smem + kTLut + r * 256) = q;
-    } else if (r < 243 + 256) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(smem + kTLut + r * 256 + 16 * ((r + i) & 15)) = q;
+    } else if (r < 243 + 256) {  // 2-bit: 256 rows x 4 replicas x 8 B
       const int b = r - 243;
       uint2 q;
       q.x = code_bf16((b & 3) - 2) | (code_bf16(((b >> 2) & 3) - 2) << 16);
       q.y = code_bf16(((b >> 4) & 3) - 2) | (code_bf16(((b >> 6) & 3) - 2) << 16);
-      *reinterpret_cast<uint2*>(smem + kI2Lut + b * 32) = q;
-    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint2*>(smem + kI2Lut + b * 32 + 8 * ((b + i) & 3)) = q;
+    } else {  // 3-bit: 64 rows x 32 replicas x 4 B
       const int e = r - 243 - 256;
-      *reinterpret_cast<uint32_t*>(smem + kI3Lut + e * 128) = code_bf16((e & 7) - 4) | (code_bf16((e >> 3) - 4) << 16);
+      const uint32_t q = code_bf16((e & 7) - 4) | (code_bf16((e >> 3) - 4) << 16);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) *reinterpret_cast<uint32_t*>(smem + kI3Lut + e * 128 + 4 * ((e + i) & 31)) = q;
     }
   }
-  __syncthreads();
-  // ternary: 243 rows x 16 replicas x 16 B; 2-bit: 256 rows x 4 replicas x 8 B;
-  // 3-bit: 64 rows x 32 replicas x 4 B
-  constexpr int kT = (243 * 16 + NT - 1) / NT, kI2 = (256 * 4 + NT - 1) / NT, kI3 = (64 * 32 + NT - 1) / NT;
-  lut_copies<lut_v4, 16, 16, 243 * 16, NT>(smem + kTLut, t, std::make_integer_sequence<int, kT>{});
-  lut_copies<lut_v2, 4, 8, 256 * 4, NT>(smem + kI2Lut, t, std::make_integer_sequence<int, kI2>{});
-  lut_copies<uint32_t, 32, 4, 64 * 32, NT>(smem + kI3Lut, t, std::make_integer_sequence<int, kI3>{});
 }
 
 // Replica offset of a lane in the 3-bit table.
