@@ -17,6 +17,7 @@
 // results stay bitwise deterministic.
 #include <algorithm>
 #include <numeric>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -81,6 +82,9 @@ __device__ void gemm_build_luts(uint8_t* lut) {
 }
 
 typedef const __attribute__((address_space(1))) u32x4g_t* gq4p;
+// scales through a global-address-space pointer: a flat load would also count against
+// the LDS counter, and the next LDS operand wait would then wait for it
+typedef const __attribute__((address_space(1))) uint16_t* gu16g_p;
 typedef const __attribute__((address_space(3))) u32x4g_t* lq4p;
 typedef const __attribute__((address_space(3))) u32x2g_t* lq2p;
 typedef const __attribute__((address_space(3))) uint32_t* lq1p;
@@ -102,6 +106,18 @@ __device__ __forceinline__ u32x2g_t row_dword2(const uint8_t* slab, int r, int64
   u32x2g_t v = {0u, 0u};
   if (slab) v = *(const __attribute__((address_space(1))) u32x2g_t*)(slab + (byte >> 4) * kSlabChunkBytes + r * kChunkBytes + (byte & 15));
   return v;
+}
+
+// The same reads of an existing slab, unconditional: a load merged with a default value
+// makes the compiler wait for it (and for every load issued before it) at the merge.
+__device__ __forceinline__ u32x4g_t row_chunk_at(const uint8_t* slab, int r, int64_t c) {
+  return *(gq4p)(slab + c * kSlabChunkBytes + r * kChunkBytes);
+}
+__device__ __forceinline__ uint32_t row_dword_at(const uint8_t* slab, int r, int64_t byte) {
+  return *(const __attribute__((address_space(1))) uint32_t*)(slab + (byte >> 4) * kSlabChunkBytes + r * kChunkBytes + (byte & 15));
+}
+__device__ __forceinline__ u32x2g_t row_dword2_at(const uint8_t* slab, int r, int64_t byte) {
+  return *(const __attribute__((address_space(1))) u32x2g_t*)(slab + (byte >> 4) * kSlabChunkBytes + r * kChunkBytes + (byte & 15));
 }
 
 __device__ __forceinline__ uint32_t dword_of(const u32x4g_t& v, int i) {
@@ -341,7 +357,7 @@ __global__ void __launch_bounds__(kThreads, QL_GEMM_WAVES_PER_EU) gemm_kernel(Ma
       st.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
     }
     st.sc = 0;
-    if (tid < kTileN && sc_n < a.N) st.sc = a.pscales[pscale_index(sc_n, g, G8)];
+    if (tid < kTileN && sc_n < a.N) st.sc = ((gu16g_p)a.pscales)[pscale_index(sc_n, g, G8)];
   };
   // x tile and scales of the staged group into LDS buffer b
   auto put_x = [&](int b) __attribute__((always_inline)) {
@@ -513,21 +529,18 @@ __device__ __forceinline__ void gemm2_tile(const MatArgs& a, int M, int nsplit, 
   // block tid >> 8 of the tile (wave-uniform)
   const int dr = (tid & 127) + 128 * (tid >> 8);
   const int dh = __builtin_amdgcn_readfirstlane((tid >> 7) & 1);
+  // Every load of the stage loop is unconditional: rows past the matrix's last slab read
+  // its last row, and tokens past M read token 0; those rows and tokens are never stored,
+  // and an output depends only on its own row and token.
   const int64_t dn = n0 + dr;
-  const int64_t dslab_i = dn / kSlab;
+  const int64_t dn_c = dn < nslabs * kSlab ? dn : nslabs * kSlab - 1;
   int gr = QL_GRID_T;
-  const uint8_t* dslab = nullptr;
-  if (dslab_i < nslabs) {
-    const int64_t off = slab_offset(dslab_i, K, a.grid, a.blk_grid, a.blk_off, &gr);
-    dslab = a.packed + off;
-  }
+  const uint8_t* dslab = a.packed + slab_offset(dn_c / kSlab, K, a.grid, a.blk_grid, a.blk_off, &gr);
   gr = __builtin_amdgcn_readfirstlane(gr);  // uniform: the wave's rows share one grid block
-  const int dslab_r = (int)(dn & (kSlab - 1));
-  const bool drow_ok = dn < a.N;
+  const int dslab_r = (int)(dn_c & (kSlab - 1));
   // x mapping: token xr of the tile, piece xp (16 * TA bytes of the stage's 128)
   const int xr = tid / XQ, xp = tid % XQ;
-  const bool x_ok = m0 + xr < M;
-  const uint16_t* xrow = a.x + (int64_t)(x_ok ? m0 + xr : 0) * K + 8 * TA * xp;
+  const uint16_t* xrow = a.x + (int64_t)(m0 + xr < M ? m0 + xr : 0) * K + 8 * TA * xp;
 
   struct Regs {
     u32x4g_t xv[TA];
@@ -537,27 +550,24 @@ __device__ __forceinline__ void gemm2_tile(const MatArgs& a, int M, int nsplit, 
   auto load = [&](int s) __attribute__((always_inline)) {
     Regs& r = st;
 #pragma unroll
-    for (int q = 0; q < TA; ++q) {
-      r.xv[q] = u32x4g_t{0u, 0u, 0u, 0u};
-      if (x_ok) r.xv[q] = *(gq4p)(xrow + (int64_t)s * kG2K + 8 * q);
-    }
+    for (int q = 0; q < TA; ++q) r.xv[q] = *(gq4p)(xrow + (int64_t)s * kG2K + 8 * q);
     const int k0 = kG2K * s + 32 * dh;  // first input of this thread's 32
     if (gr == QL_GRID_T) {
       const int64_t p = k0 / kPeriodK;
       const int kp = k0 - (int)p * kPeriodK;
-      r.ch[0] = row_chunk(dslab, dslab_r, 8 * p + (kp / 5) / 16);
-      r.ch[1] = row_chunk(dslab, dslab_r, 8 * p + ((kp + 31) / 5) / 16);
+      r.ch[0] = row_chunk_at(dslab, dslab_r, 8 * p + (kp / 5) / 16);
+      r.ch[1] = row_chunk_at(dslab, dslab_r, 8 * p + ((kp + 31) / 5) / 16);
     } else if (gr == QL_GRID_I2) {
-      const u32x2g_t v = row_dword2(dslab, dslab_r, k0 / 4);
+      const u32x2g_t v = row_dword2_at(dslab, dslab_r, k0 / 4);
       r.ch[0] = u32x4g_t{v.x, v.y, 0u, 0u};
       r.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
     } else {
       const int64_t b0 = 3 * (int64_t)k0 / 8;
-      r.ch[0] = u32x4g_t{row_dword(dslab, dslab_r, b0), row_dword(dslab, dslab_r, b0 + 4),
-                          row_dword(dslab, dslab_r, b0 + 8), 0u};
+      r.ch[0] = u32x4g_t{row_dword_at(dslab, dslab_r, b0), row_dword_at(dslab, dslab_r, b0 + 4),
+                          row_dword_at(dslab, dslab_r, b0 + 8), 0u};
       r.ch[1] = u32x4g_t{0u, 0u, 0u, 0u};
     }
-    r.sc = drow_ok ? (uint32_t)a.pscales[pscale_index(dn, k0 / kGroup, G8)] : 0u;
+    r.sc = (uint32_t)((gu16g_p)a.pscales)[pscale_index(dn_c, k0 / kGroup, G8)];
   };
   // decode the loaded stage s (bf16 c * s) and its x tile into buffer b
   auto put = [&](int s, int b) __attribute__((always_inline)) {
@@ -647,21 +657,29 @@ __device__ __forceinline__ void gemm2_tile(const MatArgs& a, int M, int nsplit, 
   // the other's decode between the barriers (same-box: 4.7 % faster on a Qwen3-8B
   // layer at 256 and 512 tokens; at 64 tokens, where a stage's MFMAs are few, 3 %
   // slower, so smaller tiles keep one order).
-  const bool mfma_first = TA == 4 && __builtin_amdgcn_readfirstlane(wave) >= 4;
-  for (int s = s_lo; s < s_hi; ++s) {
-    const int b = (s - s_lo) & 1;
-    if (mfma_first) mma(b);
-    if (s + 1 < s_hi) {
-      put(s + 1, b ^ 1);
-      if (s + 2 < s_hi) load(s + 2);
+  // Each order is a loop of its own with one MFMA call site: with both orders in one loop
+  // the accumulators took two register sets and were copied between them every stage.
+  auto stages = [&](auto mf) __attribute__((always_inline)) {
+    constexpr bool kMfmaFirst = decltype(mf)::value;
+    for (int s = s_lo; s < s_hi; ++s) {
+      const int b = (s - s_lo) & 1;
+      if constexpr (kMfmaFirst) mma(b);
+      if (s + 1 < s_hi) {
+        put(s + 1, b ^ 1);
+        if (s + 2 < s_hi) load(s + 2);
+      }
+      if constexpr (!kMfmaFirst) mma(b);
+      lds_barrier();
     }
-    if (!mfma_first) mma(b);
-    lds_barrier();
-  }
+  };
+  if (TA == 4 && __builtin_amdgcn_readfirstlane(wave) >= 4) stages(std::true_type{});
+  else stages(std::false_type{});
 
   // D register r of lane l: token 8 (r / 4) + 4 (l / 32) + r % 4 of the 32-token block,
-  // weight row l % 32 of the 32-row block
-  float* out = nsplit > 1 ? part + (int64_t)z * M * a.N : a.y;
+  // weight row l % 32 of the 32-row block (global stores: flat ones would also count
+  // against the LDS counter, which the next tile's first waits use)
+  __attribute__((address_space(1))) float* out =
+      (__attribute__((address_space(1))) float*)(nsplit > 1 ? part + (int64_t)z * M * a.N : a.y);
 #pragma unroll
   for (int ta = 0; ta < TA; ++ta)
 #pragma unroll
