@@ -1005,17 +1005,12 @@ hipError_t launch_gemm_grouped(const ql_gemv_desc* descs, int32_t count, int64_t
     hipLaunchKernelGGL(gemm2_grouped_kernel<2>, dim3(grid), dim3(kG2Threads), 0, stream, descs, count, total, M, ws, ws_floats);
   else
     hipLaunchKernelGGL(gemm2_grouped_kernel<4>, dim3(grid), dim3(kG2Threads), 0, stream, descs, count, total, M, ws, ws_floats);
-  if (ws_floats > 0)
-#ifdef QL_RED512
-    hipLaunchKernelGGL(gemm_reduce_grouped_kernel, dim3(512, count), dim3(256), 0, stream, descs, M, ws, ws_floats);
-#else
-  {
+  if (ws_floats > 0) {
     // a split entry holds at most half the workspace: about sixteen outputs per thread for it
     const int64_t bx = std::min<int64_t>(2048, std::max<int64_t>(128, ws_floats / 2 / (256 * 16)));
     hipLaunchKernelGGL(gemm_reduce_grouped_kernel, dim3((unsigned)bx, count), dim3(256), 0, stream, descs, M, ws,
                        ws_floats);
   }
-#endif
   return hipGetLastError();
 }
 
